@@ -1,0 +1,208 @@
+"""TEST INFRASTRUCTURE -- ctypes binding of the fp64 CPU oracle.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and it imports nothing from the product.
+
+The oracle is a plain, slow implementation of the forward pass of a GShard
+mixture-of-experts feed-forward layer (gate, top-k with renormalised weights,
+capacity-limited slots, dispatch, expert ReLU FFN, combine, auxiliary loss and
+z-loss); ``moe_oracle.c`` documents each step and the passage it follows.
+
+Arrays are numpy.  An activation array is ``float32`` (fp32) or ``uint16``
+(raw bf16 bit patterns); both are widened exactly inside the oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build() -> str:
+    """Compile ``moe_oracle.c`` into ``liboracle.so`` (gcc, OpenMP)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+    )
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    i32 = ctypes.c_int
+    lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double]
+    lib.oracle_capacity.restype = i32
+    lib.oracle_logits.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.oracle_route.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.oracle_expert_ffn.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.oracle_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.oracle_token_output.argtypes = [i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    for name in ("oracle_logits", "oracle_route", "oracle_dispatch", "oracle_expert_ffn",
+                 "oracle_combine", "oracle_token_output"):
+        getattr(lib, name).restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _act(a: np.ndarray) -> tuple[np.ndarray, int]:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError(f"activation arrays are float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _same_dtype(ref: int, *arrays):
+    out = []
+    for a in arrays:
+        if a is None:
+            out.append(None)
+            continue
+        a, dt = _act(a)
+        if dt != ref:
+            raise TypeError("all activation arrays must share one dtype")
+        out.append(a)
+    return out
+
+
+def capacity(S: int, E: int, k: int, capacity_factor: float) -> int:
+    """C = ceil(capacity_factor * k * S / E)."""
+    return int(_load().oracle_capacity(S, E, k, float(capacity_factor)))
+
+
+def logits(x: np.ndarray, wg: np.ndarray, bg: np.ndarray | None = None) -> np.ndarray:
+    """fp32 router logits x . Wg^T + bg, accumulated in fp64."""
+    x, dt = _act(x)
+    S, d = x.shape
+    wg = np.ascontiguousarray(wg, dtype=np.float32)
+    E = wg.shape[0]
+    assert wg.shape == (E, d)
+    if bg is not None:
+        bg = np.ascontiguousarray(bg, dtype=np.float32)
+        assert bg.shape == (E,)
+    out = np.empty((S, E), dtype=np.float32)
+    _load().oracle_logits(S, d, E, _ptr(x), dt, _ptr(wg), _ptr(bg), _ptr(out))
+    return out
+
+
+def route(lg: np.ndarray, k: int, C: int) -> dict:
+    """Softmax, top-k, renormalised weights, capacity slots, counts, losses."""
+    lg = np.ascontiguousarray(lg, dtype=np.float32)
+    S, E = lg.shape
+    assert 1 <= k <= E and C >= 1
+    idx = np.empty((S, k), np.int32)
+    w = np.empty((S, k), np.float64)
+    slot = np.empty((S, k), np.int32)
+    counts = np.empty((k, E), np.int32)
+    lse = np.empty((S,), np.float64)
+    psum = np.empty((E,), np.float64)
+    losses = np.empty((2,), np.float64)
+    _load().oracle_route(S, E, k, C, _ptr(lg), _ptr(idx), _ptr(w), _ptr(slot), _ptr(counts),
+                         _ptr(lse), _ptr(psum), _ptr(losses))
+    return dict(idx=idx, w=w, slot=slot, counts=counts, lse=lse, psum=psum,
+                aux=float(losses[0]), z=float(losses[1]))
+
+
+def occupancy(counts: np.ndarray, C: int) -> np.ndarray:
+    """Filled slots per expert: min(total assignments, C)."""
+    return np.minimum(counts.sum(axis=0), C).astype(np.int32)
+
+
+def dispatch(x: np.ndarray, idx: np.ndarray, slot: np.ndarray, E: int, C: int) -> np.ndarray:
+    """[E,C,d] buffer of dispatched rows (zero where no token was placed)."""
+    x, dt = _act(x)
+    S, d = x.shape
+    k = idx.shape[1]
+    idx = np.ascontiguousarray(idx, np.int32)
+    slot = np.ascontiguousarray(slot, np.int32)
+    xd = np.empty((E, C, d), dtype=x.dtype)
+    _load().oracle_dispatch(S, d, E, C, k, _ptr(x), dt, _ptr(idx), _ptr(slot), _ptr(xd))
+    return xd
+
+
+def expert_ffn(xd, occ, w1, b1, w2, b2) -> np.ndarray:
+    """fp64 expert outputs [E,C,d] for filled slots (zero elsewhere)."""
+    xd, dt = _act(xd)
+    E, C, d = xd.shape
+    h = w1.shape[1]
+    w1, b1, w2, b2 = _same_dtype(dt, w1, b1, w2, b2)
+    assert w1.shape == (E, h, d) and w2.shape == (E, d, h)
+    occ = np.ascontiguousarray(occ, np.int32)
+    out = np.empty((E, C, d), np.float64)
+    _load().oracle_expert_ffn(E, C, d, h, _ptr(occ), _ptr(xd), dt, _ptr(w1), _ptr(b1),
+                              _ptr(w2), _ptr(b2), _ptr(out))
+    return out
+
+
+def combine(out: np.ndarray, idx, slot, w, S: int) -> np.ndarray:
+    """fp64 layer output y [S,d] = sum of kept w * expert output rows."""
+    out = np.ascontiguousarray(out, np.float64)
+    E, C, d = out.shape
+    k = idx.shape[1]
+    idx = np.ascontiguousarray(idx, np.int32)
+    slot = np.ascontiguousarray(slot, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    y = np.empty((S, d), np.float64)
+    _load().oracle_combine(S, d, E, C, k, _ptr(out), _ptr(idx), _ptr(slot), _ptr(w), _ptr(y))
+    return y
+
+
+def token_output(tokens, x, w1, b1, w2, b2, idx, slot, w) -> np.ndarray:
+    """fp64 y rows for the given tokens, computed per token without buffers."""
+    x, dt = _act(x)
+    S, d = x.shape
+    h = w1.shape[1]
+    k = idx.shape[1]
+    w1, b1, w2, b2 = _same_dtype(dt, w1, b1, w2, b2)
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    assert tokens.size == 0 or (tokens.min() >= 0 and tokens.max() < S)
+    idx = np.ascontiguousarray(idx, np.int32)
+    slot = np.ascontiguousarray(slot, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    y = np.empty((tokens.size, d), np.float64)
+    _load().oracle_token_output(tokens.size, _ptr(tokens), d, h, k, _ptr(x), dt, _ptr(w1),
+                                _ptr(b1), _ptr(w2), _ptr(b2), _ptr(idx), _ptr(slot), _ptr(w),
+                                _ptr(y))
+    return y
+
+
+def layer(x, wg, bg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray | None = None) -> dict:
+    """Whole forward pass.  With ``lg`` given, routing starts from those fp32
+    logits instead of computing them (used to compare against a device that
+    produced the logits itself)."""
+    if lg is None:
+        lg = logits(x, wg, bg)
+    r = route(lg, k, C)
+    E = lg.shape[1]
+    S = lg.shape[0]
+    xd = dispatch(x, r["idx"], r["slot"], E, C)
+    occ = occupancy(r["counts"], C)
+    out = expert_ffn(xd, occ, w1, b1, w2, b2)
+    y = combine(out, r["idx"], r["slot"], r["w"], S)
+    r.update(logits=lg, xd=xd, occ=occ, out=out, y=y)
+    return r

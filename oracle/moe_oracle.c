@@ -1,0 +1,325 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.
+ *
+ * A plain, slow, obviously-correct CPU implementation of the forward pass of
+ * a GShard mixture-of-experts feed-forward layer, accumulating in fp64.  Only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It shares no code, header, table or helper with the HIP library;
+ * neither side includes or links the other.
+ *
+ * Sources (pages about GShard; section names as they appear on each page):
+ *  [card]  "GShard: Scaling Giant Models with Conditional Computation and
+ *          Automatic Sharding" (inference-research paper card), method
+ *          paragraph: top-2 gating with softmax-normalised top-2 weights,
+ *          auxiliary loss N*sum_j f_j*P_j plus a z-loss, tokens over an
+ *          expert's capacity dropped, capacity set by capacity_factor.
+ *  [blog]  "GShard: Scaling Giant Neural Networks with Conditional
+ *          Computation", section "Mixture-of-Experts Implementation"
+ *          (equation G(x) = Softmax(x . W_g), top-k of the gate), paragraph
+ *          "Expert Capacity", section "Core Components" ("Expert Networks":
+ *          each expert is a feed-forward network).
+ *  [atlas] "GShard (Expert Parallelism)", "In plain words": tokens are sent
+ *          to the experts by an all-to-all and returned.
+ *  [claim] research-vault atomic claim IX2-0404, section "WideEP",
+ *          "Evidence": expert results come back by a second all-to-all.
+ *
+ * Readings where the pages leave a step open (each one is a choice made here):
+ *  - capacity C = ceil(capacity_factor * k * S / E), one group = all S tokens;
+ *  - top-k is taken on the fp32 logits, larger first, equal logits ordered by
+ *    lower expert index (-0 and +0 compare equal);
+ *  - slots are handed out rank by rank (all first choices, then all second
+ *    choices, ...), tokens in order inside a rank; an assignment whose slot
+ *    would be >= C is dropped;
+ *  - the top-k weights are renormalised over the k selected experts before
+ *    capacity and are not renormalised again after drops;
+ *  - N in the auxiliary loss is E; f_j is the fraction of tokens whose first
+ *    choice is j before capacity; P_j is the mean full softmax probability;
+ *  - the z-loss is the mean over tokens of the squared natural-log
+ *    logsumexp of the logits;
+ *  - the two all-to-alls become a local permute into [E,C,d] buffers and a
+ *    gate-weighted combine back to token order (one device, no collectives);
+ *  - each expert is ReLU(x W1^T + b1) W2^T + b2 with W1 [h,d], W2 [d,h].
+ *
+ * Activation arrays (x, W1, b1, W2, b2) are fp32 or bf16; bf16 values are
+ * passed as their raw 16-bit patterns and widened exactly.  Everything the
+ * oracle computes is carried in fp64; only the logits are rounded to fp32,
+ * since that is the precision the router is defined in here.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Exact widening of one activation element to fp64.  A bf16 value is the top
+ * half of the fp32 with the same sign, exponent and leading mantissa bits. */
+static double act_at(const void *base, int dtype, size_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static size_t act_size(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+
+/* Expert capacity: C = ceil(cf * k * S / E).  [card] method paragraph
+ * (capacity governed by capacity_factor); [blog] "Expert Capacity". */
+int oracle_capacity(int S, int E, int k, double capacity_factor)
+{
+    if (S < 0 || E < 1 || k < 1 || !(capacity_factor > 0.0))
+        return -1;
+    double v = capacity_factor * (double)k * (double)S / (double)E;
+    return (int)ceil(v);
+}
+
+/* Router logits l[s,j] = sum_i x[s,i] * Wg[j,i] + bg[j], fp64 accumulation,
+ * one rounding to fp32.  [blog] "Mixture-of-Experts Implementation",
+ * G(x) = Softmax(x . W_g); Wg is stored [E,d] (the transpose of W_g). */
+void oracle_logits(int S, int d, int E, const void *x, int x_dtype,
+                   const float *wg, const float *bg, float *logits)
+{
+    #pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        for (int j = 0; j < E; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i)
+                acc += act_at(x, x_dtype, (size_t)s * d + i) * (double)wg[(size_t)j * d + i];
+            if (bg)
+                acc += (double)bg[j];
+            logits[(size_t)s * E + j] = (float)acc;
+        }
+    }
+}
+
+/* Routing of S tokens over E experts with top-k and capacity C.
+ *
+ * Per token ([blog] gating equation; [card] top-2 with softmax-normalised
+ * weights):
+ *   m = max_j l_j,  lse = m + ln sum_j exp(l_j - m),  p_j = exp(l_j - lse);
+ *   idx[s,0..k-1] = experts ordered by (l descending, index ascending);
+ *   w[s,r] = p[idx[s,r]] / sum_r' p[idx[s,r']].
+ * Capacity ([card] drops over capacity):
+ *   one counter per expert; for r = 0..k-1, for s = 0..S-1: the assignment
+ *   (s,r) to e = idx[s,r] takes slot cnt[e] if cnt[e] < C, else slot -1;
+ *   cnt[e] += 1.  counts[r,e] is the number of rank-r assignments to e.
+ * Losses ([card] auxiliary loss and z-loss):
+ *   aux = E * sum_j f_j P_j, f_j = counts[0,j] / S, P_j = sum_s p[s,j] / S;
+ *   z   = sum_s lse_s^2 / S.
+ *
+ * Outputs: idx [S,k] int32, w [S,k] fp64, slot [S,k] int32, counts [k,E]
+ * int32, lse [S] fp64, psum [E] fp64 (sum_s p[s,j]), losses [2] fp64. */
+void oracle_route(int S, int E, int k, int C, const float *logits,
+                  int32_t *idx, double *w, int32_t *slot, int32_t *counts,
+                  double *lse, double *psum, double *losses)
+{
+    double *p = (double *)malloc(sizeof(double) * (size_t)S * (size_t)E);
+
+    #pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        const float *l = logits + (size_t)s * E;
+        double m = (double)l[0];
+        for (int j = 1; j < E; ++j)
+            if ((double)l[j] > m)
+                m = (double)l[j];
+        double sum = 0.0;
+        for (int j = 0; j < E; ++j)
+            sum += exp((double)l[j] - m);
+        double lse_s = m + log(sum);
+        lse[s] = lse_s;
+        for (int j = 0; j < E; ++j)
+            p[(size_t)s * E + j] = exp((double)l[j] - lse_s);
+
+        /* Top-k by repeated selection: each round takes the largest logit
+         * among experts not yet taken; scanning j upward with a strict '>'
+         * keeps the lower index among equal logits. */
+        for (int r = 0; r < k; ++r) {
+            int best = -1;
+            for (int j = 0; j < E; ++j) {
+                int taken = 0;
+                for (int q = 0; q < r; ++q)
+                    if (idx[(size_t)s * k + q] == j)
+                        taken = 1;
+                if (taken)
+                    continue;
+                if (best < 0 || l[j] > l[best])
+                    best = j;
+            }
+            idx[(size_t)s * k + r] = best;
+        }
+
+        double den = 0.0;
+        for (int r = 0; r < k; ++r)
+            den += p[(size_t)s * E + idx[(size_t)s * k + r]];
+        for (int r = 0; r < k; ++r)
+            w[(size_t)s * k + r] = p[(size_t)s * E + idx[(size_t)s * k + r]] / den;
+    }
+
+    /* Capacity-limited slots, rank-major then token order. */
+    int32_t *cnt = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    memset(counts, 0, sizeof(int32_t) * (size_t)k * (size_t)E);
+    for (int r = 0; r < k; ++r) {
+        for (int s = 0; s < S; ++s) {
+            int e = idx[(size_t)s * k + r];
+            slot[(size_t)s * k + r] = cnt[e] < C ? cnt[e] : -1;
+            cnt[e] += 1;
+            counts[(size_t)r * E + e] += 1;
+        }
+    }
+    free(cnt);
+
+    for (int j = 0; j < E; ++j) {
+        double acc = 0.0;
+        for (int s = 0; s < S; ++s)
+            acc += p[(size_t)s * E + j];
+        psum[j] = acc;
+    }
+    double aux = 0.0;
+    for (int j = 0; j < E; ++j) {
+        double f = (double)counts[j] / (double)S; /* rank-0 row of counts */
+        double P = psum[j] / (double)S;
+        aux += f * P;
+    }
+    aux *= (double)E;
+    double z = 0.0;
+    for (int s = 0; s < S; ++s)
+        z += lse[s] * lse[s];
+    z /= (double)S;
+    losses[0] = S > 0 ? aux : 0.0;
+    losses[1] = S > 0 ? z : 0.0;
+    free(p);
+}
+
+/* Dispatch, the local stand-in for the first all-to-all ([atlas] "In plain
+ * words"): xd[e,c,:] = x[s,:] for every kept assignment (s,r) with
+ * e = idx[s,r], c = slot[s,r].  Slots nobody was assigned stay zero.  The
+ * copy is of the stored elements, so xd has x's dtype. */
+void oracle_dispatch(int S, int d, int E, int C, int k, const void *x, int dtype,
+                     const int32_t *idx, const int32_t *slot, void *xd)
+{
+    size_t es = act_size(dtype);
+    memset(xd, 0, es * (size_t)E * (size_t)C * (size_t)d);
+    for (int s = 0; s < S; ++s) {
+        for (int r = 0; r < k; ++r) {
+            int c = slot[(size_t)s * k + r];
+            if (c < 0)
+                continue;
+            int e = idx[(size_t)s * k + r];
+            memcpy((char *)xd + es * (((size_t)e * C + c) * d),
+                   (const char *)x + es * ((size_t)s * d), es * (size_t)d);
+        }
+    }
+}
+
+/* Expert FFNs ([blog] "Core Components", Expert Networks): for each expert e
+ * and each filled slot c < occ[e]:
+ *   hid = max(W1_e xd[e,c] + b1_e, 0);   out[e,c] = W2_e hid + b2_e,
+ * in fp64 with no intermediate rounding.  W1 [E,h,d], W2 [E,d,h], b1 [E,h],
+ * b2 [E,d] (biases may be NULL = 0).  Rows c >= occ[e] of out are zero. */
+void oracle_expert_ffn(int E, int C, int d, int h, const int32_t *occ,
+                       const void *xd, int dtype, const void *w1, const void *b1,
+                       const void *w2, const void *b2, double *out)
+{
+    memset(out, 0, sizeof(double) * (size_t)E * (size_t)C * (size_t)d);
+    #pragma omp parallel
+    {
+        double *hid = (double *)malloc(sizeof(double) * (size_t)h);
+        #pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int e = 0; e < E; ++e) {
+            for (int c = 0; c < C; ++c) {
+                if (c >= occ[e])
+                    continue;
+                size_t row = (size_t)e * C + c;
+                for (int j = 0; j < h; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += act_at(w1, dtype, ((size_t)e * h + j) * d + i) *
+                               act_at(xd, dtype, row * d + i);
+                    if (b1)
+                        acc += act_at(b1, dtype, (size_t)e * h + j);
+                    hid[j] = acc > 0.0 ? acc : 0.0;
+                }
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        acc += act_at(w2, dtype, ((size_t)e * d + i) * h + j) * hid[j];
+                    if (b2)
+                        acc += act_at(b2, dtype, (size_t)e * d + i);
+                    out[row * d + i] = acc;
+                }
+            }
+        }
+        free(hid);
+    }
+}
+
+/* Combine, the local stand-in for the second all-to-all ([claim] "Evidence"):
+ * y[s] = sum over kept r of w[s,r] * out[idx[s,r], slot[s,r]]; a token whose
+ * assignments were all dropped gets y[s] = 0. */
+void oracle_combine(int S, int d, int E, int C, int k, const double *out,
+                    const int32_t *idx, const int32_t *slot, const double *w,
+                    double *y)
+{
+    (void)E;
+    #pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        for (int i = 0; i < d; ++i)
+            y[(size_t)s * d + i] = 0.0;
+        for (int r = 0; r < k; ++r) {
+            int c = slot[(size_t)s * k + r];
+            if (c < 0)
+                continue;
+            int e = idx[(size_t)s * k + r];
+            const double *o = out + ((size_t)e * C + c) * d;
+            for (int i = 0; i < d; ++i)
+                y[(size_t)s * d + i] += w[(size_t)s * k + r] * o[i];
+        }
+    }
+}
+
+/* The layer output of selected tokens computed without any buffer:
+ * y[s] = sum over kept r of w[s,r] * FFN_{idx[s,r]}(x[s]).  This is the same
+ * definition as dispatch -> expert FFN -> combine, written per token, so that
+ * single rows of a full-size layer can be checked. */
+void oracle_token_output(int ns, const int64_t *tokens, int d, int h, int k,
+                         const void *x, int dtype, const void *w1, const void *b1,
+                         const void *w2, const void *b2, const int32_t *idx,
+                         const int32_t *slot, const double *w, double *y)
+{
+    #pragma omp parallel
+    {
+        double *hid = (double *)malloc(sizeof(double) * (size_t)h);
+        #pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < ns; ++t) {
+            int64_t s = tokens[t];
+            for (int i = 0; i < d; ++i)
+                y[(size_t)t * d + i] = 0.0;
+            for (int r = 0; r < k; ++r) {
+                if (slot[(size_t)s * k + r] < 0)
+                    continue;
+                int e = idx[(size_t)s * k + r];
+                for (int j = 0; j < h; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += act_at(w1, dtype, ((size_t)e * h + j) * d + i) *
+                               act_at(x, dtype, (size_t)s * d + i);
+                    if (b1)
+                        acc += act_at(b1, dtype, (size_t)e * h + j);
+                    hid[j] = acc > 0.0 ? acc : 0.0;
+                }
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        acc += act_at(w2, dtype, ((size_t)e * d + i) * h + j) * hid[j];
+                    if (b2)
+                        acc += act_at(b2, dtype, (size_t)e * d + i);
+                    y[(size_t)t * d + i] += w[(size_t)s * k + r] * acc;
+                }
+            }
+        }
+        free(hid);
+    }
+}

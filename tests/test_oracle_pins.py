@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle to facts the method and plain mathematics fix.
+
+Nothing here compares the oracle with itself: each check is a closed form, an
+invariant, a brute-force count on tiny inputs, or a special case that reduces
+to a textbook routine (torch fp64 linear/relu/softmax/logsumexp).  The tests
+use non-zero biases and h != d so that a dropped term or a transposed operand
+in the oracle fails one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import moe_workloads as mw
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def brute_topk(lg_row, k):
+    """Full sort by (logit descending, index ascending)."""
+    order = sorted(range(len(lg_row)), key=lambda j: (-float(lg_row[j]), j))
+    return order[:k]
+
+
+def brute_slots(idx, C):
+    """slot[s,r] = #{(s',r'): idx[s',r'] = e and (r' < r or (r' = r and s' < s))},
+    kept if < C: an O((S k)^2) count straight from the ordering rule."""
+    S, k = idx.shape
+    slot = np.empty((S, k), np.int64)
+    for s in range(S):
+        for r in range(k):
+            e = idx[s, r]
+            n = 0
+            for s2 in range(S):
+                for r2 in range(k):
+                    if idx[s2, r2] == e and (r2 < r or (r2 == r and s2 < s)):
+                        n += 1
+            slot[s, r] = n if n < C else -1
+    return slot
+
+
+def ffn64(x, w1, b1, w2, b2):
+    """Textbook dense ReLU FFN in torch fp64: relu(x W1^T + b1) W2^T + b2."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    hid = torch.relu(torch.nn.functional.linear(t(x), t(w1), None if b1 is None else t(b1)))
+    return torch.nn.functional.linear(hid, t(w2), None if b2 is None else t(b2)).numpy()
+
+
+def rand_layer(rng, S, d, h, E, biases=True):
+    x = rng.standard_normal((S, d)).astype(np.float32)
+    wg = (rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    bg = (0.3 * rng.standard_normal(E)).astype(np.float32)
+    w1 = (rng.standard_normal((E, h, d)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, h)) / math.sqrt(h)).astype(np.float32)
+    b1 = (0.1 * rng.standard_normal((E, h))).astype(np.float32) if biases else None
+    b2 = (0.1 * rng.standard_normal((E, d))).astype(np.float32) if biases else None
+    return x, wg, bg, w1, b1, w2, b2
+
+
+# ---------------------------------------------------------------- capacity
+def test_capacity_closed_form_for_each_workload():
+    want = {"tiny_fp32": 80, "balanced_bf16": 512, "skewed_bf16": 256, "large_bf16": 2560,
+            "deepseek_bf16": 384}
+    for name, C in want.items():
+        w = mw.get(name)
+        assert oracle.capacity(w.S, w.E, w.k, w.capacity_factor) == C
+    assert oracle.capacity(10, 3, 1, 1.0) == 4      # ceil(10/3)
+    assert oracle.capacity(7, 4, 2, 1.0) == 4       # ceil(3.5)
+    assert oracle.capacity(8, 4, 2, 1.0) == 4       # exact
+    assert oracle.capacity(1, 256, 8, 1.5) == 1     # ceil(0.046875)
+
+
+# ---------------------------------------------------------------- P1 closed form
+def test_zero_gate_closed_form_golden():
+    g = json.load(open(os.path.join(GOLDEN, "zero_gate_tiny.json")))
+    S, d, h, E, k = g["S"], g["d"], g["h"], g["E"], g["k"]
+    C = oracle.capacity(S, E, k, g["capacity_factor"])
+    assert C == g["capacity"]
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((S, d)).astype(np.float32)
+    lg = oracle.logits(x, np.zeros((E, d), np.float32), np.zeros(E, np.float32))
+    assert np.all(lg == 0)
+    r = oracle.route(lg, k, C)
+    assert np.all(r["idx"] == np.array(g["top_k"]))
+    assert np.all(r["w"] == g["weight"])
+    kept = g["kept_tokens_per_rank"]
+    for rank in range(k):
+        s = np.arange(S)
+        assert np.array_equal(r["slot"][:, rank], np.where(s < kept, s, -1))
+    assert int((r["slot"] < 0).sum()) == g["drops"]
+    assert r["counts"].tolist() == g["counts"]
+    assert r["aux"] == pytest.approx(g["aux"], rel=1e-15)
+    assert r["z"] == pytest.approx(g["z"], rel=1e-14)
+    assert np.allclose(r["lse"], math.log(E), rtol=1e-15)
+
+
+# ---------------------------------------------------------------- P2 balanced first choice
+def test_balanced_first_choice_gives_unit_aux():
+    rng = np.random.default_rng(11)
+    S, E, k = 96, 8, 3
+    lg = rng.uniform(-2, 2, (S, E)).astype(np.float32)
+    lg[np.arange(S), np.arange(S) % E] = 5.0      # argmax = s mod E
+    r = oracle.route(lg, k, C=7)                  # drops happen; aux must not care
+    assert np.array_equal(r["idx"][:, 0], np.arange(S) % E)
+    assert (r["slot"] < 0).any()
+    assert r["aux"] == pytest.approx(1.0, rel=1e-13)
+
+
+def test_aux_uses_first_choice_fraction_and_mean_probability():
+    # Two experts, first choice always expert 0: f = (1, 0), aux = E * P_0.
+    rng = np.random.default_rng(3)
+    S, E = 50, 2
+    lg = np.stack([rng.uniform(0.5, 1.0, S), rng.uniform(-1, 0.4, S)], 1).astype(np.float32)
+    r = oracle.route(lg, 1, C=S)
+    p0 = torch.softmax(torch.from_numpy(lg.astype(np.float64)), dim=1)[:, 0].mean().item()
+    assert r["aux"] == pytest.approx(E * p0, rel=1e-13)
+
+
+# ---------------------------------------------------------------- P3 shift invariance
+def test_shift_invariance():
+    rng = np.random.default_rng(7)
+    S, E, k, C = 80, 6, 2, 20
+    lg = (rng.integers(-256, 256, (S, E)) / 64.0).astype(np.float32)  # exact under + 2
+    a = oracle.route(lg, k, C)
+    b = oracle.route(lg + np.float32(2.0), k, C)
+    for key in ("idx", "slot", "counts"):
+        assert np.array_equal(a[key], b[key])
+    assert np.allclose(a["w"], b["w"], rtol=1e-13, atol=0)
+    assert np.allclose(a["psum"], b["psum"], rtol=1e-12)
+    assert a["aux"] == pytest.approx(b["aux"], rel=1e-13)
+    assert np.allclose(b["lse"] - a["lse"], 2.0, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P4 unbounded capacity
+def test_unbounded_capacity_equals_dense_topk_sum():
+    rng = np.random.default_rng(1)
+    S, d, h, E, k = 40, 12, 20, 5, 2
+    x, wg, bg, w1, b1, w2, b2 = rand_layer(rng, S, d, h, E)
+    C = oracle.capacity(S, E, k, E / k)
+    assert C == S
+    res = oracle.layer(x, wg, bg, w1, b1, w2, b2, k, C)
+    assert (res["slot"] >= 0).all()
+    want = np.zeros((S, d))
+    for s in range(S):
+        for r in range(k):
+            e = res["idx"][s, r]
+            want[s] += res["w"][s, r] * ffn64(x[s:s + 1], w1[e], b1[e], w2[e], b2[e])[0]
+    assert np.allclose(res["y"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_token_output_matches_buffered_path_with_drops():
+    rng = np.random.default_rng(2)
+    S, d, h, E, k = 64, 16, 24, 4, 2
+    x, wg, bg, w1, b1, w2, b2 = rand_layer(rng, S, d, h, E)
+    C = oracle.capacity(S, E, k, 0.5)
+    res = oracle.layer(x, wg, bg, w1, b1, w2, b2, k, C)
+    assert (res["slot"] < 0).any()
+    tok = np.arange(S)
+    yt = oracle.token_output(tok, x, w1, b1, w2, b2, res["idx"], res["slot"], res["w"])
+    assert np.allclose(yt, res["y"], rtol=1e-12, atol=1e-12)
+    # dense reference with dropped assignments removed
+    want = np.zeros((S, d))
+    for s in range(S):
+        for r in range(k):
+            if res["slot"][s, r] >= 0:
+                e = res["idx"][s, r]
+                want[s] += res["w"][s, r] * ffn64(x[s:s + 1], w1[e], b1[e], w2[e], b2[e])[0]
+    assert np.allclose(res["y"], want, rtol=1e-12, atol=1e-12)
+    # a token with every assignment dropped has y = 0
+    all_dropped = (res["slot"] < 0).all(axis=1)
+    assert all_dropped.any()
+    assert np.all(res["y"][all_dropped] == 0)
+
+
+# ---------------------------------------------------------------- P5 textbook reductions
+def test_single_expert_is_dense_ffn():
+    rng = np.random.default_rng(4)
+    S, d, h = 30, 10, 14
+    x, wg, bg, w1, b1, w2, b2 = rand_layer(rng, S, d, h, 1)
+    res = oracle.layer(x, wg, bg, w1, b1, w2, b2, k=1, C=S)
+    assert np.allclose(res["y"], ffn64(x, w1[0], b1[0], w2[0], b2[0]), rtol=1e-12, atol=1e-12)
+    assert res["aux"] == pytest.approx(1.0, rel=1e-15)
+    lg64 = res["logits"].astype(np.float64)[:, 0]
+    assert res["z"] == pytest.approx(np.mean(lg64 ** 2), rel=1e-13)
+
+
+def test_all_experts_is_softmax_mixture():
+    rng = np.random.default_rng(6)
+    S, d, h, E = 24, 8, 12, 4
+    x, wg, bg, w1, b1, w2, b2 = rand_layer(rng, S, d, h, E)
+    res = oracle.layer(x, wg, bg, w1, b1, w2, b2, k=E, C=S)
+    lg = torch.from_numpy(res["logits"].astype(np.float64))
+    p = torch.softmax(lg, dim=1).numpy()
+    want = sum(p[:, [e]] * ffn64(x, w1[e], b1[e], w2[e], b2[e]) for e in range(E))
+    assert np.allclose(res["y"], want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(res["lse"], torch.logsumexp(lg, dim=1).numpy(), rtol=1e-14)
+    assert np.allclose(res["psum"] / S, p.mean(axis=0), rtol=1e-12)
+
+
+def test_logits_match_fp64_matmul():
+    rng = np.random.default_rng(8)
+    S, d, E = 33, 40, 7
+    x, wg, bg, *_ = rand_layer(rng, S, d, 8, E)
+    want = (torch.from_numpy(x.astype(np.float64)) @ torch.from_numpy(wg.astype(np.float64)).T
+            + torch.from_numpy(bg.astype(np.float64))).numpy().astype(np.float32)
+    assert np.array_equal(oracle.logits(x, wg, bg), want)
+    # bf16 activations are widened exactly
+    xb = (np.asarray(x).view(np.uint32) >> 16).astype(np.uint16)
+    xw = mw.bf16_bits_to_f32(xb)
+    want_b = (torch.from_numpy(xw.astype(np.float64)) @ torch.from_numpy(wg.astype(np.float64)).T
+              ).numpy().astype(np.float32)
+    assert np.array_equal(oracle.logits(xb, wg, None), want_b)
+
+
+def test_expert_ffn_matches_textbook_per_expert_bf16():
+    rng = np.random.default_rng(9)
+    E, C, d, h = 3, 5, 16, 8
+    f = lambda shape, s=1.0: (s * rng.standard_normal(shape)).astype(np.float32)
+    to_b = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+    xd, w1, w2, b1, b2 = to_b(f((E, C, d))), to_b(f((E, h, d))), to_b(f((E, d, h))), \
+        to_b(f((E, h), 0.2)), to_b(f((E, d), 0.2))
+    occ = np.array([5, 2, 0], np.int32)
+    out = oracle.expert_ffn(xd, occ, w1, b1, w2, b2)
+    wd = mw.bf16_bits_to_f32
+    for e in range(E):
+        want = ffn64(wd(xd[e, :occ[e]]), wd(w1[e]), wd(b1[e]), wd(w2[e]), wd(b2[e]))
+        assert np.allclose(out[e, :occ[e]], want, rtol=1e-12, atol=1e-12)
+        assert np.all(out[e, occ[e]:] == 0)
+
+
+# ---------------------------------------------------------------- P6 invariants
+def check_route_invariants(lg, k, C, r):
+    S, E = lg.shape
+    idx, slot, w, counts = r["idx"], r["slot"], r["w"], r["counts"]
+    n = counts.sum(axis=0)
+    assert n.sum() == S * k
+    for rank in range(k):
+        assert np.array_equal(np.bincount(idx[:, rank], minlength=E), counts[rank])
+    assert (slot < 0).sum() == np.maximum(n - C, 0).sum()
+    occ = oracle.occupancy(counts, C)
+    for e in range(E):
+        kept = np.sort(slot[(idx == e) & (slot >= 0)])
+        assert np.array_equal(kept, np.arange(occ[e]))        # each slot once
+        assert occ[e] <= C
+        for rank in range(k):                                   # token order within a rank
+            sl = slot[idx[:, rank] == e, rank]
+            sk = sl[sl >= 0]
+            assert np.all(np.diff(sk) == 1)
+            if rank > 0 and (sl >= 0).any():                    # lower ranks all kept first
+                assert not ((idx[:, :rank] == e) & (slot[:, :rank] < 0)).any()
+    # distinct experts per token, weights in (0,1], descending, sum to 1
+    for s in range(S):
+        assert len(set(idx[s].tolist())) == k
+    assert np.all(w > 0) and np.all(w <= 1)
+    assert np.all(np.diff(w, axis=1) <= 1e-15)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert r["psum"].sum() == pytest.approx(S, rel=1e-12)
+    m = lg.max(axis=1).astype(np.float64)
+    assert np.all(r["lse"] >= m - 1e-12) and np.all(r["lse"] <= m + math.log(E) + 1e-12)
+
+
+def test_route_invariants_with_drops():
+    rng = np.random.default_rng(12)
+    for (S, E, k, cf) in [(200, 8, 2, 0.6), (150, 16, 4, 1.0), (64, 5, 5, 0.3), (97, 3, 1, 0.9)]:
+        lg = rng.standard_normal((S, E)).astype(np.float32)
+        lg[:, 0] += 1.0  # make expert 0 hot so it overflows
+        C = oracle.capacity(S, E, k, cf)
+        r = oracle.route(lg, k, C)
+        assert (r["slot"] < 0).any()
+        check_route_invariants(lg, k, C, r)
+
+
+# ---------------------------------------------------------------- P7 brute force
+def test_exhaustive_integer_logits_ties():
+    """Every 3x3 logit matrix over {0,1,2}: top-k by full sort and slots by the
+    O((Sk)^2) count, for k in 1..3 and C in 1..3."""
+    S = E = 3
+    for vals in itertools.product((0.0, 1.0, 2.0), repeat=S * E):
+        lg = np.array(vals, np.float32).reshape(S, E)
+        for k in (1, 2, 3):
+            want_idx = np.array([brute_topk(lg[s], k) for s in range(S)])
+            for C in (1, 2, 3):
+                r = oracle.route(lg, k, C)
+                assert np.array_equal(r["idx"], want_idx), (vals, k, C)
+                assert np.array_equal(r["slot"], brute_slots(want_idx, C)), (vals, k, C)
+
+
+def test_negative_zero_ties_positive_zero():
+    lg = np.array([[-0.0, 0.0, -1.0, 0.0], [0.0, -0.0, -0.0, -2.0]], np.float32)
+    r = oracle.route(lg, 3, 4)
+    assert r["idx"].tolist() == [[0, 1, 3], [0, 1, 2]]
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(1, 48), st.integers(1, 8), st.data())
+def test_route_matches_brute_force_random(S, E, data):
+    k = data.draw(st.integers(1, E))
+    cf = data.draw(st.sampled_from([0.25, 0.5, 0.75, 1.0, 1.5]))
+    seed = data.draw(st.integers(0, 2**31 - 1))
+    rng = np.random.default_rng(seed)
+    lg = (rng.integers(-3, 4, (S, E)) / 2.0).astype(np.float32)  # frequent ties
+    C = oracle.capacity(S, E, k, cf)
+    r = oracle.route(lg, k, C)
+    want_idx = np.array([brute_topk(lg[s], k) for s in range(S)])
+    assert np.array_equal(r["idx"], want_idx)
+    assert np.array_equal(r["slot"], brute_slots(want_idx, C))
+    p = torch.softmax(torch.from_numpy(lg.astype(np.float64)), dim=1).numpy()
+    sel = np.take_along_axis(p, want_idx, 1)
+    assert np.allclose(r["w"], sel / sel.sum(1, keepdims=True), rtol=1e-13)
+    check_route_invariants(lg, k, C, r)
+
+
+# ---------------------------------------------------------------- dispatch / combine
+def test_dispatch_is_exact_row_copy():
+    rng = np.random.default_rng(13)
+    S, d, E, k = 50, 24, 6, 2
+    x = rng.standard_normal((S, d)).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    lg = rng.standard_normal((S, E)).astype(np.float32)
+    C = oracle.capacity(S, E, k, 0.8)
+    r = oracle.route(lg, k, C)
+    for arr in (x, xb):
+        xd = oracle.dispatch(arr, r["idx"], r["slot"], E, C)
+        filled = np.zeros((E, C), bool)
+        for s in range(S):
+            for rank in range(k):
+                c = r["slot"][s, rank]
+                if c >= 0:
+                    e = r["idx"][s, rank]
+                    assert np.array_equal(xd[e, c], arr[s])
+                    filled[e, c] = True
+        assert np.all(xd[~filled] == 0)
+        assert filled.sum() == (r["slot"] >= 0).sum()
