@@ -1,0 +1,204 @@
+"""Benchmark of the MI355X GShard MoE-layer forward (one GPU).
+
+One step = one moe_layer_forward over one batch of S synthetic tokens: router
+logits, softmax, top-k, capacity slots, dispatch, both expert GEMMs, combine,
+aux loss and z-loss.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` = tokens per second of the whole layer.
+Per-stage times come from HIP events recorded between the library's kernels
+on the launch stream, inside the timed region.  ``roofline`` describes the
+slowest kernel (an expert GEMM); ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import moe_workloads as mw  # noqa: E402
+import sparse_moe_layer_wg_amd as moe  # noqa: E402
+from sparse_moe_layer_wg_amd.layer import MoELayer  # noqa: E402
+
+METRIC = "MoE-layer tokens/s (gate+dispatch+FFN+combine); % bf16 MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense, TFLOP/s
+STAGES = ["gate_logits", "route", "slot_scan", "slot_positions", "dispatch", "expert_gemm1",
+          "expert_gemm2", "combine"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="balanced_bf16", choices=mw.ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_work(w: mw.Workload, occ: np.ndarray, kept: int) -> dict:
+    """Bytes and FLOPs the method must move / do, per launch of each kernel.
+    GEMM weights count only for experts with at least one filled slot."""
+    es = 2 if w.dtype == "bf16" else 4
+    nonempty = int((occ > 0).sum())
+    S, d, h, E, k = w.S, w.d, w.h, w.E, w.k
+    return {
+        "expert_gemm1": dict(flops=2.0 * kept * d * h,
+                             bytes=nonempty * h * d * es + kept * d * es + kept * h * es),
+        "expert_gemm2": dict(flops=2.0 * kept * d * h,
+                             bytes=nonempty * d * h * es + kept * h * es + kept * d * es),
+        "dispatch": dict(flops=0.0, bytes=S * d * es + kept * d * es),
+        "combine": dict(flops=2.0 * kept * d, bytes=kept * d * es + S * d * es),
+        "gate_logits": dict(flops=2.0 * S * d * E, bytes=S * d * es + E * d * 4 + S * E * 4),
+    }
+
+
+def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float) -> dict:
+    import oracle
+    host = {n: mw.to_numpy(t) for n, t in inputs.items()}
+
+    def run(n):
+        C = oracle.capacity(n, w.E, w.k, w.capacity_factor)
+        t0 = time.perf_counter()
+        oracle.layer(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"], host["w2"],
+                     host["b2"], w.k, C)
+        return time.perf_counter() - t0
+
+    n0 = min(w.S, 256)
+    t0 = run(n0)
+    n = int(min(w.S, max(n0, n0 * target_s / max(t0, 1e-3))))
+    n = max(64, (n // 64) * 64) if n >= 64 else n
+    t = run(n) if n != n0 else t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {w.S} tokens of the same workload (same E, d, h, k, "
+                      f"capacity_factor; C scaled with the sample), full fp64 oracle layer "
+                      f"from logits to y, {t:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              f"(the layer has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = mw.get(a.workload)
+    inputs = mw.generate(w, "cuda")
+    cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype)
+    layer = MoELayer.from_inputs(cfg, inputs, keep=False)
+    x = inputs["x"]
+    stream = torch.cuda.current_stream()
+
+    def make_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_STAGE_EVENTS)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    for _ in range(a.warmup):
+        layer.forward(x)
+    step_events = [make_events() for _ in range(a.steps)]
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        layer.forward(x, events=step_events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / a.steps
+
+    stage_us = {}
+    for si, name in enumerate(STAGES):
+        vals = [ev[si].elapsed_time(ev[si + 1]) * 1000.0 for ev in step_events]
+        stage_us[name] = float(np.mean(vals))
+
+    # routing statistics of this batch (from a keep=True run)
+    probe = MoELayer.from_inputs(cfg, inputs, keep=True)
+    probe.forward(x)
+    torch.cuda.synchronize()
+    counts = probe.counts.cpu().numpy()
+    occ = np.minimum(counts.sum(0), probe.C)
+    kept = int(occ.sum())
+    aux, z = (float(v) for v in probe.losses.cpu().numpy())
+    drops = int((probe.slot < 0).sum().item())
+    del probe
+
+    work = algorithmic_work(w, occ, kept)
+    dom = max(("expert_gemm1", "expert_gemm2"), key=lambda n: stage_us[n])
+    t = stage_us[dom] * 1e-6
+    fl, by = work[dom]["flops"], work[dom]["bytes"]
+    t_mfma = fl / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+    t_hbm = by / (HBM_PEAK_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": by / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": fl / t / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["algorithmic_flops"] = fl
+    roof["algorithmic_bytes"] = by
+    roof["avg_launch_us"] = stage_us[dom]
+
+    ffn_s = (stage_us["expert_gemm1"] + stage_us["expert_gemm2"]) * 1e-6
+    ffn_flops = work["expert_gemm1"]["flops"] + work["expert_gemm2"]["flops"]
+    stage_frac = {}
+    for n in ("gate_logits", "dispatch", "combine", "expert_gemm1", "expert_gemm2"):
+        ts = stage_us[n] * 1e-6
+        stage_frac[n] = {"GB_s": work[n]["bytes"] / ts / 1e9,
+                         "TFLOP_s": work[n]["flops"] / ts / 1e12}
+
+    out = {
+        "metric": METRIC,
+        "value": w.S / (ms / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "S": w.S, "d_model": w.d, "d_ff": w.h, "E": w.E,
+                   "k": w.k, "capacity_factor": w.capacity_factor, "C": probe_C(cfg),
+                   "seed": w.seed},
+        "roofline": roof,
+        "ffn_mfma_frac": ffn_flops / ffn_s / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),
+        "stage_us": stage_us,
+        "stage_rates": stage_frac,
+        "routing": {"kept": kept, "dropped": drops, "nonempty_experts": int((occ > 0).sum()),
+                    "aux": aux, "z": z},
+        "wall_s": wall,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def probe_C(cfg):
+    return moe.capacity(cfg)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) GShard mixture-of-experts layer.
+ *
+ * The library computes the forward pass of one GShard MoE feed-forward layer
+ * on one GPU's share of tokens and experts:
+ *
+ *   logits   l = x . Wg^T + bg                         (router, fp32)
+ *   p        = softmax(l),  lse = logsumexp(l)
+ *   top-k    idx[s,0..k-1]: largest logits first, equal logits -> lower index
+ *   weights  w[s,r] = p[idx[s,r]] / sum_r' p[idx[s,r']]
+ *   slots    rank by rank, tokens in order; slot >= C -> dropped (-1)
+ *   dispatch xd[e,c,:] = x[s,:]                 (local stand-in, all-to-all)
+ *   experts  out[e,c] = ReLU(xd[e,c] W1_e^T + b1_e) W2_e^T + b2_e
+ *   combine  y[s] = sum over kept r of w[s,r] out[idx[s,r], slot[s,r]]
+ *   losses   aux = E * sum_j f_j P_j,  z = mean_s lse_s^2
+ *
+ * Sources: "GShard: Scaling Giant Models with Conditional Computation and
+ * Automatic Sharding" (inference-research paper card), method paragraph (top-2
+ * with softmax-normalised weights, aux loss N*sum f_j*P_j plus a z-loss, drops
+ * over a capacity set by capacity_factor); "GShard: Scaling Giant Neural
+ * Networks with Conditional Computation" (blog), section "Mixture-of-Experts
+ * Implementation" (G(x) = Softmax(x . W_g), top-k), paragraph "Expert
+ * Capacity", section "Core Components" (experts are feed-forward networks);
+ * "GShard (Expert Parallelism)" (atlas), "In plain words" (tokens go to the
+ * experts by an all-to-all and return); research-vault claim IX2-0404,
+ * section "WideEP", "Evidence" (results come back by a second all-to-all).
+ *
+ * Readings fixed by this library where the pages leave a step open:
+ *   C = ceil(capacity_factor * k * S / E) unless moe_config.capacity > 0;
+ *   f_j = (first choices of expert j before capacity) / S, N = E;
+ *   P_j = mean over tokens of the full softmax probability;
+ *   z = mean over tokens of the squared natural-log logsumexp;
+ *   weights are renormalised over the k selected experts before capacity and
+ *   not again after drops; a token with every assignment dropped gets y = 0.
+ *
+ * Conventions shared by every entry point
+ *   Pointers.  Every array argument is a DEVICE pointer to memory the caller
+ *     owns (for example a torch tensor's data_ptr()).  The config is host
+ *     memory.  The library allocates and frees nothing, keeps no pointer after
+ *     a call returns, and holds no global mutable state.
+ *   Execution.  Work is enqueued on `stream` (0 = the null stream) and is
+ *     asynchronous: outputs are valid once the stream has been synchronised.
+ *     The library performs no host<->device copies and no synchronisation.
+ *   Layouts.  Row-major, no padding:  x, y [S,d];  Wg [E,d] fp32;  bg [E]
+ *     fp32;  W1 [E,h,d];  b1 [E,h];  W2 [E,d,h];  b2 [E,d];  xd, out [E,C,d];
+ *     logits [S,E] fp32;  topk_idx, slot [S,k] int32;  topk_w [S,k] fp32;
+ *     counts [k,E] int32 (assignments of rank r to expert e before capacity);
+ *     losses [2] fp32 = {aux, z}.
+ *   Dtypes.  x, W1, b1, W2, b2, xd, out and y share act_dtype (fp32 or
+ *     bf16, with fp32 accumulation).  Wg, bg, logits, topk_w and losses are
+ *     always fp32.  Biases b1/b2/bg may be NULL (= zero).
+ *   Errors.  Arguments are validated on the host before anything is
+ *     enqueued; a failed check returns MOE_ERR_INVALID_ARG (bad value or NULL
+ *     required pointer), MOE_ERR_UNSUPPORTED (valid but outside what the
+ *     kernels handle: see moe_config) or MOE_ERR_WORKSPACE (ws too small) and
+ *     has no side effect.  A failed kernel launch returns MOE_ERR_HIP.  The
+ *     library never aborts and throws nothing across the ABI.
+ *   Buffers.  Slots of xd/out past an expert's occupancy are left as they
+ *     were (never read by later steps).  NaN/Inf inputs are not supported.
+ *   Workspace.  `ws` is device scratch of at least moe_workspace_bytes()
+ *     bytes, 256-byte aligned; its contents do not persist between calls.
+ *     Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape.  Valid: S >= 0; d_model, d_ff >= 1; 1 <= E; 1 <= k <= E;
+ * capacity_factor > 0 when capacity == 0; capacity >= 0.
+ * Supported by the kernels (else MOE_ERR_UNSUPPORTED): E <= 2048, k <= 8,
+ * k * E <= 16384, d_model and d_ff multiples of 64 for bf16 and of 4 for
+ * fp32, and E * C * max(d_model, d_ff) < 2^31. */
+typedef struct moe_config {
+    int32_t S;               /* tokens on this GPU                         */
+    int32_t d_model;         /* d: model width                             */
+    int32_t d_ff;            /* h: expert hidden width                     */
+    int32_t E;               /* experts on this GPU                        */
+    int32_t k;               /* experts per token                          */
+    int32_t capacity;        /* C per expert; 0 = ceil(cf * k * S / E)     */
+    double capacity_factor;  /* cf                                         */
+    int32_t act_dtype;       /* moe_dtype                                  */
+    uint32_t reserved;       /* must be 0                                  */
+} moe_config;
+
+/* moe_gate flag: read `logits` as an input instead of computing them from x,
+ * Wg and bg (x, w_gate and gate_bias may then be NULL). */
+#define MOE_GATE_LOGITS_IN 1u
+
+/* Number of events moe_layer_forward records when stage_events != NULL:
+ * [0] start, [1] after router logits, [2] after softmax/top-k, [3] after
+ * slot scan and losses, [4] after slot positions, [5] after dispatch,
+ * [6] after expert GEMM 1, [7] after expert GEMM 2, [8] after combine. */
+#define MOE_NUM_STAGE_EVENTS 9
+
+/* Capacity C of the config (capacity if > 0, else ceil(cf*k*S/E)), or -1 if
+ * the config is invalid. */
+int32_t moe_capacity(const moe_config *cfg);
+
+/* Device workspace bytes that moe_layer_forward needs (enough for every
+ * other entry point too) when all of its optional outputs are NULL. */
+moe_status moe_workspace_bytes(const moe_config *cfg, size_t *bytes);
+
+/* Static text for a status code. */
+const char *moe_status_string(int32_t status);
+
+/* Router, top-k and capacity slots.
+ * In:  x [S,d] act, w_gate [E,d] fp32, gate_bias [E] fp32 or NULL
+ *      (all unused with MOE_GATE_LOGITS_IN).
+ * Out: logits [S,E] fp32 (input with MOE_GATE_LOGITS_IN; may be NULL
+ *      otherwise, then kept in ws), topk_idx [S,k], topk_w [S,k],
+ *      slot [S,k] (-1 = dropped), counts [k,E], losses [2].
+ * Logits within a small margin of a top-k decision are re-evaluated in fp64
+ * and rounded once to fp32, and the stored logits hold those values. */
+moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,
+                    const float *gate_bias, float *logits, int32_t *topk_idx,
+                    float *topk_w, int32_t *slot, int32_t *counts, float *losses,
+                    uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permute token rows into per-expert capacity buffers (the local stand-in
+ * for the dispatch all-to-all): xd[idx[s,r], slot[s,r], :] = x[s, :] for
+ * every slot[s,r] >= 0.  Bit-exact copy.  Needs no workspace. */
+moe_status moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                        const int32_t *slot, void *xd, hipStream_t stream);
+
+/* Expert FFNs over the filled slots: for e < E and c < occ_e =
+ * min(sum_r counts[r,e], C): out[e,c] = ReLU(xd[e,c] W1_e^T + b1_e) W2_e^T
+ * + b2_e, fp32 accumulation; the hidden activations are rounded to act_dtype
+ * (they live in ws).  Rows c >= occ_e of out are not written. */
+moe_status moe_expert_ffn(const moe_config *cfg, const void *xd, const int32_t *counts,
+                          const void *w1, const void *b1, const void *w2, const void *b2,
+                          void *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gate-weighted combine back to token order (the local stand-in for the
+ * second all-to-all): y[s] = sum over slot[s,r] >= 0 of
+ * topk_w[s,r] * out[topk_idx[s,r], slot[s,r]], fp32 accumulation, rounded
+ * to act_dtype; y[s] = 0 when every assignment of s was dropped.  Needs no
+ * workspace. */
+moe_status moe_combine(const moe_config *cfg, const void *out, const int32_t *topk_idx,
+                       const int32_t *slot, const float *topk_w, void *y,
+                       hipStream_t stream);
+
+/* The whole forward pass: gate, slots, dispatch, expert FFNs, combine and
+ * losses, enqueued back to back with no host synchronisation.
+ * Required: x, w_gate, w1, w2, y, ws.  Optional (NULL = not wanted, kept in
+ * ws): gate_bias, b1, b2, logits, topk_idx, topk_w, slot, counts, losses,
+ * xd, out.  When xd and out are both NULL one workspace buffer serves as
+ * both.  stage_events: NULL, or MOE_NUM_STAGE_EVENTS events created by the
+ * caller, recorded on `stream` between the steps (for timing). */
+moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *w_gate,
+                             const float *gate_bias, const void *w1, const void *b1,
+                             const void *w2, const void *b2, void *y, float *logits,
+                             int32_t *topk_idx, float *topk_w, int32_t *slot,
+                             int32_t *counts, float *losses, void *xd, void *out,
+                             void *ws, size_t ws_bytes, hipEvent_t *stage_events,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

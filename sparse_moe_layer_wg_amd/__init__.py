@@ -1,0 +1,25 @@
+"""MI355X (gfx950) GShard mixture-of-experts layer forward.
+
+A thin ctypes binding over the C ABI in ``include/moe.h`` (``libmoe.so``):
+argument marshalling only.  Every step of the layer runs in the library's
+HIP kernels; PyTorch provides device memory and the stream.  Loading fails
+loudly when ``libmoe.so`` has not been built: there is no fallback.
+"""
+from ._lib import (  # noqa: F401
+    MOE_BF16,
+    MOE_F32,
+    MOE_GATE_LOGITS_IN,
+    MOE_NUM_STAGE_EVENTS,
+    MoeConfig,
+    MoeError,
+    capacity,
+    combine,
+    config,
+    dispatch,
+    expert_ffn,
+    gate,
+    layer_forward,
+    library,
+    library_path,
+    workspace_bytes,
+)

@@ -1,0 +1,231 @@
+"""ctypes binding of ``libmoe.so`` (the C ABI declared in ``include/moe.h``).
+
+Functions take torch tensors on the GPU, check their dtype, device, size and
+contiguity (the C ABI receives raw pointers and cannot), and pass
+``data_ptr()`` plus the current HIP stream.  Nothing is computed here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libmoe.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_GATE_LOGITS_IN = 1
+MOE_NUM_STAGE_EVENTS = 9
+
+_STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_double),
+        ("act_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.act_dtype == MOE_BF16 else torch.float32
+
+
+def config(S, d_model, d_ff, E, k, capacity_factor=1.0, capacity=0, dtype="bf16") -> MoeConfig:
+    dt = {"bf16": MOE_BF16, "f32": MOE_F32, torch.bfloat16: MOE_BF16,
+          torch.float32: MOE_F32}[dtype]
+    return MoeConfig(int(S), int(d_model), int(d_ff), int(E), int(k), int(capacity),
+                     float(capacity_factor), dt, 0)
+
+
+_lib = None
+
+
+def library():
+    """Load ``libmoe.so`` (building it first if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        from . import _build
+        _build.build()
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"HIP library {library_path} is missing and could not be built")
+    lib = ctypes.CDLL(library_path)
+    vp, cfgp = ctypes.c_void_p, ctypes.POINTER(MoeConfig)
+    lib.moe_capacity.argtypes = [cfgp]
+    lib.moe_capacity.restype = ctypes.c_int32
+    lib.moe_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_status_string.argtypes = [ctypes.c_int32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_gate.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp,
+                             ctypes.c_size_t, vp]
+    lib.moe_dispatch.argtypes = [cfgp, vp, vp, vp, vp, vp]
+    lib.moe_expert_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+    lib.moe_layer_forward.argtypes = [cfgp] + [vp] * 17 + [ctypes.c_size_t, vp, vp]
+    for f in ("moe_workspace_bytes", "moe_gate", "moe_dispatch", "moe_expert_ffn",
+              "moe_combine", "moe_layer_forward"):
+        getattr(lib, f).restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def capacity(cfg: MoeConfig) -> int:
+    return int(library().moe_capacity(ctypes.byref(cfg)))
+
+
+def workspace_bytes(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_workspace_bytes")
+    return int(n.value)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _arg(t, name, dtype, numel, required=True):
+    """data_ptr of a checked tensor (None -> NULL)."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(ws):
+    if ws is None:
+        raise ValueError("workspace is required")
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def gate(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, losses, ws,
+         logits_in=False, stream=None):
+    """Router, top-k and capacity slots (``moe_gate``)."""
+    S, d, E, k = cfg.S, cfg.d_model, cfg.E, cfg.k
+    at = cfg.torch_dtype
+    wsp, wsb = _ws(ws)
+    st = library().moe_gate(
+        ctypes.byref(cfg),
+        _arg(x, "x", at, S * d, required=not logits_in),
+        _arg(w_gate, "w_gate", torch.float32, E * d, required=not logits_in),
+        _arg(gate_bias, "gate_bias", torch.float32, E, required=False),
+        _arg(logits, "logits", torch.float32, S * E, required=logits_in),
+        _arg(topk_idx, "topk_idx", torch.int32, S * k),
+        _arg(topk_w, "topk_w", torch.float32, S * k),
+        _arg(slot, "slot", torch.int32, S * k),
+        _arg(counts, "counts", torch.int32, k * E),
+        _arg(losses, "losses", torch.float32, 2),
+        MOE_GATE_LOGITS_IN if logits_in else 0, wsp, wsb, _stream(stream))
+    _check(st, "moe_gate")
+
+
+def dispatch(cfg, x, topk_idx, slot, xd, stream=None):
+    """Permute token rows into [E,C,d] (``moe_dispatch``)."""
+    C = capacity(cfg)
+    at = cfg.torch_dtype
+    st = library().moe_dispatch(
+        ctypes.byref(cfg), _arg(x, "x", at, cfg.S * cfg.d_model),
+        _arg(topk_idx, "topk_idx", torch.int32, cfg.S * cfg.k),
+        _arg(slot, "slot", torch.int32, cfg.S * cfg.k),
+        _arg(xd, "xd", at, cfg.E * C * cfg.d_model), _stream(stream))
+    _check(st, "moe_dispatch")
+
+
+def expert_ffn(cfg, xd, counts, w1, b1, w2, b2, out, ws, stream=None):
+    """Expert ReLU FFNs over filled slots (``moe_expert_ffn``)."""
+    C = capacity(cfg)
+    E, d, h = cfg.E, cfg.d_model, cfg.d_ff
+    at = cfg.torch_dtype
+    wsp, wsb = _ws(ws)
+    st = library().moe_expert_ffn(
+        ctypes.byref(cfg), _arg(xd, "xd", at, E * C * d),
+        _arg(counts, "counts", torch.int32, cfg.k * E),
+        _arg(w1, "w1", at, E * h * d), _arg(b1, "b1", at, E * h, required=False),
+        _arg(w2, "w2", at, E * d * h), _arg(b2, "b2", at, E * d, required=False),
+        _arg(out, "out", at, E * C * d), wsp, wsb, _stream(stream))
+    _check(st, "moe_expert_ffn")
+
+
+def combine(cfg, out, topk_idx, slot, topk_w, y, stream=None):
+    """Gate-weighted combine back to token order (``moe_combine``)."""
+    C = capacity(cfg)
+    at = cfg.torch_dtype
+    S, k = cfg.S, cfg.k
+    st = library().moe_combine(
+        ctypes.byref(cfg), _arg(out, "out", at, cfg.E * C * cfg.d_model),
+        _arg(topk_idx, "topk_idx", torch.int32, S * k), _arg(slot, "slot", torch.int32, S * k),
+        _arg(topk_w, "topk_w", torch.float32, S * k), _arg(y, "y", at, S * cfg.d_model),
+        _stream(stream))
+    _check(st, "moe_combine")
+
+
+def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
+                  topk_idx=None, topk_w=None, slot=None, counts=None, losses=None, xd=None,
+                  out=None, events=None, stream=None):
+    """Whole forward pass (``moe_layer_forward``).  ``events``: None or a list
+    of MOE_NUM_STAGE_EVENTS torch.cuda.Event objects already created."""
+    C = capacity(cfg)
+    S, d, h, E, k = cfg.S, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
+    at = cfg.torch_dtype
+    wsp, wsb = _ws(ws)
+    ev = None
+    if events is not None:
+        if len(events) != MOE_NUM_STAGE_EVENTS:
+            raise ValueError(f"events must hold {MOE_NUM_STAGE_EVENTS} events")
+        handles = [e.cuda_event for e in events]
+        if not all(handles):
+            raise ValueError("events must be created (recorded once) before use")
+        ev = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
+    st = library().moe_layer_forward(
+        ctypes.byref(cfg), _arg(x, "x", at, S * d), _arg(w_gate, "w_gate", torch.float32, E * d),
+        _arg(gate_bias, "gate_bias", torch.float32, E, required=False),
+        _arg(w1, "w1", at, E * h * d), _arg(b1, "b1", at, E * h, required=False),
+        _arg(w2, "w2", at, E * d * h), _arg(b2, "b2", at, E * d, required=False),
+        _arg(y, "y", at, S * d),
+        _arg(logits, "logits", torch.float32, S * E, required=False),
+        _arg(topk_idx, "topk_idx", torch.int32, S * k, required=False),
+        _arg(topk_w, "topk_w", torch.float32, S * k, required=False),
+        _arg(slot, "slot", torch.int32, S * k, required=False),
+        _arg(counts, "counts", torch.int32, k * E, required=False),
+        _arg(losses, "losses", torch.float32, 2, required=False),
+        _arg(xd, "xd", at, E * C * d, required=False),
+        _arg(out, "out", at, E * C * d, required=False),
+        wsp, wsb, ev, _stream(stream))
+    _check(st, "moe_layer_forward")

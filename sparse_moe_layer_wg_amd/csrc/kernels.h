@@ -1,0 +1,74 @@
+// Internal launchers of the MoE-layer kernels.  Each returns the HIP status of
+// its launch; the C ABI in moe_api.hip maps failures to MOE_ERR_HIP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ gate
+// logits[s,j] = sum_i x[s,i] * wg[j,i] + bg[j]   (fp32 accumulation)
+hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
+                              float* logits, int S, int d, int E, hipStream_t st);
+
+struct RouteParams {
+    float* logits;          // [S,E]; refined entries are written back
+    const void* x;          // for refinement (NULL when refinement is off)
+    bool x_bf16;
+    const float* wg;
+    const float* bg;
+    int S, d, E, k, nb;     // nb = ceil(S / kTokBlock)
+    float tau;              // refinement margin; 0 disables refinement
+    int32_t* topk_idx;      // [S,k]
+    float* topk_w;          // [S,k]
+    int32_t* hist;          // [E][k*nb] per-(rank, token block) expert counts
+    float* ppart;           // [nb][E]  per-block sums of softmax probabilities
+    float* zpart;           // [nb]     per-block sums of lse^2
+};
+hipError_t launch_route(const RouteParams& p, hipStream_t st);
+
+// ------------------------------------------------------------------ slots
+// In-place exclusive scan of hist rows (per expert, over (rank, block)
+// tiles); writes counts [k,E] and occupancy occ[e] = min(n_e, C).
+hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t* counts,
+                            int32_t* occ, hipStream_t st);
+// losses = {aux, z}; mt_start[e] = sum_{e'<e} ceil(occ[e']/bm) (E+1 entries).
+hipError_t launch_finalize(const float* ppart, const float* zpart, const int32_t* counts,
+                           const int32_t* occ, int S, int E, int nb, int bm, float* losses,
+                           int32_t* mt_start, hipStream_t st);
+// slot[s,r] from the scanned tile bases and stable in-tile ranks.
+hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
+                                 int E, int k, int nb, int C, int32_t* slot, hipStream_t st);
+// Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN).
+hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
+                            int32_t* mt_start, hipStream_t st);
+// Zero losses and counts (empty input).
+hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st);
+
+// ------------------------------------------------------------------ permute
+hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, const int32_t* slot,
+                           void* xd, int S, int d, int k, int E, int C, int elem_bytes,
+                           hipStream_t st);
+hipError_t launch_combine(const void* out, const int32_t* topk_idx, const int32_t* slot,
+                          const float* topk_w, void* y, int S, int d, int k, int E, int C,
+                          bool bf16, hipStream_t st);
+
+// ------------------------------------------------------------------ expert GEMMs
+// Per expert e, rows m < occ[e]:
+//   Cout[e,m,n] = act(sum_k A[e,m,k] * B[e,n,k] + bias[e,n]),  act = ReLU or id.
+// A [E,C,K], B [E,N,K], bias [E,N] or NULL, Cout [E,C,N]; all act dtype.
+struct GemmParams {
+    const void* A;
+    const void* B;
+    const void* bias;
+    void* Cout;
+    const int32_t* occ;
+    const int32_t* mt_start;
+    int E, C, N, K;
+    bool relu;
+};
+int gemm_block_m(bool bf16);
+hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,337 @@
+// C ABI of the MoE layer: host-side validation, workspace carving and the
+// launch sequence.  Everything here runs on the host; nothing is allocated,
+// copied or synchronised.
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+namespace {
+
+using namespace moe;
+
+struct Plan {
+    int S, d, h, E, k, C, nb;
+    bool bf16;
+    size_t es;  // bytes per activation element
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validates the config; fills the plan.  INVALID_ARG for values outside the
+// definition, UNSUPPORTED for valid shapes the kernels do not handle.
+moe_status make_plan(const moe_config* c, Plan* pl) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
+    if (c->S < 0 || c->d_model < 1 || c->d_ff < 1 || c->E < 1 || c->k < 1 || c->k > c->E)
+        return MOE_ERR_INVALID_ARG;
+    if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (c->capacity < 0) return MOE_ERR_INVALID_ARG;
+    double C;
+    if (c->capacity > 0) {
+        C = c->capacity;
+    } else {
+        if (!(c->capacity_factor > 0.0) || !isfinite(c->capacity_factor))
+            return MOE_ERR_INVALID_ARG;
+        // C = ceil(cf * k * S / E), evaluated left to right in fp64.
+        C = ceil(c->capacity_factor * (double)c->k * (double)c->S / (double)c->E);
+    }
+    if (C > 2147483647.0) return MOE_ERR_UNSUPPORTED;
+    if (c->E > kMaxE || c->k > kMaxK || c->k * c->E > 16384) return MOE_ERR_UNSUPPORTED;
+    const bool bf16 = c->act_dtype == MOE_BF16;
+    const int q = bf16 ? 64 : 4;
+    if (c->d_model % q != 0 || c->d_ff % q != 0) return MOE_ERR_UNSUPPORTED;
+    const double wide = (double)(c->d_model > c->d_ff ? c->d_model : c->d_ff);
+    if ((double)c->E * C * wide >= 2147483648.0) return MOE_ERR_UNSUPPORTED;
+    if ((double)c->S * wide >= 2147483648.0 || (double)c->S * c->E >= 2147483648.0)
+        return MOE_ERR_UNSUPPORTED;
+    pl->S = c->S;
+    pl->d = c->d_model;
+    pl->h = c->d_ff;
+    pl->E = c->E;
+    pl->k = c->k;
+    pl->C = (int)C;
+    pl->nb = (int)ceil_div(c->S, kTokBlock);
+    pl->bf16 = bf16;
+    pl->es = bf16 ? 2 : 4;
+    return MOE_OK;
+}
+
+// Workspace layout, every region 256-byte aligned:
+//   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, occ, mt_start
+//   [ffn]    H [E,C,h]
+//   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
+struct Carve {
+    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, occ, mt_start;
+    size_t route_end, H, ffn_end, xo, end;
+};
+
+size_t up(size_t v) { return (v + 255) & ~size_t(255); }
+
+Carve carve(const Plan& p) {
+    Carve c{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = up(o + bytes);
+        return at;
+    };
+    c.logits = take((size_t)p.S * p.E * 4);
+    c.idx = take((size_t)p.S * p.k * 4);
+    c.w = take((size_t)p.S * p.k * 4);
+    c.slot = take((size_t)p.S * p.k * 4);
+    c.counts = take((size_t)p.k * p.E * 4);
+    c.losses = take(2 * 4);
+    c.hist = take((size_t)p.E * p.k * p.nb * 4);
+    c.ppart = take((size_t)p.nb * p.E * 4);
+    c.zpart = take((size_t)p.nb * 4);
+    c.occ = take((size_t)p.E * 4);
+    c.mt_start = take((size_t)(p.E + 1) * 4);
+    c.route_end = o;
+    c.H = take((size_t)p.E * p.C * p.h * p.es);
+    c.ffn_end = o;
+    c.xo = take((size_t)p.E * p.C * p.d * p.es);
+    c.end = o;
+    return c;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Router margin below which a top-k decision is re-evaluated in fp64: 32
+// ulps of 1.0 scaled by sqrt(d), the growth of fp32 accumulation error.
+float refine_tau(int d) { return (float)(ldexp(32.0, -24) * sqrt((double)d)); }
+
+#define MOE_TRY(call)                                  \
+    do {                                               \
+        if ((call) != hipSuccess) return MOE_ERR_HIP;  \
+    } while (0)
+
+void record(hipEvent_t* ev, int i, hipStream_t st) {
+    if (ev) (void)hipEventRecord(ev[i], st);
+}
+
+// Router + slots for a planned layer.  logits: device array (input when
+// logits_in).  Writes topk_idx/topk_w/slot/counts/losses; leaves occ and
+// mt_start in the workspace.
+moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* wg,
+                    const float* bg, float* logits, bool logits_in, int32_t* topk_idx,
+                    float* topk_w, int32_t* slot, int32_t* counts, float* losses, void* ws,
+                    hipEvent_t* ev, hipStream_t st) {
+    int32_t* hist = at<int32_t>(ws, cv.hist);
+    float* ppart = at<float>(ws, cv.ppart);
+    float* zpart = at<float>(ws, cv.zpart);
+    int32_t* occ = at<int32_t>(ws, cv.occ);
+    int32_t* mt = at<int32_t>(ws, cv.mt_start);
+    if (!logits_in) MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, st));
+    record(ev, 1, st);
+    RouteParams rp{};
+    rp.logits = logits;
+    rp.x = logits_in ? nullptr : x;
+    rp.x_bf16 = p.bf16;
+    rp.wg = logits_in ? nullptr : wg;
+    rp.bg = logits_in ? nullptr : bg;
+    rp.S = p.S;
+    rp.d = p.d;
+    rp.E = p.E;
+    rp.k = p.k;
+    rp.nb = p.nb;
+    rp.tau = logits_in ? 0.f : refine_tau(p.d);
+    rp.topk_idx = topk_idx;
+    rp.topk_w = topk_w;
+    rp.hist = hist;
+    rp.ppart = ppart;
+    rp.zpart = zpart;
+    MOE_TRY(launch_route(rp, st));
+    record(ev, 2, st);
+    MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, st));
+    MOE_TRY(launch_finalize(ppart, zpart, counts, occ, p.S, p.E, p.nb, gemm_block_m(p.bf16),
+                            losses, mt, st));
+    record(ev, 3, st);
+    MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, st));
+    record(ev, 4, st);
+    return MOE_OK;
+}
+
+moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1, const void* w2,
+                   const void* b2, void* out, const int32_t* occ, const int32_t* mt, void* H,
+                   hipEvent_t* ev, hipStream_t st) {
+    GemmParams g{};
+    g.occ = occ;
+    g.mt_start = mt;
+    g.E = p.E;
+    g.C = p.C;
+    g.A = xd;
+    g.B = w1;
+    g.bias = b1;
+    g.Cout = H;
+    g.N = p.h;
+    g.K = p.d;
+    g.relu = true;
+    MOE_TRY(launch_expert_gemm(g, p.bf16, st));
+    record(ev, 6, st);
+    g.A = H;
+    g.B = w2;
+    g.bias = b2;
+    g.Cout = out;
+    g.N = p.d;
+    g.K = p.h;
+    g.relu = false;
+    MOE_TRY(launch_expert_gemm(g, p.bf16, st));
+    record(ev, 7, st);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(const moe_config* cfg) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s == MOE_ERR_INVALID_ARG) return -1;
+    if (s != MOE_OK) {
+        // Valid but unsupported configs still have a capacity.
+        if (cfg->capacity > 0) return cfg->capacity;
+        double C = ceil(cfg->capacity_factor * (double)cfg->k * (double)cfg->S / (double)cfg->E);
+        return C > 2147483647.0 ? -1 : (int32_t)C;
+    }
+    return p.C;
+}
+
+moe_status moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    *bytes = carve(p).end;
+    return MOE_OK;
+}
+
+const char* moe_status_string(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype not supported";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch failed";
+        default: return "unknown moe_status";
+    }
+}
+
+moe_status moe_gate(const moe_config* cfg, const void* x, const float* w_gate,
+                    const float* gate_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                    int32_t* slot, int32_t* counts, float* losses, uint32_t flags, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (flags & ~MOE_GATE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+    const bool logits_in = (flags & MOE_GATE_LOGITS_IN) != 0;
+    if (!counts || !losses) return MOE_ERR_INVALID_ARG;
+    if (p.S > 0 && (!topk_idx || !topk_w || !slot)) return MOE_ERR_INVALID_ARG;
+    if (p.S > 0 && (logits_in ? !logits : (!x || !w_gate))) return MOE_ERR_INVALID_ARG;
+    if (!logits_in && !aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+    if (p.S == 0) {
+        MOE_TRY(launch_zero_outputs(counts, p.k * p.E, losses, stream));
+        return MOE_OK;
+    }
+    if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+    const Carve cv = carve(p);
+    if (ws_bytes < cv.route_end) return MOE_ERR_WORKSPACE;
+    float* L = logits ? logits : at<float>(ws, cv.logits);
+    return run_gate(p, cv, x, w_gate, gate_bias, L, logits_in, topk_idx, topk_w, slot, counts,
+                    losses, ws, nullptr, stream);
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                        const int32_t* slot, void* xd, hipStream_t stream) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (p.S == 0) return MOE_OK;
+    if (!x || !topk_idx || !slot || !xd) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(xd, 16)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_dispatch(x, topk_idx, slot, xd, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* counts,
+                          const void* w1, const void* b1, const void* w2, const void* b2,
+                          void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (!xd || !counts || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+    for (const void* q : {xd, w1, b1, w2, b2, (const void*)out})
+        if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
+    if (p.C == 0) return MOE_OK;
+    if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+    const Carve cv = carve(p);
+    if (ws_bytes < cv.ffn_end) return MOE_ERR_WORKSPACE;
+    int32_t* occ = at<int32_t>(ws, cv.occ);
+    int32_t* mt = at<int32_t>(ws, cv.mt_start);
+    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16), occ, mt, stream));
+    return run_ffn(p, xd, w1, b1, w2, b2, out, occ, mt, at<void>(ws, cv.H), nullptr, stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* out, const int32_t* topk_idx,
+                       const int32_t* slot, const float* topk_w, void* y, hipStream_t stream) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (p.S == 0) return MOE_OK;
+    if (!out || !topk_idx || !slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_combine(out, topk_idx, slot, topk_w, y, p.S, p.d, p.k, p.E, p.C, p.bf16, stream));
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* w_gate,
+                             const float* gate_bias, const void* w1, const void* b1,
+                             const void* w2, const void* b2, void* y, float* logits,
+                             int32_t* topk_idx, float* topk_w, int32_t* slot, int32_t* counts,
+                             float* losses, void* xd, void* out, void* ws, size_t ws_bytes,
+                             hipEvent_t* stage_events, hipStream_t stream) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (!w_gate || !w1 || !w2 || !ws) return MOE_ERR_INVALID_ARG;
+    if (p.S > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+    for (const void* q : {x, w1, b1, w2, b2, (const void*)y, (const void*)xd, (const void*)out})
+        if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+    const Carve cv = carve(p);
+    if (ws_bytes < cv.end) return MOE_ERR_WORKSPACE;
+    hipEvent_t* ev = stage_events;
+    record(ev, 0, stream);
+    if (p.S == 0) {
+        MOE_TRY(launch_zero_outputs(counts, counts ? p.k * p.E : 0, losses, stream));
+        for (int i = 1; i < MOE_NUM_STAGE_EVENTS; ++i) record(ev, i, stream);
+        return MOE_OK;
+    }
+    float* L = logits ? logits : at<float>(ws, cv.logits);
+    int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, cv.idx);
+    float* w = topk_w ? topk_w : at<float>(ws, cv.w);
+    int32_t* sl = slot ? slot : at<int32_t>(ws, cv.slot);
+    int32_t* cnt = counts ? counts : at<int32_t>(ws, cv.counts);
+    float* los = losses ? losses : at<float>(ws, cv.losses);
+    void* XD = xd ? xd : at<void>(ws, cv.xo);
+    void* OUT = out ? out : (xd ? at<void>(ws, cv.xo) : XD);
+
+    s = run_gate(p, cv, x, w_gate, gate_bias, L, false, idx, w, sl, cnt, los, ws, ev, stream);
+    if (s != MOE_OK) return s;
+    MOE_TRY(launch_dispatch(x, idx, sl, XD, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
+    record(ev, 5, stream);
+    s = run_ffn(p, XD, w1, b1, w2, b2, OUT, at<int32_t>(ws, cv.occ), at<int32_t>(ws, cv.mt_start),
+                at<void>(ws, cv.H), ev, stream);
+    if (s != MOE_OK) return s;
+    MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, p.C, p.bf16, stream));
+    record(ev, 8, stream);
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+// Capacity-limited slot assignment and the load-balance / z losses.
+//
+// Method: "GShard: Scaling Giant Models with Conditional Computation and
+// Automatic Sharding" (paper card), method paragraph: assignments beyond an
+// expert's capacity (set by capacity_factor) are dropped; aux loss
+// N*sum_j f_j*P_j plus a z-loss.  "GShard: Scaling Giant Neural Networks with
+// Conditional Computation" (blog), paragraph "Expert Capacity".
+//
+// Slot order (a reading the pages leave open): all first choices, then all
+// second choices, ..., each in token order.  The assignment stream is cut
+// into tiles t = (rank r, token block b) in that order.  The router kernel
+// counts each tile's assignments per expert; a per-expert exclusive scan over
+// tiles gives every tile its base position; inside a tile the stable rank of
+// a token among earlier tokens with the same expert comes from wavefront
+// ballots.  Positions never depend on atomic ordering, so slots are
+// deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// Exclusive scan of the 256-thread block; returns the prefix of `v` and
+// writes the block total to *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int incl = wave_inclusive_scan(v);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int t = s_wave[w];
+        before += w < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+// One block per expert: hist[e][0..T) becomes the exclusive positions.
+__global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hist, int E, int k,
+                                                        int nb, int C,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ occ) {
+    __shared__ int s_wave[4];
+    __shared__ int s_rank_start[kMaxK + 1];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int T = k * nb;
+    int32_t* row = hist + (size_t)e * T;
+    int carry = 0;
+    for (int base = 0; base < T; base += 256) {
+        const int i = base + tid;
+        const int v = i < T ? row[i] : 0;
+        int total;
+        const int ex = block_exclusive_scan(v, s_wave, &total);
+        if (i < T) {
+            row[i] = carry + ex;
+            if (i % nb == 0) s_rank_start[i / nb] = carry + ex;
+        }
+        carry += total;
+    }
+    __syncthreads();
+    if (tid < k) {
+        const int start = s_rank_start[tid];
+        const int end = tid + 1 < k ? s_rank_start[tid + 1] : carry;
+        counts[(size_t)tid * E + e] = end - start;
+    }
+    if (tid == 0) occ[e] = carry < C ? carry : C;
+}
+
+// aux = E * sum_j f_j P_j with f_j = counts[0,j] / S and P_j = (sum of the
+// block partials of p[:,j]) / S;  z = (sum of block partials of lse^2) / S.
+// Partials are summed in a fixed order in fp64, so the result is
+// deterministic.  Also the per-expert m-tile prefix for the expert GEMMs.
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ ppart,
+                                                       const float* __restrict__ zpart,
+                                                       const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ occ, int S,
+                                                       int E, int nb, int bm,
+                                                       float* __restrict__ losses,
+                                                       int32_t* __restrict__ mt_start) {
+    __shared__ double s_red[256];
+    __shared__ int s_wave[4];
+    const int tid = threadIdx.x;
+    double term = 0.0;
+    for (int j = tid; j < E; j += 256) {
+        double P = 0.0;
+        for (int b = 0; b < nb; ++b) P += (double)ppart[(size_t)b * E + j];
+        term += (double)counts[j] * P;
+    }
+    s_red[tid] = term;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) s_red[tid] += s_red[tid + off];
+        __syncthreads();
+    }
+    const double aux_sum = s_red[0];
+    __syncthreads();
+    double z = 0.0;
+    for (int b = tid; b < nb; b += 256) z += (double)zpart[b];
+    s_red[tid] = z;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) s_red[tid] += s_red[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const double Sd = (double)S;
+        losses[0] = (float)((double)E * aux_sum / (Sd * Sd));
+        losses[1] = (float)(s_red[0] / Sd);
+    }
+    // m-tile prefix
+    int carry = 0;
+    for (int base = 0; base < E; base += 256) {
+        const int e = base + tid;
+        const int v = e < E ? (int)ceil_div(occ[e], bm) : 0;
+        int total;
+        const int ex = block_exclusive_scan(v, s_wave, &total);
+        if (e < E) mt_start[e] = carry + ex;
+        carry += total;
+    }
+    if (tid == 0) mt_start[E] = carry;
+}
+
+// One block (4 waves) per token block; wave w takes ranks w, w+4, ...
+__global__ __launch_bounds__(256) void slot_positions_kernel(const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ hist_base,
+                                                             int S, int E, int k, int nb, int C,
+                                                             int nbits,
+                                                             int32_t* __restrict__ slot) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x;
+    const int s = b * kTokBlock + lane;
+    const bool valid = s < S;
+    const int T = k * nb;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int r = wave; r < k; r += 4) {
+        const int e = valid ? topk_idx[(size_t)s * k + r] : 0;
+        uint64_t same = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool one = (e >> bit) & 1;
+            const uint64_t ones = __ballot(one);
+            same &= one ? ones : ~ones;
+        }
+        const int before = __popcll(same & lt_mask);
+        if (valid) {
+            const int pos = hist_base[(size_t)e * T + (size_t)r * nb + b] + before;
+            slot[(size_t)s * k + r] = pos < C ? pos : -1;
+        }
+    }
+}
+
+// occ[e] = min(sum_r counts[r,e], C) and the m-tile prefix (one block).
+__global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restrict__ counts, int E,
+                                                        int k, int C, int bm,
+                                                        int32_t* __restrict__ occ,
+                                                        int32_t* __restrict__ mt_start) {
+    __shared__ int s_wave[4];
+    const int tid = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < E; base += 256) {
+        const int e = base + tid;
+        int o = 0;
+        if (e < E) {
+            long long n = 0;
+            for (int r = 0; r < k; ++r) n += counts[(size_t)r * E + e];
+            o = n < C ? (int)n : C;
+            occ[e] = o;
+        }
+        int total;
+        const int ex = block_exclusive_scan(e < E ? (int)ceil_div(o, bm) : 0, s_wave, &total);
+        if (e < E) mt_start[e] = carry + ex;
+        carry += total;
+    }
+    if (tid == 0) mt_start[E] = carry;
+}
+
+__global__ void zero_outputs_kernel(int32_t* counts, int n, float* losses) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (counts && i < n) counts[i] = 0;
+    if (losses && i < 2) losses[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t* counts,
+                            int32_t* occ, hipStream_t st) {
+    slot_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, counts, occ);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* ppart, const float* zpart, const int32_t* counts,
+                           const int32_t* occ, int S, int E, int nb, int bm, float* losses,
+                           int32_t* mt_start, hipStream_t st) {
+    finalize_kernel<<<1, 256, 0, st>>>(ppart, zpart, counts, occ, S, E, nb, bm, losses, mt_start);
+    return hipGetLastError();
+}
+
+hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
+                                 int E, int k, int nb, int C, int32_t* slot, hipStream_t st) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    slot_positions_kernel<<<nb, 256, 0, st>>>(topk_idx, hist_base, S, E, k, nb, C, nbits, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
+                            int32_t* mt_start, hipStream_t st) {
+    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, occ, mt_start);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st) {
+    const int n = n_counts > 2 ? n_counts : 2;
+    zero_outputs_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(counts, n_counts, losses);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,53 @@
+"""Convenience owner of one MoE layer's device buffers.
+
+``MoELayer`` keeps the weights, allocates the workspace and the optional
+outputs once, and calls ``moe_layer_forward``.  It only allocates torch
+tensors and forwards pointers; all computation happens in ``libmoe.so``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+class MoELayer:
+    def __init__(self, cfg: _lib.MoeConfig, w_gate, gate_bias, w1, b1, w2, b2,
+                 keep: bool = True, device="cuda"):
+        self.cfg = cfg
+        self.C = _lib.capacity(cfg)
+        self.w_gate, self.gate_bias = w_gate, gate_bias
+        self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
+        dev = torch.device(device)
+        S, d, E, k = cfg.S, cfg.d_model, cfg.E, cfg.k
+        at = cfg.torch_dtype
+        self.ws = torch.empty(_lib.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((S, d), dtype=at, device=dev)
+        self.keep = keep
+        if keep:
+            self.logits = torch.empty((S, E), dtype=torch.float32, device=dev)
+            self.topk_idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+            self.topk_w = torch.empty((S, k), dtype=torch.float32, device=dev)
+            self.slot = torch.empty((S, k), dtype=torch.int32, device=dev)
+            self.counts = torch.empty((k, E), dtype=torch.int32, device=dev)
+            self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
+            self.xd = torch.empty((E, self.C, d), dtype=at, device=dev)
+            self.out = torch.empty((E, self.C, d), dtype=at, device=dev)
+        else:
+            self.logits = self.topk_idx = self.topk_w = self.slot = None
+            self.counts = self.losses = self.xd = self.out = None
+            self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
+
+    @classmethod
+    def from_inputs(cls, cfg, inputs: dict, keep=True):
+        return cls(cfg, inputs["wg"], inputs["bg"], inputs["w1"], inputs["b1"], inputs["w2"],
+                   inputs["b2"], keep=keep, device=inputs["x"].device)
+
+    def forward(self, x, y=None, events=None, stream=None):
+        y = self.y if y is None else y
+        _lib.layer_forward(self.cfg, x, self.w_gate, self.gate_bias, self.w1, self.b1, self.w2,
+                           self.b2, y, self.ws, logits=self.logits, topk_idx=self.topk_idx,
+                           topk_w=self.topk_w, slot=self.slot, counts=self.counts,
+                           losses=self.losses, xd=self.xd, out=self.out, events=events,
+                           stream=stream)
+        return y

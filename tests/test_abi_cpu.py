@@ -1,0 +1,129 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+``include/moe.h`` declares, and refuses bad arguments on the host before any
+launch (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_wg_amd as moe
+from sparse_moe_layer_wg_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = moe.library()
+    names = declared_functions()
+    assert set(names) >= {"moe_gate", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                          "moe_layer_forward", "moe_capacity", "moe_workspace_bytes",
+                          "moe_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_config_struct_matches_header_layout():
+    # int32 x6, double, int32, uint32 -> 40 bytes with the double at offset 24
+    assert ctypes.sizeof(moe.MoeConfig) == 40
+    assert moe.MoeConfig.capacity_factor.offset == 24
+    assert moe.MoeConfig.act_dtype.offset == 32
+
+
+def test_capacity_formula():
+    for (S, E, k, cf, C) in [(256, 8, 2, 1.25, 80), (16384, 128, 2, 2.0, 512),
+                             (16384, 128, 2, 1.0, 256), (65536, 64, 2, 1.25, 2560),
+                             (8192, 256, 8, 1.5, 384), (10, 3, 1, 1.0, 4), (0, 4, 2, 1.0, 0)]:
+        assert moe.capacity(moe.config(S, 64, 64, E, k, cf)) == C
+    assert moe.capacity(moe.config(100, 64, 64, 8, 2, 1.0, capacity=7)) == 7
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_configs_rejected_on_host():
+    lib = moe.library()
+    n = ctypes.c_size_t(0)
+    bad = [
+        moe.config(-1, 64, 64, 8, 2),          # negative S
+        moe.config(10, 0, 64, 8, 2),           # d = 0
+        moe.config(10, 64, 64, 0, 1),          # E = 0
+        moe.config(10, 64, 64, 4, 5),          # k > E
+        moe.config(10, 64, 64, 4, 0),          # k = 0
+        moe.config(10, 64, 64, 4, 2, capacity_factor=0.0),
+        moe.config(10, 64, 64, 4, 2, capacity=-3),
+    ]
+    c = moe.config(10, 64, 64, 4, 2)
+    c.act_dtype = 7
+    bad.append(c)
+    c = moe.config(10, 64, 64, 4, 2)
+    c.reserved = 1
+    bad.append(c)
+    for cfg in bad:
+        assert lib.moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 1
+        assert lib.moe_capacity(ctypes.byref(cfg)) == -1
+    assert lib.moe_workspace_bytes(None, ctypes.byref(n)) == 1
+
+
+def test_unsupported_shapes_rejected_on_host():
+    lib = moe.library()
+    n = ctypes.c_size_t(0)
+    for cfg in [moe.config(10, 96, 128, 4, 2, dtype="bf16"),    # d not a multiple of 64
+                moe.config(10, 64, 100, 4, 2, dtype="bf16"),    # h not a multiple of 64
+                moe.config(10, 66, 64, 4, 2, dtype="f32"),      # d not a multiple of 4
+                moe.config(10, 64, 64, 4096, 2),                # E > 2048
+                moe.config(10, 64, 64, 16, 9)]:                 # k > 8
+        assert lib.moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 2
+
+
+def test_workspace_size_and_errors_before_launch():
+    lib = moe.library()
+    cfg = moe.config(1000, 256, 512, 16, 2, 1.0)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 0
+    C = moe.capacity(cfg)
+    assert C == 125
+    # at least H [E,C,h] + one [E,C,d] buffer in bf16
+    assert n.value >= 16 * C * (512 + 256) * 2
+    assert lib.moe_workspace_bytes(ctypes.byref(cfg), None) == 1
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    vp = lambda: fake
+    # required pointer missing -> INVALID_ARG
+    st = lib.moe_layer_forward(ctypes.byref(cfg), None, vp(), None, vp(), None, vp(), None, vp(),
+                               None, None, None, None, None, None, None, None, vp(), n.value,
+                               None, None)
+    assert st == 1
+    # workspace too small -> WORKSPACE
+    st = lib.moe_layer_forward(ctypes.byref(cfg), vp(), vp(), None, vp(), None, vp(), None, vp(),
+                               None, None, None, None, None, None, None, None, vp(), n.value - 1,
+                               None, None)
+    assert st == 3
+    # misaligned activation pointer -> INVALID_ARG
+    st = lib.moe_dispatch(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 2), vp(), vp(), vp(),
+                          None)
+    assert st == 1
+    # unknown gate flag -> INVALID_ARG
+    st = lib.moe_gate(ctypes.byref(cfg), vp(), vp(), None, None, vp(), vp(), vp(), vp(), vp(),
+                      2, vp(), n.value, None)
+    assert st == 1
+    for s in range(5):
+        assert lib.moe_status_string(s).startswith(b"MOE_")
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    cfg = moe.config(4, 64, 64, 2, 1, 1.0, dtype="f32")
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        moe.dispatch(cfg, x, torch.zeros(4, 1, dtype=torch.int32),
+                     torch.zeros(4, 1, dtype=torch.int32), torch.zeros(2, 2, 64))
+    assert _lib.MOE_NUM_STAGE_EVENTS == 9
