@@ -119,20 +119,23 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const
 }
 
 // ---------------------------------------------------------------------------
-// Route: one wavefront per token, 16 tokens per wave, 64 tokens per block
-// (one routing tile).  Lane l holds the logits of experts l, l+64, ...
+// Route: one wavefront per token at a time; a block of 16 waves (4 when
+// E > 512) owns one 64-token routing tile.  Lane l holds the logits of
+// experts l, l+64, ...
 //
 // Top-k uses a 64-bit key per logit: the order-preserving uint32 image of
 // the fp32 value (with -0 folded onto +0) above the bitwise complement of
 // the expert index, so one wave max-reduction yields the largest logit and,
 // among equal logits, the lowest index.
 //
-// Refinement: the fp32 logit GEMM accumulates differently from an exactly
-// rounded dot product.  When two consecutive values among the top k+1 lie
-// within `tau` of each other, every logit within `tau` of the (k+1)-th is
-// recomputed with fp64 accumulation, rounded once to fp32 and written back,
-// and the selection is redone; no decision is then taken on a difference
-// smaller than the GEMM's rounding error.
+// Refinement: the logit GEMM accumulates in fp32, so its values can differ
+// by a few ulps from exactly rounded dot products.  The ordered top-k depends
+// only on the comparisons between sorted neighbours r, r+1 for r < k.  When
+// such a pair differs by less than `tau` (well above the GEMM's error), the
+// chain of sorted neighbours linked by differences below tau is recomputed
+// with fp64 accumulation, rounded once to fp32 (the stored logits are
+// overwritten) and the selection is redone.  Experts outside the chain differ
+// from it by at least tau, so their order against it is already certain.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -145,37 +148,109 @@ __device__ __forceinline__ int key_index(uint64_t key) {
     return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key & 0xffffffffu));
 }
 
+constexpr int kMaxSel = 16;  // sorted positions examined for near-tie clusters
+
+// Next-largest key among the experts not yet taken (wave-uniform result);
+// marks it taken in the owner lane's bitmask.
 template <int EQ>
-__device__ __forceinline__ void select_topn(const float (&v)[EQ], int E, int lane, int n,
-                                            uint64_t (&top)[kMaxK + 1]) {
-    uint32_t taken = 0;
+__device__ __forceinline__ uint64_t select_next(const float (&v)[EQ], int E, int lane,
+                                                uint32_t& taken) {
+    uint64_t best = 0;
 #pragma unroll
-    for (int r = 0; r < kMaxK + 1; ++r) {
-        if (r >= n) break;
-        uint64_t best = 0;
+    for (int q = 0; q < EQ; ++q) {
+        const int j = lane + kWave * q;
+        if (j < E && !((taken >> q) & 1u)) {
+            uint64_t key = (static_cast<uint64_t>(float_order_key(v[q])) << 32) |
+                           (0xffffffffu - static_cast<uint32_t>(j));
+            best = key > best ? key : best;
+        }
+    }
+    best = wave_max_u64(best);
+    // every lane holds the same key: keep it in scalar registers
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(best >> 32));
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(best));
+    best = (static_cast<uint64_t>(hi) << 32) | lo;
+    const int j = key_index(best);
+    if ((j & (kWave - 1)) == lane) taken |= 1u << (j / kWave);
+    return best;
+}
+
+// fp64 dot products x[s,:] . wg[j_u,:] (+ bg) for up to four experts, rounded
+// once to fp32.  Lanes take 8-element (bf16) or 4-element (fp32) chunks.
+__device__ __forceinline__ void refine_group(const RouteParams& p, int s, const int (&js)[4],
+                                             float (&nv)[4]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (p.x_bf16) {
+        const bf16_t* xr = static_cast<const bf16_t*>(p.x) + (size_t)s * p.d;
+#pragma unroll 1
+        for (int i = lane * 8; i < p.d; i += kWave * 8) {
+            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(xr + i);
+            float xv[8];
 #pragma unroll
-        for (int q = 0; q < EQ; ++q) {
-            const int j = lane + kWave * q;
-            if (j < E && !((taken >> q) & 1u)) {
-                uint64_t key = (static_cast<uint64_t>(float_order_key(v[q])) << 32) |
-                               (0xffffffffu - static_cast<uint32_t>(j));
-                best = key > best ? key : best;
+            for (int q = 0; q < 4; ++q) {
+                xv[2 * q] = __uint_as_float(raw[q] << 16);
+                xv[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (js[u] < 0) continue;
+                const f32x4_t* wr = reinterpret_cast<const f32x4_t*>(p.wg + (size_t)js[u] * p.d + i);
+                const f32x4_t w0 = wr[0], w1 = wr[1];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[u] += (double)xv[q] * (double)w0[q];
+                    acc[u] += (double)xv[4 + q] * (double)w1[q];
+                }
             }
         }
-        best = wave_max_u64(best);
-        top[r] = best;
-        const int j = key_index(best);
-        if ((j & (kWave - 1)) == lane) taken |= 1u << (j / kWave);
+    } else {
+        const float* xr = static_cast<const float*>(p.x) + (size_t)s * p.d;
+#pragma unroll 1
+        for (int i = lane * 4; i < p.d; i += kWave * 4) {
+            const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xr + i);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (js[u] < 0) continue;
+                const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(p.wg + (size_t)js[u] * p.d + i);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u] += (double)xv[q] * (double)w0[q];
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        double t = wave_sum_f64(acc[u]);
+        if (js[u] >= 0 && p.bg) t += (double)p.bg[js[u]];
+        nv[u] = (float)t;
     }
 }
 
+// Replaces the logits of experts js[u] by nv[u]: in the owner lane's
+// registers and in the stored logits row.
 template <int EQ>
-__global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
+__device__ __forceinline__ void apply_refined(float (&v)[EQ], float* lrow, const int (&js)[4],
+                                              const float (&nv)[4], int lane) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = js[u];
+        if (j < 0 || (j & (kWave - 1)) != lane) continue;
+#pragma unroll
+        for (int q = 0; q < EQ; ++q)
+            if (q == (j >> 6)) v[q] = nv[u];
+        lrow[j] = nv[u];
+    }
+}
+
+// NW waves per block share one 64-token routing tile, 64/NW tokens each.
+template <int EQ, int NW>
+__global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
     extern __shared__ unsigned char smem[];
     const int E = p.E, k = p.k, nb = p.nb;
     int* s_hist = reinterpret_cast<int*>(smem);                 // [k][E]
-    float* s_p = reinterpret_cast<float*>(s_hist + k * E);      // [4][E]
-    __shared__ float s_z[4];
+    float* s_p = reinterpret_cast<float*>(s_hist + k * E);      // [NW][E]
+    __shared__ float s_z[NW];
+    __shared__ int s_cand[NW][kMaxSel];
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int b = blockIdx.x;
@@ -188,8 +263,8 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
     float zacc = 0.f;
     const int nsel = k + 1 <= E ? k + 1 : E;
 
-    for (int t = 0; t < kTokBlock / 4; ++t) {
-        const int s = b * kTokBlock + wave * (kTokBlock / 4) + t;
+    for (int t = 0; t < kTokBlock / NW; ++t) {
+        const int s = b * kTokBlock + wave * (kTokBlock / NW) + t;
         if (s >= p.S) break;
         float* lrow = p.logits + (size_t)s * E;
         float v[EQ];
@@ -198,50 +273,76 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
             const int j = lane + kWave * q;
             v[q] = j < E ? lrow[j] : 0.f;
         }
-        uint64_t top[kMaxK + 1];
-        select_topn<EQ>(v, E, lane, nsel, top);
+        // top[r]: key of the r-th largest logit (wave-uniform)
+        uint64_t top[kMaxSel];
+        uint32_t taken = 0;
+#pragma unroll
+        for (int r = 0; r < kMaxK + 1; ++r)
+            if (r < nsel) top[r] = select_next<EQ>(v, E, lane, taken);
 
-        if (p.tau > 0.f) {
-            bool close = false;
-            float last = key_value(top[0]);
+        if (p.tau > 0.f && nsel > 1) {
+            // Pair r joins sorted positions r and r+1 and is "close" when their
+            // difference is below tau.  Pairs r < k decide the ordered top-k.
+            bool need = false;
 #pragma unroll
-            for (int r = 0; r < kMaxK; ++r) {
-                if (r + 1 < nsel) {
-                    close |= (key_value(top[r]) - key_value(top[r + 1])) < p.tau;
-                    last = key_value(top[r + 1]);
+            for (int r = 0; r < kMaxK; ++r)
+                if (r < k && r + 1 < nsel)
+                    need |= key_value(top[r]) - key_value(top[r + 1]) < p.tau;
+            if (need) {
+                // follow a chain of close pairs past position k
+                int n = nsel;
+#pragma unroll
+                for (int r = 2; r < kMaxSel; ++r) {
+                    if (r == n && n < E && key_value(top[r - 2]) - key_value(top[r - 1]) < p.tau) {
+                        top[r] = select_next<EQ>(v, E, lane, taken);
+                        ++n;
+                    }
                 }
-            }
-            if (close) {
-                const float thr = last - p.tau;
+                const bool overflow =
+                    n == kMaxSel && n < E &&
+                    key_value(top[kMaxSel - 2]) - key_value(top[kMaxSel - 1]) < p.tau;
+                int ncand = 0;
+                if (!overflow) {
+                    // members of the close chains that contain a pair r < k
+                    uint32_t closebits = 0;
 #pragma unroll
-                for (int q = 0; q < EQ; ++q) {
-                    const int jl = lane + kWave * q;
-                    uint64_t cand = __ballot(jl < E && v[q] >= thr);
-                    while (cand) {
-                        const int cl = __ffsll(static_cast<long long>(cand)) - 1;
-                        cand &= cand - 1;
-                        const int j = cl + kWave * q;
-                        const float* wr = p.wg + (size_t)j * p.d;
-                        double acc = 0.0;
-                        if (p.x_bf16) {
-                            const bf16_t* xr = static_cast<const bf16_t*>(p.x) + (size_t)s * p.d;
-                            for (int i = lane; i < p.d; i += kWave)
-                                acc += (double)bf16_to_f32(xr[i]) * (double)wr[i];
-                        } else {
-                            const float* xr = static_cast<const float*>(p.x) + (size_t)s * p.d;
-                            for (int i = lane; i < p.d; i += kWave)
-                                acc += (double)xr[i] * (double)wr[i];
+                    for (int r = 0; r + 1 < kMaxSel; ++r)
+                        if (r + 1 < n && key_value(top[r]) - key_value(top[r + 1]) < p.tau)
+                            closebits |= 1u << r;
+                    uint32_t members = 0;
+                    int r = 0;
+                    while (r + 1 < n) {
+                        if (!((closebits >> r) & 1u)) {
+                            ++r;
+                            continue;
                         }
-                        acc = wave_sum_f64(acc);
-                        if (p.bg) acc += (double)p.bg[j];
-                        const float nv = (float)acc;
-                        if (lane == cl) {
-                            v[q] = nv;
-                            lrow[j] = nv;
+                        const int a = r;
+                        while (r + 1 < n && ((closebits >> r) & 1u)) ++r;
+                        if (a < k) members |= ((2u << r) - 1u) & ~((1u << a) - 1u);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kMaxSel; ++q) {
+                        if ((members >> q) & 1u) {
+                            s_cand[wave][ncand] = key_index(top[q]);
+                            ++ncand;
                         }
                     }
                 }
-                select_topn<EQ>(v, E, lane, k, top);
+                // a chain longer than kMaxSel: refine every logit of the token
+                const int total = overflow ? E : ncand;
+                for (int g = 0; g < total; g += 4) {
+                    int js[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        js[u] = g + u < total ? (overflow ? g + u : s_cand[wave][g + u]) : -1;
+                    float nv[4];
+                    refine_group(p, s, js, nv);
+                    apply_refined<EQ>(v, lrow, js, nv, lane);
+                }
+                taken = 0;
+#pragma unroll
+                for (int r = 0; r < kMaxK; ++r)
+                    if (r < k) top[r] = select_next<EQ>(v, E, lane, taken);
             }
         }
 
@@ -286,9 +387,18 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
     }
     if (lane == 0) s_z[wave] = zacc;
     __syncthreads();
-    for (int j = tid; j < E; j += blockDim.x)
-        p.ppart[(size_t)b * E + j] = ((s_p[j] + s_p[E + j]) + s_p[2 * E + j]) + s_p[3 * E + j];
-    if (tid == 0) p.zpart[b] = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
+    for (int j = tid; j < E; j += blockDim.x) {
+        float a = s_p[j];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) a += s_p[w * E + j];
+        p.ppart[(size_t)b * E + j] = a;
+    }
+    if (tid == 0) {
+        float a = s_z[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) a += s_z[w];
+        p.zpart[b] = a;
+    }
     const int T = k * nb;
     for (int i = tid; i < k * E; i += blockDim.x) {
         const int r = i / E, e = i - r * E;
@@ -296,25 +406,25 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
     }
 }
 
-template <int EQ>
+template <int EQ, int NW>
 hipError_t launch_route_t(const RouteParams& p, hipStream_t st) {
-    const size_t lds = sizeof(int) * (size_t)p.k * p.E + sizeof(float) * 4 * (size_t)p.E;
+    const size_t lds = sizeof(int) * (size_t)p.k * p.E + sizeof(float) * NW * (size_t)p.E;
     if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<EQ>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<EQ, NW>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    route_kernel<EQ><<<p.nb, 256, lds, st>>>(p);
+    route_kernel<EQ, NW><<<p.nb, NW * 64, lds, st>>>(p);
     return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_route(const RouteParams& p, hipStream_t st) {
     const int eq = (int)ceil_div(p.E, kWave);
-    if (eq <= 1) return launch_route_t<1>(p, st);
-    if (eq <= 2) return launch_route_t<2>(p, st);
-    if (eq <= 4) return launch_route_t<4>(p, st);
-    if (eq <= 8) return launch_route_t<8>(p, st);
-    if (eq <= 16) return launch_route_t<16>(p, st);
-    return launch_route_t<32>(p, st);
+    if (eq <= 1) return launch_route_t<1, 16>(p, st);
+    if (eq <= 2) return launch_route_t<2, 16>(p, st);
+    if (eq <= 4) return launch_route_t<4, 16>(p, st);
+    if (eq <= 8) return launch_route_t<8, 16>(p, st);
+    if (eq <= 16) return launch_route_t<16, 4>(p, st);
+    return launch_route_t<32, 4>(p, st);
 }
 
 }  // namespace moe

@@ -30,11 +30,12 @@ hipError_t launch_route(const RouteParams& p, hipStream_t st);
 
 // ------------------------------------------------------------------ slots
 // In-place exclusive scan of hist rows (per expert, over (rank, block)
-// tiles); writes counts [k,E] and occupancy occ[e] = min(n_e, C).
+// tiles); writes counts [k,E], occupancy occ[e] = min(n_e, C) and
+// psum[e] = sum over blocks of ppart[b][e].
 hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t* counts,
-                            int32_t* occ, hipStream_t st);
+                            int32_t* occ, const float* ppart, double* psum, hipStream_t st);
 // losses = {aux, z}; mt_start[e] = sum_{e'<e} ceil(occ[e']/bm) (E+1 entries).
-hipError_t launch_finalize(const float* ppart, const float* zpart, const int32_t* counts,
+hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
                            const int32_t* occ, int S, int E, int nb, int bm, float* losses,
                            int32_t* mt_start, hipStream_t st);
 // slot[s,r] from the scanned tile bases and stable in-tile ranks.

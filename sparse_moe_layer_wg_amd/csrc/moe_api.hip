@@ -59,11 +59,12 @@ moe_status make_plan(const moe_config* c, Plan* pl) {
 }
 
 // Workspace layout, every region 256-byte aligned:
-//   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, occ, mt_start
+//   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
+//            mt_start
 //   [ffn]    H [E,C,h]
 //   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
 struct Carve {
-    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, occ, mt_start;
+    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -86,6 +87,7 @@ Carve carve(const Plan& p) {
     c.hist = take((size_t)p.E * p.k * p.nb * 4);
     c.ppart = take((size_t)p.nb * p.E * 4);
     c.zpart = take((size_t)p.nb * 4);
+    c.psum = take((size_t)p.E * 8);
     c.occ = take((size_t)p.E * 4);
     c.mt_start = take((size_t)(p.E + 1) * 4);
     c.route_end = o;
@@ -124,6 +126,7 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     int32_t* hist = at<int32_t>(ws, cv.hist);
     float* ppart = at<float>(ws, cv.ppart);
     float* zpart = at<float>(ws, cv.zpart);
+    double* psum = at<double>(ws, cv.psum);
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
     if (!logits_in) MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, st));
@@ -147,8 +150,8 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     rp.zpart = zpart;
     MOE_TRY(launch_route(rp, st));
     record(ev, 2, st);
-    MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, st));
-    MOE_TRY(launch_finalize(ppart, zpart, counts, occ, p.S, p.E, p.nb, gemm_block_m(p.bf16),
+    MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, ppart, psum, st));
+    MOE_TRY(launch_finalize(psum, zpart, counts, occ, p.S, p.E, p.nb, gemm_block_m(p.bf16),
                             losses, mt, st));
     record(ev, 3, st);
     MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, st));

@@ -39,14 +39,29 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
     return before + incl - v;
 }
 
-// One block per expert: hist[e][0..T) becomes the exclusive positions.
+// One block per expert: hist[e][0..T) becomes the exclusive positions;
+// counts[r,e] and occ[e] follow.  The block also sums the router's per-block
+// probability partials of expert e into psum[e] (fixed assignment of blocks to
+// threads and a fixed tree, so the sum is deterministic).
 __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hist, int E, int k,
                                                         int nb, int C,
                                                         int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ occ) {
+                                                        int32_t* __restrict__ occ,
+                                                        const float* __restrict__ ppart,
+                                                        double* __restrict__ psum) {
     __shared__ int s_wave[4];
     __shared__ int s_rank_start[kMaxK + 1];
+    __shared__ double s_red[256];
     const int e = blockIdx.x, tid = threadIdx.x;
+    double pa = 0.0;
+    for (int b = tid; b < nb; b += 256) pa += (double)ppart[(size_t)b * E + e];
+    s_red[tid] = pa;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) s_red[tid] += s_red[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) psum[e] = s_red[0];
     const int T = k * nb;
     int32_t* row = hist + (size_t)e * T;
     int carry = 0;
@@ -70,11 +85,11 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hi
     if (tid == 0) occ[e] = carry < C ? carry : C;
 }
 
-// aux = E * sum_j f_j P_j with f_j = counts[0,j] / S and P_j = (sum of the
-// block partials of p[:,j]) / S;  z = (sum of block partials of lse^2) / S.
-// Partials are summed in a fixed order in fp64, so the result is
-// deterministic.  Also the per-expert m-tile prefix for the expert GEMMs.
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ ppart,
+// aux = E * sum_j f_j P_j with f_j = counts[0,j] / S and P_j = psum[j] / S;
+// z = (sum of the block partials of lse^2) / S.  Sums run in a fixed order
+// in fp64, so the result is deterministic.  Also the per-expert m-tile
+// prefix for the expert GEMMs.
+__global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict__ psum,
                                                        const float* __restrict__ zpart,
                                                        const int32_t* __restrict__ counts,
                                                        const int32_t* __restrict__ occ, int S,
@@ -85,11 +100,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
     double term = 0.0;
-    for (int j = tid; j < E; j += 256) {
-        double P = 0.0;
-        for (int b = 0; b < nb; ++b) P += (double)ppart[(size_t)b * E + j];
-        term += (double)counts[j] * P;
-    }
+    for (int j = tid; j < E; j += 256) term += (double)counts[j] * psum[j];
     s_red[tid] = term;
     __syncthreads();
     for (int off = 128; off >= 1; off >>= 1) {
@@ -186,15 +197,15 @@ __global__ void zero_outputs_kernel(int32_t* counts, int n, float* losses) {
 }  // namespace
 
 hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t* counts,
-                            int32_t* occ, hipStream_t st) {
-    slot_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, counts, occ);
+                            int32_t* occ, const float* ppart, double* psum, hipStream_t st) {
+    slot_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, counts, occ, ppart, psum);
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const float* ppart, const float* zpart, const int32_t* counts,
+hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
                            const int32_t* occ, int S, int E, int nb, int bm, float* losses,
                            int32_t* mt_start, hipStream_t st) {
-    finalize_kernel<<<1, 256, 0, st>>>(ppart, zpart, counts, occ, S, E, nb, bm, losses, mt_start);
+    finalize_kernel<<<1, 256, 0, st>>>(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start);
     return hipGetLastError();
 }
 

@@ -196,3 +196,46 @@ def test_full_size_sampled(name):
     _print(name, rep)
     del layer, inputs
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------- near-tie refinement
+def test_duplicated_router_rows_exact_ties():
+    """Router rows duplicated in pairs: every token has exactly tied logits,
+    so every token goes through the fp64 re-evaluation; ties must resolve to
+    the lower expert index exactly as in the oracle."""
+    w = mw.Workload("dup_rows", S=2000, d=512, h=128, E=64, k=4, capacity_factor=1.0,
+                    dtype="bf16", seed=31)
+    inputs = mw.generate(w, "cuda")
+    inputs["wg"] = inputs["wg"][0::2].repeat_interleave(2, dim=0).contiguous()
+    inputs, layer = run_layer(w, inputs)
+    rep = check_layer(w, inputs, layer, full=True)
+    _print(w.name, rep)
+    idx = layer.topk_idx.cpu().numpy()
+    # the lower index of each tied pair always comes first
+    for r in range(w.k - 1):
+        pair = (idx[:, r] // 2 == idx[:, r + 1] // 2)
+        assert np.all(idx[pair, r] < idx[pair, r + 1])
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 2), (40, 8)])
+def test_zero_router_closed_form(E, k):
+    """All-zero router weight: every logit is 0, so the top-k is (0..k-1) with
+    weights 1/k, aux = 1, z = (ln E)^2 and the first C tokens of each rank are
+    kept.  E = 64 drives the re-evaluation through its longest-chain path."""
+    S, d, h = 300, 64, 64
+    cf = 1.0
+    w = mw.Workload("zero_router", S=S, d=d, h=h, E=E, k=k, capacity_factor=cf, dtype="bf16",
+                    seed=41)
+    inputs = mw.generate(w, "cuda")
+    inputs["wg"].zero_()
+    inputs, layer = run_layer(w, inputs)
+    C = layer.C
+    idx = layer.topk_idx.cpu().numpy()
+    assert np.all(idx == np.arange(k)[None, :])
+    assert np.allclose(layer.topk_w.cpu().numpy(), 1.0 / k, rtol=1e-6)
+    s = np.arange(S)
+    for r in range(k):
+        assert np.array_equal(layer.slot.cpu().numpy()[:, r], np.where(s < C, s, -1))
+    aux, z = layer.losses.cpu().numpy()
+    assert abs(aux - 1.0) <= 1e-5 and abs(z - np.log(E) ** 2) <= 1e-5 * np.log(E) ** 2
+    _print(f"zero_router_E{E}", check_layer(w, inputs, layer, full=True))
