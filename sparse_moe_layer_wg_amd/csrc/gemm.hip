@@ -10,126 +10,229 @@
 // Both are "A . B^T" with A [E,C,K] and B [E,N,K] row-major, K contiguous in
 // both operands, which is the operand order the MFMA fragments want.
 //
-// bf16 path: gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulation.  Block tile
-// 128x128x64, four waves in a 2x2 grid, each wave 64x64 = 2x2 MFMA tiles.
-// Operand tiles are staged in LDS (rows padded by 16 bytes so that the
-// 16-byte fragment reads of 8 consecutive rows fall in distinct banks) and
-// double-buffered: the global loads of tile k+1 are in flight while the
-// MFMAs consume tile k.  Blocks whose m-tile lies past the expert's
-// occupancy exit at once, so empty experts and empty slots cost nothing
-// beyond a launch slot.
+// bf16 path: gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+//   Block tile BM x 256 x 64 (BM = 128 or 256), 256 threads = 4 waves in a
+//   2x2 grid; each wave owns a (BM/2) x 128 block of accumulators, i.e.
+//   (BM/64) x 4 MFMA tiles of 32x32 (up to 256 fp32 per lane, held in AGPRs).
+//   A wave tile this large keeps LDS traffic per MFMA low and halves the L2
+//   traffic of a 128x128 tile.
+//   Operands are staged through registers into two LDS buffers: the global
+//   loads of k-tile t+1 are spread over the MFMAs of the first 16-wide step
+//   of tile t and their LDS stores over the MFMAs of the last step, and the
+//   fragments of the next step are read from LDS while the current MFMAs run
+//   (instruction groups placed with sched_group_barrier; a wave issues in
+//   order, so bursts of memory instructions would stall its MFMAs).  Plain
+//   vector loads are used rather than global->LDS copies: on gfx950 the copy
+//   path moves about 16 bytes per clock per CU, a quarter of the load path.
+//   LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so that the
+//   fragment reads of 16 consecutive rows hit distinct bank groups.  Rows
+//   past an expert's occupancy (and columns past N) load a clamped valid row;
+//   their results are never stored.
+//   Tiles come from a compact list: expert e owns m-tiles
+//   [mt_start[e], mt_start[e+1]) (built on the device from the occupancies),
+//   ordered (expert, n-tile, m-tile).  The grid is persistent, one block per
+//   CU; block b runs on XCD b % 8, XCD x owns the x-th eighth of the list and
+//   its blocks walk it in rounds, so the blocks of one XCD work on
+//   neighbouring tiles (sharing A and B tiles through L2) at the same time.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+constexpr int BN = 256;
 
-template <bool RELU>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) bf16_t As[2][BM][LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN][LDK];
+// Physical 16-byte chunk of logical chunk c in a row of CH chunks.  A
+// fragment read has the lanes of a 16-lane group read 16 consecutive rows at
+// one logical chunk; the XOR pattern spreads those 16 reads over distinct
+// 16-byte bank groups of a 256-byte LDS line (and any aligned 8 of them over
+// a 128-byte line), so 128-bit reads are conflict-free.
+template <int CH>
+__device__ __forceinline__ int swz(int row, int c) {
+    return CH == 8 ? (c ^ ((row ^ (row >> 3)) & 7)) : (c ^ (((row >> 1) ^ (row >> 3)) & 3));
+}
 
-    const int e = blockIdx.z;
-    const int M = p.occ[e];
-    const int m0 = blockIdx.y * BM;
-    if (m0 >= M) return;
-    const int n0 = blockIdx.x * BN;
+// WNC waves along N (2 or 4), 2 along M: 4 or 8 waves per block.
+template <int BM, int WNC, bool RELU>
+__global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
+    constexpr int NTH = 128 * WNC;             // threads per block
+    constexpr int BK = 64, CH = BK / 8;        // k-tile; 16-byte chunks per row
+    constexpr int WM = BM / 2, WNT = BN / WNC; // wave tile
+    constexpr int TM = WM / 32, TN = WNT / 32; // 32x32 MFMA tiles per wave
+    constexpr int KS = BK / 16;                // MFMA k steps per k-tile
+    constexpr int A_CH = BM * CH / NTH;        // A chunks per thread per k-tile
+    constexpr int B_CH = BN * CH / NTH;        // B chunks per thread per k-tile
+    constexpr int STAGE = (BM + BN) * CH;      // chunks per LDS buffer
+    __shared__ u32x4_t smem[2 * STAGE];
+
     const int N = p.N, K = p.K;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-    const int wm = wave >> 1, wn = wave & 1;
-
-    const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A) + (size_t)e * p.C * K;
-    const bf16_t* __restrict__ B = static_cast<const bf16_t*>(p.B) + (size_t)e * N * K;
-
-    // Loader: the 128x64 tile is 1024 16-byte chunks, 4 per thread; chunk
-    // c covers row c/8, columns (c%8)*8 .. +8.
-    u32x4_t ra[4], rb[4];
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-            ra[i] = (m0 + row < M)
-                        ? *reinterpret_cast<const u32x4_t*>(A + (size_t)(m0 + row) * K + k0 + col)
-                        : zero;
-            rb[i] = (n0 + row < N)
-                        ? *reinterpret_cast<const u32x4_t*>(B + (size_t)(n0 + row) * K + k0 + col)
-                        : zero;
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-            *reinterpret_cast<u32x4_t*>(&As[buf][row][col]) = ra[i];
-            *reinterpret_cast<u32x4_t*>(&Bs[buf][row][col]) = rb[i];
-        }
-    };
-
-    f32x16_t acc[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
+    const int NT = (N + BN - 1) / BN;
+    const int T = p.mt_start[p.E] * NT;
+    const int per = (T + 7) >> 3;
+    const int xcd = blockIdx.x & 7, nslot = gridDim.x >> 3;
+    const int t_end = min(T, (xcd + 1) * per);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WNC, wn = wave % WNC;
+    const int frow = lane & 31, fhalf = lane >> 5;
     const int KT = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    // Fragment addressing (32x32x16): lane l supplies row l%32 and the 8
-    // consecutive k starting at (l/32)*8 of the 16-wide k-step.
-    const int frow = lane & 31, fk = (lane >> 5) * 8;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) gload((kt + 1) * BK);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t a[2], b[2];
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                a[mi] = *reinterpret_cast<const bf16x8_t*>(
-                    &As[buf][wm * 64 + mi * 32 + frow][ks * 16 + fk]);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                b[ni] = *reinterpret_cast<const bf16x8_t*>(
-                    &Bs[buf][wn * 64 + ni * 32 + frow][ks * 16 + fk]);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni],
-                                                                         acc[mi][ni], 0, 0, 0);
-        }
-        if (kt + 1 < KT) sstore(buf ^ 1);
-        __syncthreads();
-    }
 
-    // Epilogue.  32x32 accumulator layout: lane l holds column l%32; register
-    // r holds row 8*(r/4) + 4*(l/32) + r%4.
-    bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) + (size_t)e * p.C * N;
-    const bf16_t* bias = p.bias ? static_cast<const bf16_t*>(p.bias) + (size_t)e * N : nullptr;
+    for (int t = xcd * per + (blockIdx.x >> 3); t < t_end; t += nslot) {
+        // expert of tile t: the largest e with mt_start[e] <= t / NT
+        const int q = t / NT;
+        int lo = 0, hi = p.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.mt_start[mid] <= q) lo = mid; else hi = mid - 1;
+        }
+        const int e = lo;
+        const int mtiles = p.mt_start[e + 1] - p.mt_start[e];
+        const int local = t - p.mt_start[e] * NT;
+        const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * BN;
+        const int M = p.occ[e];
+        const char* __restrict__ Ab =
+            reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.A) + (size_t)e * p.C * K);
+        const char* __restrict__ Bb =
+            reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.B) + (size_t)e * N * K);
+
+        // Loader: chunk c = tid + NTH*i covers row c/CH, columns (c%CH)*8..+8
+        // of the k-tile; it is stored at its swizzled LDS position.
+        uint32_t aoff[A_CH], boff[B_CH];
+        int alds[A_CH], blds[B_CH];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-        const int n = n0 + wn * 64 + ni * 32 + (lane & 31);
-        if (n >= N) continue;
-        const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+        for (int i = 0; i < A_CH; ++i) {
+            const int c = tid + NTH * i, row = c / CH, ch = c % CH;
+            aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)ch * 16u;
+            alds[i] = row * CH + swz<CH>(row, ch);
+        }
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
+        for (int i = 0; i < B_CH; ++i) {
+            const int c = tid + NTH * i, row = c / CH, ch = c % CH;
+            boff[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K * 2u + (uint32_t)ch * 16u;
+            blds[i] = BM * CH + row * CH + swz<CH>(row, ch);
+        }
+        u32x4_t ra[A_CH], rb[B_CH];
+        auto gload = [&](int kt) {
+            const uint32_t kb = (uint32_t)kt * BK * 2u;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M) {
-                    float v = acc[mi][ni][r] + bv;
-                    if (RELU) v = v > 0.f ? v : 0.f;
-                    Cout[(size_t)m * N + n] = f32_to_bf16(v);
+            for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(Ab + aoff[i] + kb);
+#pragma unroll
+            for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(Bb + boff[i] + kb);
+        };
+        auto sstore = [&](int buf) {
+            u32x4_t* st = smem + buf * STAGE;
+#pragma unroll
+            for (int i = 0; i < A_CH; ++i) st[alds[i]] = ra[i];
+#pragma unroll
+            for (int i = 0; i < B_CH; ++i) st[blds[i]] = rb[i];
+        };
+
+        // Fragment (32x32x16): lane l supplies row l%32 and the 8 consecutive
+        // k at (l/32)*8 of the 16-wide step, i.e. logical chunk 2*ks + l/32.
+        bf16x8_t fa[2][TM], fb[2][TN];
+        auto load_frags = [&](const u32x4_t* st, int ks, int slot) {
+            const u32x4_t* sb = st + BM * CH;
+            const int c = 2 * ks + fhalf;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM + i * 32 + frow;
+                fa[slot][i] = __builtin_bit_cast(bf16x8_t, st[row * CH + swz<CH>(row, c)]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn * WNT + j * 32 + frow;
+                fb[slot][j] = __builtin_bit_cast(bf16x8_t, sb[row * CH + swz<CH>(row, c)]);
+            }
+        };
+
+        f32x16_t acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+        gload(0);
+        sstore(0);
+        __syncthreads();
+
+        // One k-tile from LDS buffer kt&1.  With REFILL, k-tile kt+1 is loaded
+        // into registers during the first step and stored to the other buffer
+        // (which every wave finished reading before the previous barrier)
+        // during the last step.
+        auto ktile = [&](auto refill_tag, int kt) {
+            constexpr bool REFILL = decltype(refill_tag)::value;
+            constexpr int NL = A_CH + B_CH;   // loads (and stores) per thread
+            const u32x4_t* st = smem + (kt & 1) * STAGE;
+            load_frags(st, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if constexpr (REFILL) {
+                    if (ks == 0) gload(kt + 1);
+                    if (ks == KS - 1) sstore((kt + 1) & 1);
+                }
+                if (ks + 1 < KS) load_frags(st, ks + 1, (ks + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+                // instruction groups: spread memory instructions over the MFMAs
+                if (REFILL && ks == 0) {
+#pragma unroll
+                    for (int g = 0; g < NL; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+                        if (g < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN + NL - 1) / NL, 0);
+                    }
+                } else if (REFILL && ks == KS - 1) {
+#pragma unroll
+                    for (int g = 0; g < NL; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // LDS write
+                        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN + NL - 1) / NL, 0);
+                    }
+                } else if (ks + 1 < KS) {
+#pragma unroll
+                    for (int g = 0; g < TM + TN; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+        };
+        int kt = 0;
+        for (; kt + 1 < KT; ++kt) ktile(std::true_type{}, kt);
+        ktile(std::false_type{}, kt);
+
+        // Epilogue.  32x32 accumulator layout: lane l holds column l%32;
+        // register r holds row 8*(r/4) + 4*(l/32) + r%4.
+        bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) + (size_t)e * p.C * N;
+        const bf16_t* bias = p.bias ? static_cast<const bf16_t*>(p.bias) + (size_t)e * N : nullptr;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * WNT + j * 32 + frow;
+            if (n >= N) continue;
+            const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                    if (m < M) {
+                        float v = acc[i][j][r] + bv;
+                        if (RELU) v = v > 0.f ? v : 0.f;
+                        Cout[(size_t)m * N + n] = f32_to_bf16(v);
+                    }
                 }
             }
         }
-    }
+    }  // tile loop
 }
 
 // fp32 activations: LDS-tiled fp32 FMA, tile 64x64x16, 4x4 outputs per
@@ -202,16 +305,46 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 
 }  // namespace
 
-int gemm_block_m(bool bf16) { return bf16 ? BM : FM; }
+// Compute units of the current device (one-time query per process and device).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 8)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
-hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, hipStream_t st) {
+// m-tile height: 256 when experts average at least 160 rows (each weight
+// tile is then streamed once per expert and a 256x256 tile halves operand
+// traffic per flop), else 128 so that lightly filled experts waste less.
+int gemm_block_m(bool bf16, int S, int E, int k) {
+    if (!bf16) return FM;
+    const long long avg = (long long)S * k / (E > 0 ? E : 1);
+    return avg >= 160 ? 256 : 128;
+}
+
+hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, int bm, hipStream_t st) {
     if (p.E == 0 || p.C == 0) return hipSuccess;
     if (bf16) {
-        dim3 grid((unsigned)ceil_div(p.N, BN), (unsigned)ceil_div(p.C, BM), (unsigned)p.E);
-        if (p.relu)
-            gemm_bf16_kernel<true><<<grid, 256, 0, st>>>(p);
-        else
-            gemm_bf16_kernel<false><<<grid, 256, 0, st>>>(p);
+        // persistent grid: one block per CU (the LDS stages fill a CU), at most
+        // one per possible tile, a multiple of the 8 XCDs
+        const long long tiles = (long long)p.E * ceil_div(p.C, bm) * ceil_div(p.N, BN);
+        const long long slots = (long long)(device_cus() / 8) * 8;
+        const unsigned grid = (unsigned)(tiles < slots ? ceil_div(tiles, 8) * 8 : slots);
+        // 8 waves (2 per SIMD): the second wave fills MFMA gaps while one waits
+        if (bm == 256) {
+            if (p.relu) gemm_bf16_kernel<256, 4, true><<<grid, 512, 0, st>>>(p);
+            else gemm_bf16_kernel<256, 4, false><<<grid, 512, 0, st>>>(p);
+        } else {
+            if (p.relu) gemm_bf16_kernel<128, 4, true><<<grid, 512, 0, st>>>(p);
+            else gemm_bf16_kernel<128, 4, false><<<grid, 512, 0, st>>>(p);
+        }
     } else {
         dim3 grid((unsigned)ceil_div(p.N, FN), (unsigned)ceil_div(p.C, FM), (unsigned)p.E);
         if (p.relu)

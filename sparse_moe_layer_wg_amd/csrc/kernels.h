@@ -69,7 +69,9 @@ struct GemmParams {
     int E, C, N, K;
     bool relu;
 };
-int gemm_block_m(bool bf16);
-hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, hipStream_t st);
+// m-tile height the expert GEMMs use for a layer shape (the m-tile prefix
+// mt_start must be built with the same value).
+int gemm_block_m(bool bf16, int S, int E, int k);
+hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, int bm, hipStream_t st);
 
 }  // namespace moe

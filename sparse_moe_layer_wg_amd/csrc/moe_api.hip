@@ -151,7 +151,7 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     MOE_TRY(launch_route(rp, st));
     record(ev, 2, st);
     MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, ppart, psum, st));
-    MOE_TRY(launch_finalize(psum, zpart, counts, occ, p.S, p.E, p.nb, gemm_block_m(p.bf16),
+    MOE_TRY(launch_finalize(psum, zpart, counts, occ, p.S, p.E, p.nb, gemm_block_m(p.bf16, p.S, p.E, p.k),
                             losses, mt, st));
     record(ev, 3, st);
     MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, st));
@@ -174,7 +174,7 @@ moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1
     g.N = p.h;
     g.K = p.d;
     g.relu = true;
-    MOE_TRY(launch_expert_gemm(g, p.bf16, st));
+    MOE_TRY(launch_expert_gemm(g, p.bf16, gemm_block_m(p.bf16, p.S, p.E, p.k), st));
     record(ev, 6, st);
     g.A = H;
     g.B = w2;
@@ -183,7 +183,7 @@ moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1
     g.N = p.d;
     g.K = p.h;
     g.relu = false;
-    MOE_TRY(launch_expert_gemm(g, p.bf16, st));
+    MOE_TRY(launch_expert_gemm(g, p.bf16, gemm_block_m(p.bf16, p.S, p.E, p.k), st));
     record(ev, 7, st);
     return MOE_OK;
 }
@@ -277,7 +277,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* 
     if (ws_bytes < cv.ffn_end) return MOE_ERR_WORKSPACE;
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
-    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16), occ, mt, stream));
+    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16, p.S, p.E, p.k), occ, mt, stream));
     return run_ffn(p, xd, w1, b1, w2, b2, out, occ, mt, at<void>(ws, cv.H), nullptr, stream);
 }
 
