@@ -16,7 +16,7 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router logits, fp32 FMA.  Block tile 64 tokens x 64 experts, k-step 32;
+// Router logits, fp32 FMA (fp32 activations).  Block tile 64 tokens x 64 experts, k-step 32;
 // 256 threads, each owns a 4x4 grid of outputs strided by 16 so that LDS
 // reads are conflict-free broadcasts.  Every output accumulates its d
 // products in index order.
@@ -108,13 +108,147 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 }
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Router logits for bf16 activations on the MFMA units.  Each fp32 router
+// weight is split exactly into three bf16 terms, w = hi + lo1 + lo2 (hi is w
+// rounded to bf16, lo1 the rounded remainder, lo2 what is left; 3 x 8
+// significand bits cover fp32's 24).  A bf16 x bf16 product is exact in fp32,
+// so x . w = x . hi + x . (lo1 + lo2) with fp32 accumulation throughout:
+// v_mfma_f32_32x32x16_bf16 accumulates x . hi in one accumulator and the two
+// small terms in another, which are added (with the bias) at the end.
+// Block tile 64 tokens x 64 experts x 64 k, 4 waves of 32 x 32; operands are
+// staged through registers into two LDS buffers (x as is, the weight as three
+// bf16 planes, XOR-swizzled by row like the expert GEMMs).  Rows past S or E
+// load a clamped valid row and are never stored.
+namespace {
+constexpr int GM_BM = 64, GM_BN = 64, GM_BK = 64, GM_CH = GM_BK / 8;
+
+__device__ __forceinline__ int gm_swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
+
+// Exact three-way bf16 split of 8 fp32 values into three 16-byte chunks.
+__device__ __forceinline__ void split3(const f32x4_t& a, const f32x4_t& b, u32x4_t& hi,
+                                       u32x4_t& l1, u32x4_t& l2) {
+    float w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    bf16_t h[8], m[8], t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[i] = f32_to_bf16(w[i]);
+        const float r1 = w[i] - bf16_to_f32(h[i]);
+        m[i] = f32_to_bf16(r1);
+        t[i] = f32_to_bf16(r1 - bf16_to_f32(m[i]));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        hi[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
+        l1[q] = (uint32_t)m[2 * q] | ((uint32_t)m[2 * q + 1] << 16);
+        l2[q] = (uint32_t)t[2 * q] | ((uint32_t)t[2 * q + 1] << 16);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void gate_logits_mfma_kernel(const bf16_t* __restrict__ x,
+                                                                  const float* __restrict__ wg,
+                                                                  const float* __restrict__ bg,
+                                                                  float* __restrict__ logits,
+                                                                  int S, int d, int E) {
+    // stage: A [64][8 chunks], then three weight planes [64][8 chunks]
+    constexpr int A_SZ = GM_BM * GM_CH, B_SZ = GM_BN * GM_CH, STAGE = A_SZ + 3 * B_SZ;
+    __shared__ u32x4_t smem[2 * STAGE];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int s0 = blockIdx.x * GM_BM, j0 = blockIdx.y * GM_BN;
+
+    // loader: x chunks c = tid + 256*i (i < 2): row c/8, chunk c%8;
+    // weight chunk-pairs c = tid + 256*i (i < 2): row c/8, k chunk c%8
+    // (two float4 = 8 consecutive k, split into three bf16 chunks)
+    const bf16_t* xa[2];
+    const float* wb[2];
+    int ald[2], bld[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+        xa[i] = x + (size_t)min(s0 + row, S - 1) * d + ch * 8;
+        wb[i] = wg + (size_t)min(j0 + row, E - 1) * d + ch * 8;
+        ald[i] = row * GM_CH + gm_swz(row, ch);
+        bld[i] = A_SZ + row * GM_CH + gm_swz(row, ch);
+    }
+    u32x4_t rx[2];
+    f32x4_t rw[2][2];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
+            rw[i][0] = *reinterpret_cast<const f32x4_t*>(wb[i] + k0);
+            rw[i][1] = *reinterpret_cast<const f32x4_t*>(wb[i] + k0 + 4);
+        }
+    };
+    auto sstore = [&](int buf) {
+        u32x4_t* st = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            st[ald[i]] = rx[i];
+            u32x4_t h, l1, l2;
+            split3(rw[i][0], rw[i][1], h, l1, l2);
+            st[bld[i]] = h;
+            st[bld[i] + B_SZ] = l1;
+            st[bld[i] + 2 * B_SZ] = l2;
+        }
+    };
+
+    f32x16_t acc_hi, acc_lo;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_hi[r] = 0.f, acc_lo[r] = 0.f;
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const int KT = d / GM_BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) gload((kt + 1) * GM_BK);
+        const u32x4_t* st = smem + buf * STAGE;
+#pragma unroll
+        for (int ks = 0; ks < GM_BK / 16; ++ks) {
+            const int c = 2 * ks + fhalf;
+            const int ra = wm * 32 + frow, rb = wn * 32 + frow;
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, st[ra * GM_CH + gm_swz(ra, c)]);
+            const int bo = A_SZ + rb * GM_CH + gm_swz(rb, c);
+            const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, st[bo]);
+            const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, st[bo + B_SZ]);
+            const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, st[bo + 2 * B_SZ]);
+            acc_hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc_hi, 0, 0, 0);
+            acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc_lo, 0, 0, 0);
+            acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b2, acc_lo, 0, 0, 0);
+        }
+        if (kt + 1 < KT) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    // 32x32 accumulator layout: lane l holds column l%32, register r row
+    // 8*(r/4) + 4*(l/32) + r%4.
+    const int j = j0 + wn * 32 + frow;
+    if (j < E) {
+        const float bj = bg ? bg[j] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int s = s0 + wm * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+            if (s < S) logits[(size_t)s * E + j] = (acc_hi[r] + acc_lo[r]) + bj;
+        }
+    }
+}
+}  // namespace
+
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
                               float* logits, int S, int d, int E, hipStream_t st) {
-    dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
-    if (x_bf16)
-        gate_logits_kernel<true><<<grid, 256, 0, st>>>(x, wg, bg, logits, S, d, E);
-    else
-        gate_logits_kernel<false><<<grid, 256, 0, st>>>(x, wg, bg, logits, S, d, E);
+    if (x_bf16 && d % GM_BK == 0) {
+        dim3 grid((unsigned)ceil_div(S, GM_BM), (unsigned)ceil_div(E, GM_BN));
+        gate_logits_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), wg, bg,
+                                                      logits, S, d, E);
+    } else {
+        dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
+        if (x_bf16)
+            gate_logits_kernel<true><<<grid, 256, 0, st>>>(x, wg, bg, logits, S, d, E);
+        else
+            gate_logits_kernel<false><<<grid, 256, 0, st>>>(x, wg, bg, logits, S, d, E);
+    }
     return hipGetLastError();
 }
 

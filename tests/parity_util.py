@@ -81,6 +81,12 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
     # end to end: the oracle's own logits and routing
     lg_or = oracle.logits(host["x"], host["wg"], host["bg"])
     rep["logit_max_abs_err"] = float(np.abs(lg.astype(np.float64) - lg_or).max())
+    # The router re-evaluates in fp64 every top-k decision closer than
+    # tau = 32 * sqrt(d) * 2^-24; that is exact only while the logit error
+    # stays well below tau / 2.
+    tau = 32.0 * np.sqrt(w.d) * 2.0 ** -24
+    rep["logit_err_over_tau"] = rep["logit_max_abs_err"] / tau
+    assert rep["logit_err_over_tau"] < 0.25, rep
     r_or = oracle.route(lg_or, k, C)
     agree = np.all(idx == r_or["idx"], axis=1)
     rep["topk_agreement"] = float(agree.mean())
