@@ -45,7 +45,35 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(reference kernel for the FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def gemm_source_sha() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "sparse_moe_layer_wg_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None
+    when there is none or the GEMM source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        entries = json.load(open(path))
+    except ValueError:
+        return None
+    for ent in entries:
+        if ent.get("workload") == workload and ent.get("kernel") == kernel:
+            if ent.get("gemm_source_sha256") != gemm_source_sha():
+                return None
+            return float(ent["fetch_bytes"]) + float(ent["write_bytes"])
+    return None
 
 
 def algorithmic_work(w: mw.Workload, occ: np.ndarray, kept: int) -> dict:
@@ -153,7 +181,7 @@ def main():
         roof = {"bound": "mfma", "achieved": fl / t / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name, dom)
     roof["kernel"] = dom
     roof["algorithmic_flops"] = fl
     roof["algorithmic_bytes"] = by
@@ -191,6 +219,15 @@ def main():
                     "aux": aux, "z": z},
         "wall_s": wall,
     }
+    if a.copy_calibration_mb > 0:
+        n = a.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, a.cpu_seconds)
     print(json.dumps(out), flush=True)
