@@ -32,8 +32,9 @@
 //   [mt_start[e], mt_start[e+1]) (built on the device from the occupancies),
 //   ordered (expert, n-tile, m-tile).  The grid is persistent, one block per
 //   CU; block b runs on XCD b % 8, XCD x owns the x-th eighth of the list and
-//   its blocks walk it in rounds, so the blocks of one XCD work on
-//   neighbouring tiles (sharing A and B tiles through L2) at the same time.
+//   its blocks take that chunk's tiles in order from an atomic counter, so
+//   the blocks of one XCD work on neighbouring tiles (sharing A and B tiles
+//   through L2) at the same time and tiles of unequal cost balance out.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,7 +43,6 @@
 namespace moe {
 namespace {
 
-constexpr int BN = 256;
 
 // Physical 16-byte chunk of logical chunk c in a row of CH chunks.  A
 // fragment read has the lanes of a 16-lane group read 16 consecutive rows at
@@ -54,8 +54,8 @@ __device__ __forceinline__ int swz(int row, int c) {
     return CH == 8 ? (c ^ ((row ^ (row >> 3)) & 7)) : (c ^ (((row >> 1) ^ (row >> 3)) & 3));
 }
 
-// WNC waves along N (2 or 4), 2 along M: 4 or 8 waves per block.
-template <int BM, int WNC, bool RELU>
+// Block tile BM x BN; WNC waves along N (2 or 4), 2 along M: 4 or 8 waves.
+template <int BM, int BN, int WNC, bool RELU>
 __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NTH = 128 * WNC;             // threads per block
     constexpr int BK = 64, CH = BK / 8;        // k-tile; 16-byte chunks per row
@@ -71,14 +71,21 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     const int NT = (N + BN - 1) / BN;
     const int T = p.mt_start[p.E] * NT;
     const int per = (T + 7) >> 3;
-    const int xcd = blockIdx.x & 7, nslot = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7;
     const int t_end = min(T, (xcd + 1) * per);
+    __shared__ int s_next;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WNC, wn = wave % WNC;
     const int frow = lane & 31, fhalf = lane >> 5;
     const int KT = K / BK;
 
-    for (int t = xcd * per + (blockIdx.x >> 3); t < t_end; t += nslot) {
+    for (;;) {
+        // next tile of this XCD's chunk: tiles differ in cost (partly filled
+        // m-tiles skip MFMAs), so they are handed out on demand
+        if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
+        __syncthreads();
+        const int t = s_next;
+        if (t >= t_end) break;
         // expert of tile t: the largest e with mt_start[e] <= t / NT
         const int q = t / NT;
         int lo = 0, hi = p.E - 1;
@@ -130,19 +137,23 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
 
         // Fragment (32x32x16): lane l supplies row l%32 and the 8 consecutive
         // k at (l/32)*8 of the 16-wide step, i.e. logical chunk 2*ks + l/32.
+        // Only the first VI of the wave's TM row sub-tiles are read.
         bf16x8_t fa[2][TM], fb[2][TN];
-        auto load_frags = [&](const u32x4_t* st, int ks, int slot) {
+        auto load_frags = [&](auto vi_tag, const u32x4_t* st, int ks, int slot) {
+            constexpr int VI = decltype(vi_tag)::value;
             const u32x4_t* sb = st + BM * CH;
             const int c = 2 * ks + fhalf;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+            for (int i = 0; i < VI; ++i) {
                 const int row = wm * WM + i * 32 + frow;
                 fa[slot][i] = __builtin_bit_cast(bf16x8_t, st[row * CH + swz<CH>(row, c)]);
             }
+            if constexpr (VI > 0) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int row = wn * WNT + j * 32 + frow;
-                fb[slot][j] = __builtin_bit_cast(bf16x8_t, sb[row * CH + swz<CH>(row, c)]);
+                for (int j = 0; j < TN; ++j) {
+                    const int row = wn * WNT + j * 32 + frow;
+                    fb[slot][j] = __builtin_bit_cast(bf16x8_t, sb[row * CH + swz<CH>(row, c)]);
+                }
             }
         };
 
@@ -161,12 +172,16 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         // One k-tile from LDS buffer kt&1.  With REFILL, k-tile kt+1 is loaded
         // into registers during the first step and stored to the other buffer
         // (which every wave finished reading before the previous barrier)
-        // during the last step.
-        auto ktile = [&](auto refill_tag, int kt) {
+        // during the last step.  VI: how many of this wave's TM row sub-tiles
+        // hold filled rows; the MFMAs of the others are skipped (an expert's
+        // last m-tile is usually partly empty).  Every wave still takes part
+        // in the loads, stores and barriers.
+        auto ktile = [&](auto refill_tag, auto vi_tag, int kt) {
             constexpr bool REFILL = decltype(refill_tag)::value;
+            constexpr int VI = decltype(vi_tag)::value;
             constexpr int NL = A_CH + B_CH;   // loads (and stores) per thread
             const u32x4_t* st = smem + (kt & 1) * STAGE;
-            load_frags(st, 0, 0);
+            load_frags(vi_tag, st, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -174,9 +189,9 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
                     if (ks == 0) gload(kt + 1);
                     if (ks == KS - 1) sstore((kt + 1) & 1);
                 }
-                if (ks + 1 < KS) load_frags(st, ks + 1, (ks + 1) & 1);
+                if (ks + 1 < KS) load_frags(vi_tag, st, ks + 1, (ks + 1) & 1);
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < VI; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -206,9 +221,18 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
             }
             __syncthreads();
         };
-        int kt = 0;
-        for (; kt + 1 < KT; ++kt) ktile(std::true_type{}, kt);
-        ktile(std::false_type{}, kt);
+        auto kloop = [&](auto vi_tag) {
+            int kt = 0;
+            for (; kt + 1 < KT; ++kt) ktile(std::true_type{}, vi_tag, kt);
+            ktile(std::false_type{}, vi_tag, kt);
+        };
+        // filled 32-row sub-tiles of this wave (wave-uniform); 3 runs as TM
+        const int rows_left = M - m0 - wm * WM;
+        const int vi = rows_left <= 0 ? 0 : min(TM, (rows_left + 31) / 32);
+        if (vi == 0) kloop(std::integral_constant<int, 0>{});
+        else if (vi == 1) kloop(std::integral_constant<int, 1>{});
+        else if (TM > 2 && vi == 2) kloop(std::integral_constant<int, (TM > 2 ? 2 : TM)>{});
+        else kloop(std::integral_constant<int, TM>{});
 
         // Epilogue.  32x32 accumulator layout: lane l holds column l%32;
         // register r holds row 8*(r/4) + 4*(l/32) + r%4.
@@ -334,16 +358,19 @@ hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, int bm, hipStream_
     if (bf16) {
         // persistent grid: one block per CU (the LDS stages fill a CU), at most
         // one per possible tile, a multiple of the 8 XCDs
-        const long long tiles = (long long)p.E * ceil_div(p.C, bm) * ceil_div(p.N, BN);
+        const int bn = 256;
+        const long long tiles = (long long)p.E * ceil_div(p.C, bm) * ceil_div(p.N, bn);
         const long long slots = (long long)(device_cus() / 8) * 8;
         const unsigned grid = (unsigned)(tiles < slots ? ceil_div(tiles, 8) * 8 : slots);
-        // 8 waves (2 per SIMD): the second wave fills MFMA gaps while one waits
+        // BM 256: 8 waves (2 per SIMD), so each SIMD holds one upper- and one
+        // lower-half wave and a partly filled m-tile sheds MFMA work on every
+        // SIMD; BM 128: 4 waves of 64 x 128
         if (bm == 256) {
-            if (p.relu) gemm_bf16_kernel<256, 4, true><<<grid, 512, 0, st>>>(p);
-            else gemm_bf16_kernel<256, 4, false><<<grid, 512, 0, st>>>(p);
+            if (p.relu) gemm_bf16_kernel<256, 256, 4, true><<<grid, 512, 0, st>>>(p);
+            else gemm_bf16_kernel<256, 256, 4, false><<<grid, 512, 0, st>>>(p);
         } else {
-            if (p.relu) gemm_bf16_kernel<128, 4, true><<<grid, 512, 0, st>>>(p);
-            else gemm_bf16_kernel<128, 4, false><<<grid, 512, 0, st>>>(p);
+            if (p.relu) gemm_bf16_kernel<128, 256, 2, true><<<grid, 256, 0, st>>>(p);
+            else gemm_bf16_kernel<128, 256, 2, false><<<grid, 256, 0, st>>>(p);
         }
     } else {
         dim3 grid((unsigned)ceil_div(p.N, FN), (unsigned)ceil_div(p.C, FM), (unsigned)p.E);

@@ -34,16 +34,18 @@ hipError_t launch_route(const RouteParams& p, hipStream_t st);
 // psum[e] = sum over blocks of ppart[b][e].
 hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t* counts,
                             int32_t* occ, const float* ppart, double* psum, hipStream_t st);
-// losses = {aux, z}; mt_start[e] = sum_{e'<e} ceil(occ[e']/bm) (E+1 entries).
+// losses = {aux, z}; mt_start[e] = sum_{e'<e} ceil(occ[e']/bm) (E+1 entries);
+// zeroes the n_ctr GEMM tile counters.
 hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
                            const int32_t* occ, int S, int E, int nb, int bm, float* losses,
-                           int32_t* mt_start, hipStream_t st);
+                           int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st);
 // slot[s,r] from the scanned tile bases and stable in-tile ranks.
 hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
                                  int E, int k, int nb, int C, int32_t* slot, hipStream_t st);
-// Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN).
+// Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN);
+// zeroes the n_ctr GEMM tile counters.
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
-                            int32_t* mt_start, hipStream_t st);
+                            int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st);
 // Zero losses and counts (empty input).
 hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st);
 
@@ -66,6 +68,7 @@ struct GemmParams {
     void* Cout;
     const int32_t* occ;
     const int32_t* mt_start;
+    int32_t* tile_ctr;      // 8 counters (one per XCD chunk), zero at launch
     int E, C, N, K;
     bool relu;
 };

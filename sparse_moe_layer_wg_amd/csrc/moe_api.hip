@@ -58,13 +58,16 @@ moe_status make_plan(const moe_config* c, Plan* pl) {
     return MOE_OK;
 }
 
+// Two expert GEMMs, 8 tile counters each (one per XCD chunk).
+constexpr int kTileCounters = 16;
+
 // Workspace layout, every region 256-byte aligned:
 //   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
-//            mt_start
+//            mt_start, GEMM tile counters
 //   [ffn]    H [E,C,h]
 //   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
 struct Carve {
-    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start;
+    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, ctr;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -90,6 +93,7 @@ Carve carve(const Plan& p) {
     c.psum = take((size_t)p.E * 8);
     c.occ = take((size_t)p.E * 4);
     c.mt_start = take((size_t)(p.E + 1) * 4);
+    c.ctr = take(kTileCounters * 4);
     c.route_end = o;
     c.H = take((size_t)p.E * p.C * p.h * p.es);
     c.ffn_end = o;
@@ -151,8 +155,9 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     MOE_TRY(launch_route(rp, st));
     record(ev, 2, st);
     MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, ppart, psum, st));
-    MOE_TRY(launch_finalize(psum, zpart, counts, occ, p.S, p.E, p.nb, gemm_block_m(p.bf16, p.S, p.E, p.k),
-                            losses, mt, st));
+    MOE_TRY(launch_finalize(psum, zpart, counts, occ, p.S, p.E, p.nb,
+                            gemm_block_m(p.bf16, p.S, p.E, p.k), losses, mt,
+                            at<int32_t>(ws, cv.ctr), kTileCounters, st));
     record(ev, 3, st);
     MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, st));
     record(ev, 4, st);
@@ -160,11 +165,12 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
 }
 
 moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1, const void* w2,
-                   const void* b2, void* out, const int32_t* occ, const int32_t* mt, void* H,
-                   hipEvent_t* ev, hipStream_t st) {
+                   const void* b2, void* out, const int32_t* occ, const int32_t* mt, int32_t* ctr,
+                   void* H, hipEvent_t* ev, hipStream_t st) {
     GemmParams g{};
     g.occ = occ;
     g.mt_start = mt;
+    g.tile_ctr = ctr;
     g.E = p.E;
     g.C = p.C;
     g.A = xd;
@@ -176,6 +182,7 @@ moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1
     g.relu = true;
     MOE_TRY(launch_expert_gemm(g, p.bf16, gemm_block_m(p.bf16, p.S, p.E, p.k), st));
     record(ev, 6, st);
+    g.tile_ctr = ctr + 8;
     g.A = H;
     g.B = w2;
     g.bias = b2;
@@ -277,8 +284,10 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* 
     if (ws_bytes < cv.ffn_end) return MOE_ERR_WORKSPACE;
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
-    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16, p.S, p.E, p.k), occ, mt, stream));
-    return run_ffn(p, xd, w1, b1, w2, b2, out, occ, mt, at<void>(ws, cv.H), nullptr, stream);
+    int32_t* ctr = at<int32_t>(ws, cv.ctr);
+    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16, p.S, p.E, p.k), occ, mt,
+                             ctr, kTileCounters, stream));
+    return run_ffn(p, xd, w1, b1, w2, b2, out, occ, mt, ctr, at<void>(ws, cv.H), nullptr, stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* out, const int32_t* topk_idx,
@@ -330,7 +339,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     MOE_TRY(launch_dispatch(x, idx, sl, XD, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
     record(ev, 5, stream);
     s = run_ffn(p, XD, w1, b1, w2, b2, OUT, at<int32_t>(ws, cv.occ), at<int32_t>(ws, cv.mt_start),
-                at<void>(ws, cv.H), ev, stream);
+                at<int32_t>(ws, cv.ctr), at<void>(ws, cv.H), ev, stream);
     if (s != MOE_OK) return s;
     MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, p.C, p.bf16, stream));
     record(ev, 8, stream);

@@ -95,10 +95,12 @@ __global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict_
                                                        const int32_t* __restrict__ occ, int S,
                                                        int E, int nb, int bm,
                                                        float* __restrict__ losses,
-                                                       int32_t* __restrict__ mt_start) {
+                                                       int32_t* __restrict__ mt_start,
+                                                       int32_t* __restrict__ ctr, int n_ctr) {
     __shared__ double s_red[256];
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
+    if (tid < n_ctr) ctr[tid] = 0;
     double term = 0.0;
     for (int j = tid; j < E; j += 256) term += (double)counts[j] * psum[j];
     s_red[tid] = term;
@@ -167,9 +169,11 @@ __global__ __launch_bounds__(256) void slot_positions_kernel(const int32_t* __re
 __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restrict__ counts, int E,
                                                         int k, int C, int bm,
                                                         int32_t* __restrict__ occ,
-                                                        int32_t* __restrict__ mt_start) {
+                                                        int32_t* __restrict__ mt_start,
+                                                        int32_t* __restrict__ ctr, int n_ctr) {
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
+    if (tid < n_ctr) ctr[tid] = 0;
     int carry = 0;
     for (int base = 0; base < E; base += 256) {
         const int e = base + tid;
@@ -204,8 +208,9 @@ hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t*
 
 hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
                            const int32_t* occ, int S, int E, int nb, int bm, float* losses,
-                           int32_t* mt_start, hipStream_t st) {
-    finalize_kernel<<<1, 256, 0, st>>>(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start);
+                           int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st) {
+    finalize_kernel<<<1, 256, 0, st>>>(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start,
+                                       ctr, n_ctr);
     return hipGetLastError();
 }
 
@@ -218,8 +223,8 @@ hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_ba
 }
 
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
-                            int32_t* mt_start, hipStream_t st) {
-    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, occ, mt_start);
+                            int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st) {
+    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, occ, mt_start, ctr, n_ctr);
     return hipGetLastError();
 }
 
