@@ -1,8 +1,8 @@
 """Benchmark of the MI355X GShard MoE-layer forward (one GPU).
 
 One step = one moe_layer_forward over one batch of S synthetic tokens: router
-logits, softmax, top-k, capacity slots, dispatch, both expert GEMMs, combine,
-aux loss and z-loss.  Inputs are resident in HBM before timing starts.
+logits, softmax, top-k, capacity slots, dispatch (for bf16, a row gather fused
+into the first expert GEMM), both expert GEMMs, combine, aux loss and z-loss.  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` = tokens per second of the whole layer.
 Per-stage times come from HIP events recorded between the library's kernels
@@ -189,8 +189,14 @@ def main():
 
     ffn_s = (stage_us["expert_gemm1"] + stage_us["expert_gemm2"]) * 1e-6
     ffn_flops = work["expert_gemm1"]["flops"] + work["expert_gemm2"]["flops"]
+    # bf16 layers without a dispatch buffer gather token rows inside the first
+    # expert GEMM (x under 4 GiB): the dispatch stage is then empty.
+    fused = w.dtype == "bf16" and w.S * w.d * 2 < 2 ** 32
     stage_frac = {}
     for n in ("gate_logits", "dispatch", "combine", "expert_gemm1", "expert_gemm2"):
+        if n == "dispatch" and fused:
+            stage_frac[n] = "fused into expert_gemm1"
+            continue
         ts = stage_us[n] * 1e-6
         stage_frac[n] = {"GB_s": work[n]["bytes"] / ts / 1e9,
                          "TFLOP_s": work[n]["flops"] / ts / 1e12}

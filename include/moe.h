@@ -161,8 +161,12 @@ moe_status moe_combine(const moe_config *cfg, const void *out, const int32_t *to
  * Required: x, w_gate, w1, w2, y, ws.  Optional (NULL = not wanted, kept in
  * ws): gate_bias, b1, b2, logits, topk_idx, topk_w, slot, counts, losses,
  * xd, out.  When xd and out are both NULL one workspace buffer serves as
- * both.  stage_events: NULL, or MOE_NUM_STAGE_EVENTS events created by the
- * caller, recorded on `stream` between the steps (for timing). */
+ * both.  With bf16 activations, xd NULL and S*d*2 < 2^32 bytes, no dispatch
+ * buffer is written at all: the first expert GEMM reads each slot's row
+ * straight from x through an inverse slot map (same results bit for bit;
+ * the dispatch stage then takes no time).  stage_events: NULL, or
+ * MOE_NUM_STAGE_EVENTS events created by the caller, recorded on `stream`
+ * between the steps (for timing). */
 moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *w_gate,
                              const float *gate_bias, const void *w1, const void *b1,
                              const void *w2, const void *b2, void *y, float *logits,

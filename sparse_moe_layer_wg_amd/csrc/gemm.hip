@@ -98,8 +98,9 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         const int local = t - p.mt_start[e] * NT;
         const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * BN;
         const int M = p.occ[e];
-        const char* __restrict__ Ab =
-            reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.A) + (size_t)e * p.C * K);
+        const char* __restrict__ Ab = reinterpret_cast<const char*>(
+            static_cast<const bf16_t*>(p.A) + (p.a_rows ? (size_t)0 : (size_t)e * p.C * K));
+        const int32_t* __restrict__ arow = p.a_rows ? p.a_rows + (size_t)e * p.C : nullptr;
         const char* __restrict__ Bb =
             reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.B) + (size_t)e * N * K);
 
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
             const int c = tid + NTH * i, row = c / CH, ch = c % CH;
-            aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)ch * 16u;
+            const int rg = min(m0 + row, M - 1);
+            aoff[i] = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u + (uint32_t)ch * 16u;
             alds[i] = row * CH + swz<CH>(row, ch);
         }
 #pragma unroll

@@ -39,9 +39,11 @@ hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t*
 hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
                            const int32_t* occ, int S, int E, int nb, int bm, float* losses,
                            int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st);
-// slot[s,r] from the scanned tile bases and stable in-tile ranks.
+// slot[s,r] from the scanned tile bases and stable in-tile ranks; with inv
+// non-null also the inverse map inv[e*C + slot] = s of every kept assignment.
 hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
-                                 int E, int k, int nb, int C, int32_t* slot, hipStream_t st);
+                                 int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
+                                 hipStream_t st);
 // Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN);
 // zeroes the n_ctr GEMM tile counters.
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
@@ -61,6 +63,9 @@ hipError_t launch_combine(const void* out, const int32_t* topk_idx, const int32_
 // Per expert e, rows m < occ[e]:
 //   Cout[e,m,n] = act(sum_k A[e,m,k] * B[e,n,k] + bias[e,n]),  act = ReLU or id.
 // A [E,C,K], B [E,N,K], bias [E,N] or NULL, Cout [E,C,N]; all act dtype.
+// With a_rows non-null, row m of expert e is instead row a_rows[e*C + m] of
+// A [*,K] (a gather straight from the token rows: the dispatch permute fused
+// into the loads).
 struct GemmParams {
     const void* A;
     const void* B;
@@ -68,6 +73,7 @@ struct GemmParams {
     void* Cout;
     const int32_t* occ;
     const int32_t* mt_start;
+    const int32_t* a_rows;  // NULL, or [E*C] token row of each filled slot
     int32_t* tile_ctr;      // 8 counters (one per XCD chunk), zero at launch
     int E, C, N, K;
     bool relu;

@@ -63,11 +63,11 @@ constexpr int kTileCounters = 16;
 
 // Workspace layout, every region 256-byte aligned:
 //   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
-//            mt_start, GEMM tile counters
+//            mt_start, GEMM tile counters, inverse slot map [E,C]
 //   [ffn]    H [E,C,h]
 //   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
 struct Carve {
-    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, ctr;
+    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, ctr, inv;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -94,6 +94,7 @@ Carve carve(const Plan& p) {
     c.occ = take((size_t)p.E * 4);
     c.mt_start = take((size_t)(p.E + 1) * 4);
     c.ctr = take(kTileCounters * 4);
+    c.inv = take((size_t)p.E * p.C * 4);
     c.route_end = o;
     c.H = take((size_t)p.E * p.C * p.h * p.es);
     c.ffn_end = o;
@@ -126,7 +127,7 @@ void record(hipEvent_t* ev, int i, hipStream_t st) {
 moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* wg,
                     const float* bg, float* logits, bool logits_in, int32_t* topk_idx,
                     float* topk_w, int32_t* slot, int32_t* counts, float* losses, void* ws,
-                    hipEvent_t* ev, hipStream_t st) {
+                    int32_t* inv, hipEvent_t* ev, hipStream_t st) {
     int32_t* hist = at<int32_t>(ws, cv.hist);
     float* ppart = at<float>(ws, cv.ppart);
     float* zpart = at<float>(ws, cv.zpart);
@@ -159,18 +160,21 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
                             gemm_block_m(p.bf16, p.S, p.E, p.k), losses, mt,
                             at<int32_t>(ws, cv.ctr), kTileCounters, st));
     record(ev, 3, st);
-    MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, st));
+    MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, inv, st));
     record(ev, 4, st);
     return MOE_OK;
 }
 
-moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1, const void* w2,
-                   const void* b2, void* out, const int32_t* occ, const int32_t* mt, int32_t* ctr,
-                   void* H, hipEvent_t* ev, hipStream_t st) {
+// Both expert GEMMs.  a_rows: NULL (GEMM 1 reads the dispatch buffer xd) or
+// the inverse slot map (GEMM 1 gathers its rows from the token rows in xd).
+moe_status run_ffn(const Plan& p, const void* xd, const int32_t* a_rows, const void* w1,
+                   const void* b1, const void* w2, const void* b2, void* out, const int32_t* occ,
+                   const int32_t* mt, int32_t* ctr, void* H, hipEvent_t* ev, hipStream_t st) {
     GemmParams g{};
     g.occ = occ;
     g.mt_start = mt;
     g.tile_ctr = ctr;
+    g.a_rows = a_rows;
     g.E = p.E;
     g.C = p.C;
     g.A = xd;
@@ -183,6 +187,7 @@ moe_status run_ffn(const Plan& p, const void* xd, const void* w1, const void* b1
     MOE_TRY(launch_expert_gemm(g, p.bf16, gemm_block_m(p.bf16, p.S, p.E, p.k), st));
     record(ev, 6, st);
     g.tile_ctr = ctr + 8;
+    g.a_rows = nullptr;
     g.A = H;
     g.B = w2;
     g.bias = b2;
@@ -254,7 +259,7 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const float* w_gate,
     if (ws_bytes < cv.route_end) return MOE_ERR_WORKSPACE;
     float* L = logits ? logits : at<float>(ws, cv.logits);
     return run_gate(p, cv, x, w_gate, gate_bias, L, logits_in, topk_idx, topk_w, slot, counts,
-                    losses, ws, nullptr, stream);
+                    losses, ws, nullptr, nullptr, stream);
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
@@ -287,7 +292,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* 
     int32_t* ctr = at<int32_t>(ws, cv.ctr);
     MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16, p.S, p.E, p.k), occ, mt,
                              ctr, kTileCounters, stream));
-    return run_ffn(p, xd, w1, b1, w2, b2, out, occ, mt, ctr, at<void>(ws, cv.H), nullptr, stream);
+    return run_ffn(p, xd, nullptr, w1, b1, w2, b2, out, occ, mt, ctr, at<void>(ws, cv.H), nullptr,
+                   stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* out, const int32_t* topk_idx,
@@ -334,12 +340,19 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     void* XD = xd ? xd : at<void>(ws, cv.xo);
     void* OUT = out ? out : (xd ? at<void>(ws, cv.xo) : XD);
 
-    s = run_gate(p, cv, x, w_gate, gate_bias, L, false, idx, w, sl, cnt, los, ws, ev, stream);
+    // Without a requested dispatch buffer (and for bf16 activations), GEMM 1
+    // gathers its rows straight from x through the inverse slot map, so the
+    // permute costs no separate pass over HBM.
+    // (The gather offsets are 32-bit: x must stay below 4 GiB.)
+    const bool fuse = xd == nullptr && p.bf16 && (size_t)p.S * p.d * p.es < ((size_t)1 << 32);
+    int32_t* inv = fuse ? at<int32_t>(ws, cv.inv) : nullptr;
+    s = run_gate(p, cv, x, w_gate, gate_bias, L, false, idx, w, sl, cnt, los, ws, inv, ev, stream);
     if (s != MOE_OK) return s;
-    MOE_TRY(launch_dispatch(x, idx, sl, XD, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
+    if (!fuse) MOE_TRY(launch_dispatch(x, idx, sl, XD, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
     record(ev, 5, stream);
-    s = run_ffn(p, XD, w1, b1, w2, b2, OUT, at<int32_t>(ws, cv.occ), at<int32_t>(ws, cv.mt_start),
-                at<int32_t>(ws, cv.ctr), at<void>(ws, cv.H), ev, stream);
+    s = run_ffn(p, fuse ? x : XD, inv, w1, b1, w2, b2, OUT, at<int32_t>(ws, cv.occ),
+                at<int32_t>(ws, cv.mt_start), at<int32_t>(ws, cv.ctr), at<void>(ws, cv.H), ev,
+                stream);
     if (s != MOE_OK) return s;
     MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, p.C, p.bf16, stream));
     record(ev, 8, stream);

@@ -142,7 +142,8 @@ __global__ __launch_bounds__(256) void slot_positions_kernel(const int32_t* __re
                                                              const int32_t* __restrict__ hist_base,
                                                              int S, int E, int k, int nb, int C,
                                                              int nbits,
-                                                             int32_t* __restrict__ slot) {
+                                                             int32_t* __restrict__ slot,
+                                                             int32_t* __restrict__ inv) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int b = blockIdx.x;
     const int s = b * kTokBlock + lane;
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(256) void slot_positions_kernel(const int32_t* __re
         if (valid) {
             const int pos = hist_base[(size_t)e * T + (size_t)r * nb + b] + before;
             slot[(size_t)s * k + r] = pos < C ? pos : -1;
+            if (inv && pos < C) inv[(size_t)e * C + pos] = s;
         }
     }
 }
@@ -215,10 +217,12 @@ hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t
 }
 
 hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
-                                 int E, int k, int nb, int C, int32_t* slot, hipStream_t st) {
+                                 int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
+                                 hipStream_t st) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    slot_positions_kernel<<<nb, 256, 0, st>>>(topk_idx, hist_base, S, E, k, nb, C, nbits, slot);
+    slot_positions_kernel<<<nb, 256, 0, st>>>(topk_idx, hist_base, S, E, k, nb, C, nbits, slot,
+                                              inv);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ from . import _lib
 
 class MoELayer:
     def __init__(self, cfg: _lib.MoeConfig, w_gate, gate_bias, w1, b1, w2, b2,
-                 keep: bool = True, device="cuda"):
+                 keep: bool = True, device="cuda", dispatch_buffer: bool = True):
         self.cfg = cfg
         self.C = _lib.capacity(cfg)
         self.w_gate, self.gate_bias = w_gate, gate_bias
@@ -31,7 +31,10 @@ class MoELayer:
             self.slot = torch.empty((S, k), dtype=torch.int32, device=dev)
             self.counts = torch.empty((k, E), dtype=torch.int32, device=dev)
             self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
-            self.xd = torch.empty((E, self.C, d), dtype=at, device=dev)
+            # Without a dispatch buffer the first expert GEMM gathers token
+            # rows straight from x (bf16); with one, x is first permuted into it.
+            self.xd = torch.empty((E, self.C, d), dtype=at, device=dev) if dispatch_buffer \
+                else None
             self.out = torch.empty((E, self.C, d), dtype=at, device=dev)
         else:
             self.logits = self.topk_idx = self.topk_w = self.slot = None
@@ -39,9 +42,10 @@ class MoELayer:
             self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
 
     @classmethod
-    def from_inputs(cls, cfg, inputs: dict, keep=True):
+    def from_inputs(cls, cfg, inputs: dict, keep=True, dispatch_buffer=True):
         return cls(cfg, inputs["wg"], inputs["bg"], inputs["w1"], inputs["b1"], inputs["w2"],
-                   inputs["b2"], keep=keep, device=inputs["x"].device)
+                   inputs["b2"], keep=keep, device=inputs["x"].device,
+                   dispatch_buffer=dispatch_buffer)
 
     def forward(self, x, y=None, events=None, stream=None):
         y = self.y if y is None else y

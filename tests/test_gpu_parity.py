@@ -184,14 +184,33 @@ def test_deterministic_repeat():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("w", [w for w in MID if w.dtype == "bf16"], ids=lambda w: w.name)
+def test_fused_gather_matches_dispatch_buffer(w):
+    """Without a dispatch buffer the first expert GEMM gathers rows from x:
+    y, out and every routing output equal the unfused run bit for bit, and
+    the fused run passes the full oracle check."""
+    print(f"\n[fused] {w}", flush=True)
+    inputs, ref = run_layer(w)
+    _, fused = run_layer(w, inputs, dispatch_buffer=False)
+    assert fused.xd is None
+    occ = np.minimum(ref.counts.cpu().numpy().sum(0), ref.C)
+    filled = torch.from_numpy(np.arange(ref.C)[None, :] < occ[:, None]).cuda()
+    assert torch.equal(ref.out[filled], fused.out[filled])
+    for a, b in ((ref.y, fused.y), (ref.slot, fused.slot), (ref.topk_idx, fused.topk_idx),
+                 (ref.losses, fused.losses)):
+        assert torch.equal(a, b)
+    _print(w.name + "_fused", check_layer(w, inputs, fused, full=True))
+
+
 # --------------------------------------------------------------------- full sizes
 @pytest.mark.parametrize("name", ["balanced_bf16", "skewed_bf16", "large_bf16", "deepseek_bf16"])
 def test_full_size_sampled(name):
-    """Full-size workloads in the benchmark's launch configuration: all routing
+    """Full-size workloads in the benchmark's launch configuration (no dispatch
+    buffer: the gather is fused into the first expert GEMM): all routing
     checked exactly, y checked on sampled tokens (including dropped ones)."""
     w = mw.get(name)
     print(f"\n[full] {w}", flush=True)
-    inputs, layer = run_layer(w)
+    inputs, layer = run_layer(w, dispatch_buffer=False)
     rep = check_layer(w, inputs, layer, full=False)
     _print(name, rep)
     del layer, inputs
