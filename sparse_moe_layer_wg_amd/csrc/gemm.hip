@@ -59,13 +59,21 @@ template <int BM, int BN, int WNC, bool RELU>
 __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NTH = 128 * WNC;             // threads per block
     constexpr int BK = 64, CH = BK / 8;        // k-tile; 16-byte chunks per row
+    constexpr int RS = BK * 2 + 16;            // LDS row stride in bytes (padded)
     constexpr int WM = BM / 2, WNT = BN / WNC; // wave tile
     constexpr int TM = WM / 32, TN = WNT / 32; // 32x32 MFMA tiles per wave
     constexpr int KS = BK / 16;                // MFMA k steps per k-tile
     constexpr int A_CH = BM * CH / NTH;        // A chunks per thread per k-tile
     constexpr int B_CH = BN * CH / NTH;        // B chunks per thread per k-tile
-    constexpr int STAGE = (BM + BN) * CH;      // chunks per LDS buffer
-    __shared__ u32x4_t smem[2 * STAGE];
+    constexpr int RPI = NTH / CH;              // rows per loader pass
+    // An expert's last m-tile may carry SR more rows (the strip): each wave
+    // multiplies them into one extra 32x32 block with a B fragment it holds.
+    constexpr int SR = BM == 256 ? kStripRows : 0;
+    constexpr int BOFF = (BM + SR) * RS;       // byte offset of B in a stage
+    constexpr int STAGE = BOFF + BN * RS;      // bytes per LDS buffer
+    static_assert(SR == 0 || (NTH * 8 == SR * BK * 2 && TN >= 2),
+                  "strip: one 8-byte piece per thread, B fragment per wave row");
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
     const int N = p.N, K = p.K;
     const int NT = (N + BN - 1) / BN;
@@ -78,6 +86,13 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     const int wm = wave / WNC, wn = wave % WNC;
     const int frow = lane & 31, fhalf = lane >> 5;
     const int KT = K / BK;
+    // LDS byte offsets: loader chunk (row tid/CH + RPI*i, chunk tid%CH);
+    // fragment rows of this lane (row + 32*i, chunk 2*ks + fhalf)
+    const int ld_off = (tid / CH) * RS + (tid % CH) * 16;
+    const int fa_off = (wm * WM + frow) * RS + fhalf * 16;
+    const int fb_off = BOFF + (wn * WNT + frow) * RS + fhalf * 16;
+    const int fs_off = (BM + frow) * RS + fhalf * 16;
+    const int ls_off = (BM + tid / 16) * RS + (tid & 15) * 8;
 
     for (;;) {
         // next tile of this XCD's chunk: tiles differ in cost (partly filled
@@ -96,66 +111,73 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         const int e = lo;
         const int mtiles = p.mt_start[e + 1] - p.mt_start[e];
         const int local = t - p.mt_start[e] * NT;
-        const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * BN;
+        const int mi = local % mtiles;
+        const int m0 = mi * BM, n0 = (local / mtiles) * BN;
         const int M = p.occ[e];
+        const bool strip = SR > 0 && mi == mtiles - 1 && M - m0 > BM;
         const char* __restrict__ Ab = reinterpret_cast<const char*>(
             static_cast<const bf16_t*>(p.A) + (p.a_rows ? (size_t)0 : (size_t)e * p.C * K));
         const int32_t* __restrict__ arow = p.a_rows ? p.a_rows + (size_t)e * p.C : nullptr;
         const char* __restrict__ Bb =
             reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.B) + (size_t)e * N * K);
 
-        // Loader: chunk c = tid + NTH*i covers row c/CH, columns (c%CH)*8..+8
-        // of the k-tile; it is stored at its swizzled LDS position.
+        // Global byte offsets of this thread's chunks (rows past the
+        // occupancy or past N load a clamped valid row).
         uint32_t aoff[A_CH], boff[B_CH];
-        int alds[A_CH], blds[B_CH];
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
-            const int c = tid + NTH * i, row = c / CH, ch = c % CH;
-            const int rg = min(m0 + row, M - 1);
-            aoff[i] = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u + (uint32_t)ch * 16u;
-            alds[i] = row * CH + swz<CH>(row, ch);
+            const int rg = min(m0 + tid / CH + RPI * i, M - 1);
+            aoff[i] = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u + (uint32_t)(tid % CH) * 16u;
         }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int c = tid + NTH * i, row = c / CH, ch = c % CH;
-            boff[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K * 2u + (uint32_t)ch * 16u;
-            blds[i] = BM * CH + row * CH + swz<CH>(row, ch);
+        for (int i = 0; i < B_CH; ++i)
+            boff[i] = (uint32_t)min(n0 + tid / CH + RPI * i, N - 1) * (uint32_t)K * 2u +
+                      (uint32_t)(tid % CH) * 16u;
+        // strip rows: one 8-byte piece per thread
+        uint32_t soff = 0;
+        if constexpr (SR > 0) {
+            const int rg = min(m0 + BM + tid / 16, M - 1);
+            soff = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u + (uint32_t)(tid & 15) * 8u;
         }
         u32x4_t ra[A_CH], rb[B_CH];
-        auto gload = [&](int kt) {
+        uint2 rs;
+        auto gload = [&](auto strip_tag, int kt) {
             const uint32_t kb = (uint32_t)kt * BK * 2u;
+            if constexpr (decltype(strip_tag)::value)
+                rs = *reinterpret_cast<const uint2*>(Ab + soff + kb);
 #pragma unroll
             for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(Ab + aoff[i] + kb);
 #pragma unroll
             for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(Bb + boff[i] + kb);
         };
-        auto sstore = [&](int buf) {
-            u32x4_t* st = smem + buf * STAGE;
+        auto sstore = [&](auto strip_tag, int buf) {
+            char* st = smem + buf * STAGE;
+            if constexpr (decltype(strip_tag)::value)
+                *reinterpret_cast<uint2*>(st + ls_off) = rs;
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i) st[alds[i]] = ra[i];
+            for (int i = 0; i < A_CH; ++i)
+                *reinterpret_cast<u32x4_t*>(st + ld_off + i * RPI * RS) = ra[i];
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i) st[blds[i]] = rb[i];
+            for (int i = 0; i < B_CH; ++i)
+                *reinterpret_cast<u32x4_t*>(st + BOFF + ld_off + i * RPI * RS) = rb[i];
         };
 
         // Fragment (32x32x16): lane l supplies row l%32 and the 8 consecutive
-        // k at (l/32)*8 of the 16-wide step, i.e. logical chunk 2*ks + l/32.
-        // Only the first VI of the wave's TM row sub-tiles are read.
-        bf16x8_t fa[2][TM], fb[2][TN];
-        auto load_frags = [&](auto vi_tag, const u32x4_t* st, int ks, int slot) {
+        // k at (l/32)*8 of the 16-wide step, i.e. chunk 2*ks + l/32 of the
+        // row.  Only the first VI of the wave's TM row sub-tiles are read.
+        bf16x8_t fa[2][TM], fb[2][TN], fs[2];
+        auto load_frags = [&](auto vi_tag, auto strip_tag, const char* st, int ks, int slot) {
             constexpr int VI = decltype(vi_tag)::value;
-            const u32x4_t* sb = st + BM * CH;
-            const int c = 2 * ks + fhalf;
+            if constexpr (decltype(strip_tag)::value)
+                fs[slot] = *reinterpret_cast<const bf16x8_t*>(st + fs_off + ks * 32);
 #pragma unroll
-            for (int i = 0; i < VI; ++i) {
-                const int row = wm * WM + i * 32 + frow;
-                fa[slot][i] = __builtin_bit_cast(bf16x8_t, st[row * CH + swz<CH>(row, c)]);
-            }
+            for (int i = 0; i < VI; ++i)
+                fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(st + fa_off + i * 32 * RS + ks * 32);
             if constexpr (VI > 0) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int row = wn * WNT + j * 32 + frow;
-                    fb[slot][j] = __builtin_bit_cast(bf16x8_t, sb[row * CH + swz<CH>(row, c)]);
-                }
+                for (int j = 0; j < TN; ++j)
+                    fb[slot][j] =
+                        *reinterpret_cast<const bf16x8_t*>(st + fb_off + j * 32 * RS + ks * 32);
             }
         };
 
@@ -166,10 +188,9 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-        gload(0);
-        sstore(0);
-        __syncthreads();
+        f32x16_t acc_s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
 
         // One k-tile from LDS buffer kt&1.  With REFILL, k-tile kt+1 is loaded
         // into registers during the first step and stored to the other buffer
@@ -178,63 +199,76 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         // hold filled rows; the MFMAs of the others are skipped (an expert's
         // last m-tile is usually partly empty).  Every wave still takes part
         // in the loads, stores and barriers.
-        auto ktile = [&](auto refill_tag, auto vi_tag, int kt) {
+        auto ktile = [&](auto refill_tag, auto vi_tag, auto strip_tag, int kt) {
             constexpr bool REFILL = decltype(refill_tag)::value;
             constexpr int VI = decltype(vi_tag)::value;
-            constexpr int NL = A_CH + B_CH;   // loads (and stores) per thread
-            const u32x4_t* st = smem + (kt & 1) * STAGE;
-            load_frags(vi_tag, st, 0, 0);
+            constexpr int SI = decltype(strip_tag)::value ? 1 : 0;
+            constexpr int NL = A_CH + B_CH + SI;   // loads (and stores) per thread
+            constexpr int NF = TM + TN + SI;       // fragment reads per step
+            constexpr int NM = TM * TN + SI;       // MFMAs per step (full tile)
+            const char* st = smem + (kt & 1) * STAGE;
+            load_frags(vi_tag, strip_tag, st, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if constexpr (REFILL) {
-                    if (ks == 0) gload(kt + 1);
-                    if (ks == KS - 1) sstore((kt + 1) & 1);
+                    if (ks == 0) gload(strip_tag, kt + 1);
+                    if (ks == KS - 1) sstore(strip_tag, (kt + 1) & 1);
                 }
-                if (ks + 1 < KS) load_frags(vi_tag, st, ks + 1, (ks + 1) & 1);
+                if (ks + 1 < KS) load_frags(vi_tag, strip_tag, st, ks + 1, (ks + 1) & 1);
 #pragma unroll
                 for (int i = 0; i < VI; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+                if constexpr (SI) {
+                    // strip columns of this wave: its B fragment wm
+                    const bf16x8_t bs = wm ? fb[ks & 1][1] : fb[ks & 1][0];
+                    acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[ks & 1], bs, acc_s, 0, 0, 0);
+                }
                 // instruction groups: spread memory instructions over the MFMAs
                 if (REFILL && ks == 0) {
 #pragma unroll
                     for (int g = 0; g < NL; ++g) {
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
-                        if (g < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN + NL - 1) / NL, 0);
+                        if (g < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, (NM + NL - 1) / NL, 0);
                     }
                 } else if (REFILL && ks == KS - 1) {
 #pragma unroll
                     for (int g = 0; g < NL; ++g) {
                         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // LDS write
-                        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN + NL - 1) / NL, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, (NM + NL - 1) / NL, 0);
                     }
                 } else if (ks + 1 < KS) {
 #pragma unroll
-                    for (int g = 0; g < TM + TN; ++g) {
+                    for (int g = 0; g < NF; ++g) {
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, NM / NF, 0);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
         };
-        auto kloop = [&](auto vi_tag) {
+        auto kloop = [&](auto vi_tag, auto strip_tag) {
+            gload(strip_tag, 0);
+            sstore(strip_tag, 0);
+            __syncthreads();
             int kt = 0;
-            for (; kt + 1 < KT; ++kt) ktile(std::true_type{}, vi_tag, kt);
-            ktile(std::false_type{}, vi_tag, kt);
+            for (; kt + 1 < KT; ++kt) ktile(std::true_type{}, vi_tag, strip_tag, kt);
+            ktile(std::false_type{}, vi_tag, strip_tag, kt);
         };
         // filled 32-row sub-tiles of this wave (wave-uniform); 3 runs as TM
         const int rows_left = M - m0 - wm * WM;
         const int vi = rows_left <= 0 ? 0 : min(TM, (rows_left + 31) / 32);
-        if (vi == 0) kloop(std::integral_constant<int, 0>{});
-        else if (vi == 1) kloop(std::integral_constant<int, 1>{});
-        else if (TM > 2 && vi == 2) kloop(std::integral_constant<int, (TM > 2 ? 2 : TM)>{});
-        else kloop(std::integral_constant<int, TM>{});
+        constexpr std::false_type no_strip{};
+        if (strip) kloop(std::integral_constant<int, TM>{}, std::bool_constant<(SR > 0)>{});
+        else if (vi == 0) kloop(std::integral_constant<int, 0>{}, no_strip);
+        else if (vi == 1) kloop(std::integral_constant<int, 1>{}, no_strip);
+        else if (TM > 2 && vi == 2) kloop(std::integral_constant<int, (TM > 2 ? 2 : TM)>{}, no_strip);
+        else kloop(std::integral_constant<int, TM>{}, no_strip);
 
         // Epilogue.  32x32 accumulator layout: lane l holds column l%32;
         // register r holds row 8*(r/4) + 4*(l/32) + r%4.
@@ -252,6 +286,21 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
                     const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
                     if (m < M) {
                         float v = acc[i][j][r] + bv;
+                        if (RELU) v = v > 0.f ? v : 0.f;
+                        Cout[(size_t)m * N + n] = f32_to_bf16(v);
+                    }
+                }
+            }
+        }
+        if (strip) {
+            const int n = n0 + wn * WNT + wm * 32 + frow;
+            if (n < N) {
+                const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + BM + 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                    if (m < M) {
+                        float v = acc_s[r] + bv;
                         if (RELU) v = v > 0.f ? v : 0.f;
                         Cout[(size_t)m * N + n] = f32_to_bf16(v);
                     }

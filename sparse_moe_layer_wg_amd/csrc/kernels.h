@@ -78,6 +78,16 @@ struct GemmParams {
     int E, C, N, K;
     bool relu;
 };
+// m-tiles of an expert with occ filled rows.  Tiles are bm rows high, but
+// with bm = 256 an expert's last m-tile may reach kStripRows further: the
+// GEMM then runs those rows as an extra strip against the weight fragments
+// it already holds instead of as a nearly empty m-tile of their own.
+constexpr int kStripRows = 32;
+__host__ __device__ inline int expert_mtiles(int occ, int bm) {
+    if (occ <= 0) return 0;
+    const int extra = bm == 256 ? kStripRows : 0;
+    return occ <= bm + extra ? 1 : (occ - extra + bm - 1) / bm;
+}
 // m-tile height the expert GEMMs use for a layer shape (the m-tile prefix
 // mt_start must be built with the same value).
 int gemm_block_m(bool bf16, int S, int E, int k);

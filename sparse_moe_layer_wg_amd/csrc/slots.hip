@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict_
     int carry = 0;
     for (int base = 0; base < E; base += 256) {
         const int e = base + tid;
-        const int v = e < E ? (int)ceil_div(occ[e], bm) : 0;
+        const int v = e < E ? expert_mtiles(occ[e], bm) : 0;
         int total;
         const int ex = block_exclusive_scan(v, s_wave, &total);
         if (e < E) mt_start[e] = carry + ex;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
             occ[e] = o;
         }
         int total;
-        const int ex = block_exclusive_scan(e < E ? (int)ceil_div(o, bm) : 0, s_wave, &total);
+        const int ex = block_exclusive_scan(e < E ? expert_mtiles(o, bm) : 0, s_wave, &total);
         if (e < E) mt_start[e] = carry + ex;
         carry += total;
     }
