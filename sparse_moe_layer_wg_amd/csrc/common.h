@@ -24,17 +24,15 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (IEEE-754 rounding of the low
-// 16 bits).  Inputs here are finite.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    uint32_t lsb = (u >> 16) & 1u;
-    u += 0x7fffu + lsb;
-    return static_cast<bf16_t>(u >> 16);
-}
-
+// fp32 -> bf16, round to nearest even, by gfx950's packed conversion
+// (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_native_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_native_t));
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    return static_cast<bf16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key); -0 is

@@ -11,11 +11,9 @@
 // both operands, which is the operand order the MFMA fragments want.
 //
 // bf16 path: gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulation.
-//   Block tile BM x 256 x 64 (BM = 128 or 256), 256 threads = 4 waves in a
-//   2x2 grid; each wave owns a (BM/2) x 128 block of accumulators, i.e.
-//   (BM/64) x 4 MFMA tiles of 32x32 (up to 256 fp32 per lane, held in AGPRs).
-//   A wave tile this large keeps LDS traffic per MFMA low and halves the L2
-//   traffic of a 128x128 tile.
+//   Block tile BM x 256 x 64.  BM = 256: 512 threads = 8 waves in a 2 x 4
+//   grid, 128 x 64 per wave (two waves per SIMD, 128 fp32 accumulators per
+//   lane); BM = 128 (experts with few rows): 4 waves of 64 x 128.
 //   Operands are staged through registers into two LDS buffers: the global
 //   loads of k-tile t+1 are spread over the MFMAs of the first 16-wide step
 //   of tile t and their LDS stores over the MFMAs of the last step, and the
@@ -24,10 +22,21 @@
 //   order, so bursts of memory instructions would stall its MFMAs).  Plain
 //   vector loads are used rather than global->LDS copies: on gfx950 the copy
 //   path moves about 16 bytes per clock per CU, a quarter of the load path.
-//   LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so that the
-//   fragment reads of 16 consecutive rows hit distinct bank groups.  Rows
-//   past an expert's occupancy (and columns past N) load a clamped valid row;
-//   their results are never stored.
+//   LDS rows are padded to 144 bytes: the 16 rows a fragment read touches at
+//   one 16-byte column fall on distinct bank groups, and every fragment
+//   read or store is one base register plus an immediate offset.
+//   Rows past an expert's occupancy (and columns past N) load a clamped
+//   valid row; their results are never stored.
+//   An expert's last 256-row m-tile may hold up to 32 more rows (a strip):
+//   each wave multiplies them against B fragments it already holds, so an
+//   expert with 257..288 rows costs one m-tile, not a second, nearly empty
+//   one that reloads all of W.
+//   The MFMAs take the weight fragment as their first operand, so each lane
+//   ends with four consecutive output columns per register quad; bias, ReLU
+//   and bf16 rounding are applied there and the tile leaves through LDS as
+//   16-byte row-contiguous stores.
+//   With a_rows set, A rows are gathered from the token rows through the
+//   inverse slot map (the dispatch permute fused into the loads).
 //   Tiles come from a compact list: expert e owns m-tiles
 //   [mt_start[e], mt_start[e+1]) (built on the device from the occupancies),
 //   ordered (expert, n-tile, m-tile).  The grid is persistent, one block per
@@ -35,6 +44,9 @@
 //   its blocks take that chunk's tiles in order from an atomic counter, so
 //   the blocks of one XCD work on neighbouring tiles (sharing A and B tiles
 //   through L2) at the same time and tiles of unequal cost balance out.
+//   On random bf16 data this kernel is power-bound: the shader clock settles
+//   near 1.4 GHz (2.2 GHz on constant data), so data moved per MFMA, not
+//   issue slots, sets the rate.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,17 +54,6 @@
 
 namespace moe {
 namespace {
-
-
-// Physical 16-byte chunk of logical chunk c in a row of CH chunks.  A
-// fragment read has the lanes of a 16-lane group read 16 consecutive rows at
-// one logical chunk; the XOR pattern spreads those 16 reads over distinct
-// 16-byte bank groups of a 256-byte LDS line (and any aligned 8 of them over
-// a 128-byte line), so 128-bit reads are conflict-free.
-template <int CH>
-__device__ __forceinline__ int swz(int row, int c) {
-    return CH == 8 ? (c ^ ((row ^ (row >> 3)) & 7)) : (c ^ (((row >> 1) ^ (row >> 3)) & 3));
-}
 
 // Block tile BM x BN; WNC waves along N (2 or 4), 2 along M: 4 or 8 waves.
 template <int BM, int BN, int WNC, bool RELU>
@@ -67,12 +68,15 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     constexpr int B_CH = BN * CH / NTH;        // B chunks per thread per k-tile
     constexpr int RPI = NTH / CH;              // rows per loader pass
     // An expert's last m-tile may carry SR more rows (the strip): each wave
-    // multiplies them into one extra 32x32 block with a B fragment it holds.
+    // multiplies them into SB extra 32x32 blocks, with B fragments it holds.
     constexpr int SR = BM == 256 ? kStripRows : 0;
+    constexpr int SB = BN / 32 / (NTH / 64);   // strip blocks per wave
+    constexpr int SP = SR * BK * 2 / NTH;      // strip bytes per thread (8 or 16)
     constexpr int BOFF = (BM + SR) * RS;       // byte offset of B in a stage
     constexpr int STAGE = BOFF + BN * RS;      // bytes per LDS buffer
-    static_assert(SR == 0 || (NTH * 8 == SR * BK * 2 && TN >= 2),
-                  "strip: one 8-byte piece per thread, B fragment per wave row");
+    static_assert(SR == 0 || ((SP == 8 || SP == 16) && SB * 2 == TN),
+                  "strip: 8 or 16 bytes per thread; a wave row's share of the B fragments");
+    using strip_t = std::conditional_t<SP == 16, u32x4_t, uint2>;
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
     const int N = p.N, K = p.K;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     const int fa_off = (wm * WM + frow) * RS + fhalf * 16;
     const int fb_off = BOFF + (wn * WNT + frow) * RS + fhalf * 16;
     const int fs_off = (BM + frow) * RS + fhalf * 16;
-    const int ls_off = (BM + tid / 16) * RS + (tid & 15) * 8;
+    const int ls_off = (BM + tid * SP / (BK * 2)) * RS + (tid * SP) % (BK * 2);
 
     for (;;) {
         // next tile of this XCD's chunk: tiles differ in cost (partly filled
@@ -136,15 +140,16 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         // strip rows: one 8-byte piece per thread
         uint32_t soff = 0;
         if constexpr (SR > 0) {
-            const int rg = min(m0 + BM + tid / 16, M - 1);
-            soff = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u + (uint32_t)(tid & 15) * 8u;
+            const int rg = min(m0 + BM + tid * SP / (BK * 2), M - 1);
+            soff = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u +
+                   (uint32_t)((tid * SP) % (BK * 2));
         }
         u32x4_t ra[A_CH], rb[B_CH];
-        uint2 rs;
+        strip_t rs;
         auto gload = [&](auto strip_tag, int kt) {
             const uint32_t kb = (uint32_t)kt * BK * 2u;
             if constexpr (decltype(strip_tag)::value)
-                rs = *reinterpret_cast<const uint2*>(Ab + soff + kb);
+                rs = *reinterpret_cast<const strip_t*>(Ab + soff + kb);
 #pragma unroll
             for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(Ab + aoff[i] + kb);
 #pragma unroll
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         auto sstore = [&](auto strip_tag, int buf) {
             char* st = smem + buf * STAGE;
             if constexpr (decltype(strip_tag)::value)
-                *reinterpret_cast<uint2*>(st + ls_off) = rs;
+                *reinterpret_cast<strip_t*>(st + ls_off) = rs;
 #pragma unroll
             for (int i = 0; i < A_CH; ++i)
                 *reinterpret_cast<u32x4_t*>(st + ld_off + i * RPI * RS) = ra[i];
@@ -188,9 +193,11 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-        f32x16_t acc_s;
+        f32x16_t acc_s[SB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_s[b][r] = 0.f;
 
         // One k-tile from LDS buffer kt&1.  With REFILL, k-tile kt+1 is loaded
         // into registers during the first step and stored to the other buffer
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
             constexpr int SI = decltype(strip_tag)::value ? 1 : 0;
             constexpr int NL = A_CH + B_CH + SI;   // loads (and stores) per thread
             constexpr int NF = TM + TN + SI;       // fragment reads per step
-            constexpr int NM = TM * TN + SI;       // MFMAs per step (full tile)
+            constexpr int NM = TM * TN + SI * SB;  // MFMAs per step (full tile)
             const char* st = smem + (kt & 1) * STAGE;
             load_frags(vi_tag, strip_tag, st, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -221,11 +228,15 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+                            fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
                 if constexpr (SI) {
-                    // strip columns of this wave: its B fragment wm
-                    const bf16x8_t bs = wm ? fb[ks & 1][1] : fb[ks & 1][0];
-                    acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[ks & 1], bs, acc_s, 0, 0, 0);
+                    // strip columns of this wave: its B fragments wm*SB + b
+#pragma unroll
+                    for (int b = 0; b < SB; ++b) {
+                        const bf16x8_t bs = wm ? fb[ks & 1][SB + b] : fb[ks & 1][b];
+                        acc_s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bs, fs[ks & 1], acc_s[b],
+                                                                           0, 0, 0);
+                    }
                 }
                 // instruction groups: spread memory instructions over the MFMAs
                 if (REFILL && ks == 0) {
@@ -270,41 +281,73 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         else if (TM > 2 && vi == 2) kloop(std::integral_constant<int, (TM > 2 ? 2 : TM)>{}, no_strip);
         else kloop(std::integral_constant<int, TM>{}, no_strip);
 
-        // Epilogue.  32x32 accumulator layout: lane l holds column l%32;
-        // register r holds row 8*(r/4) + 4*(l/32) + r%4.
+        // Epilogue.  The MFMAs take the weight fragment as their first
+        // operand, so a 32x32 accumulator block is (n x m): lane l holds row
+        // m = l%32 and register r column n = 8*(r/4) + 4*(l/32) + r%4, i.e.
+        // four consecutive columns per register quad.  Bias and ReLU are
+        // applied there; the bf16 results pass through LDS (the stage
+        // buffers are free after the k-loop's last barrier; each wave uses
+        // its own region) and leave as 16-byte row-contiguous stores.
         bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) + (size_t)e * p.C * N;
         const bf16_t* bias = p.bias ? static_cast<const bf16_t*>(p.bias) + (size_t)e * N : nullptr;
+        auto finish4 = [&](const f32x16_t& a, int q, int n) {
+            float v[4];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * WNT + j * 32 + frow;
-            if (n >= N) continue;
-            const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                    if (m < M) {
-                        float v = acc[i][j][r] + bv;
-                        if (RELU) v = v > 0.f ? v : 0.f;
-                        Cout[(size_t)m * N + n] = f32_to_bf16(v);
-                    }
-                }
+            for (int r = 0; r < 4; ++r) v[r] = a[4 * q + r];
+            if (bias && n < N) {
+                const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+                v[0] += __uint_as_float(bb.x << 16);
+                v[1] += __uint_as_float(bb.x & 0xffff0000u);
+                v[2] += __uint_as_float(bb.y << 16);
+                v[3] += __uint_as_float(bb.y & 0xffff0000u);
             }
+            if (RELU) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = v[r] > 0.f ? v[r] : 0.f;
+            }
+            return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        };
+        constexpr int EPS = WNT * 2 + 8;            // LDS bytes per staged row
+        static_assert(NTH / 64 * WM * EPS <= 2 * STAGE, "epilogue staging fits LDS");
+        char* ep = smem + wave * (WM * EPS);
+        const int nw = n0 + wn * WNT;               // first column of this wave
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = j * 32 + 8 * q + 4 * fhalf;
+                    *reinterpret_cast<uint2*>(ep + (i * 32 + frow) * EPS + nl * 2) =
+                        finish4(acc[i][j], q, nw + nl);
+                }
+        __builtin_amdgcn_wave_barrier();
+        constexpr int CPR = WNT * 2 / 16;           // 16-byte chunks per row
+        constexpr int NIT = WM * CPR / 64;          // chunks per lane
+        u32x4_t ov[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+            ov[it] = *reinterpret_cast<const u32x4_t*>(ep + row * EPS + ch * 16);
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+            const int m = m0 + wm * WM + row, n = nw + ch * 8;
+            if (m < M && n < N) *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = ov[it];
         }
         if (strip) {
-            const int n = n0 + wn * WNT + wm * 32 + frow;
-            if (n < N) {
-                const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+            const int m = m0 + BM + frow;
+            if (m < M) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + BM + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                    if (m < M) {
-                        float v = acc_s[r] + bv;
-                        if (RELU) v = v > 0.f ? v : 0.f;
-                        Cout[(size_t)m * N + n] = f32_to_bf16(v);
+                for (int b = 0; b < SB; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = nw + (wm * SB + b) * 32 + 8 * q + 4 * fhalf;
+                        if (n < N)
+                            *reinterpret_cast<uint2*>(Cout + (size_t)m * N + n) =
+                                finish4(acc_s[b], q, n);
                     }
-                }
             }
         }
     }  // tile loop
