@@ -98,26 +98,25 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     const int fs_off = (BM + frow) * RS + fhalf * 16;
     const int ls_off = (BM + tid * SP / (BK * 2)) * RS + (tid * SP) % (BK * 2);
 
+    // Tiles of this XCD's chunk are handed out on demand (tiles differ in
+    // cost: partly filled m-tiles skip MFMAs).  The next tile is claimed at
+    // the start of each epilogue and published at its end, so the atomic's
+    // latency overlaps the epilogue and does not wait for its stores.
+    if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
     for (;;) {
-        // next tile of this XCD's chunk: tiles differ in cost (partly filled
-        // m-tiles skip MFMAs), so they are handed out on demand
-        if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
         __syncthreads();
-        const int t = s_next;
+        const int t = __builtin_amdgcn_readfirstlane(s_next);
         if (t >= t_end) break;
-        // expert of tile t: the largest e with mt_start[e] <= t / NT
+        // expert and m-/n-tile of tile t (uniform values, kept in scalar
+        // registers; the loads themselves go through the vector path)
         const int q = t / NT;
-        int lo = 0, hi = p.E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.mt_start[mid] <= q) lo = mid; else hi = mid - 1;
-        }
-        const int e = lo;
-        const int mtiles = p.mt_start[e + 1] - p.mt_start[e];
-        const int local = t - p.mt_start[e] * NT;
+        const int e = __builtin_amdgcn_readfirstlane(p.mt_expert[q]);
+        const int mt0 = __builtin_amdgcn_readfirstlane(p.mt_start[e]);
+        const int mtiles = __builtin_amdgcn_readfirstlane(p.mt_start[e + 1]) - mt0;
+        const int local = t - mt0 * NT;
         const int mi = local % mtiles;
         const int m0 = mi * BM, n0 = (local / mtiles) * BN;
-        const int M = p.occ[e];
+        const int M = __builtin_amdgcn_readfirstlane(p.occ[e]);
         const bool strip = SR > 0 && mi == mtiles - 1 && M - m0 > BM;
         const char* __restrict__ Ab = reinterpret_cast<const char*>(
             static_cast<const bf16_t*>(p.A) + (p.a_rows ? (size_t)0 : (size_t)e * p.C * K));
@@ -281,6 +280,8 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         else if (TM > 2 && vi == 2) kloop(std::integral_constant<int, (TM > 2 ? 2 : TM)>{}, no_strip);
         else kloop(std::integral_constant<int, TM>{}, no_strip);
 
+        int nx = 0;
+        if (tid == 0) nx = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
         // Epilogue.  The MFMAs take the weight fragment as their first
         // operand, so a 32x32 accumulator block is (n x m): lane l holds row
         // m = l%32 and register r column n = 8*(r/4) + 4*(l/32) + r%4, i.e.
@@ -321,6 +322,9 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
                     *reinterpret_cast<uint2*>(ep + (i * 32 + frow) * EPS + nl * 2) =
                         finish4(acc[i][j], q, nw + nl);
                 }
+        // publish the next tile (every wave read s_next before the k-loop's
+        // first barrier; the atomic has long returned)
+        if (tid == 0) s_next = nx;
         __builtin_amdgcn_wave_barrier();
         constexpr int CPR = WNT * 2 / 16;           // 16-byte chunks per row
         constexpr int NIT = WM * CPR / 64;          // chunks per lane

@@ -73,6 +73,7 @@ struct GemmParams {
     void* Cout;
     const int32_t* occ;
     const int32_t* mt_start;
+    const int32_t* mt_expert;  // expert of each m-tile (mt_start[E] entries)
     const int32_t* a_rows;  // NULL, or [E*C] token row of each filled slot
     int32_t* tile_ctr;      // 8 counters (one per XCD chunk), zero at launch
     int E, C, N, K;
@@ -88,6 +89,9 @@ __host__ __device__ inline int expert_mtiles(int occ, int bm) {
     const int extra = bm == 256 ? kStripRows : 0;
     return occ <= bm + extra ? 1 : (occ - extra + bm - 1) / bm;
 }
+// The m-tile prefix mt_start [E+1] is followed in memory by the expert of
+// every m-tile; room for both: (E + 1) + mtile_table_len(E, C) int32.
+inline size_t mtile_table_len(int E, int C) { return (size_t)E * ((C + 63) / 64); }
 // m-tile height the expert GEMMs use for a layer shape (the m-tile prefix
 // mt_start must be built with the same value).
 int gemm_block_m(bool bf16, int S, int E, int k);

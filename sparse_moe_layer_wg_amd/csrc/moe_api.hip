@@ -63,7 +63,7 @@ constexpr int kTileCounters = 16;
 
 // Workspace layout, every region 256-byte aligned:
 //   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
-//            mt_start, GEMM tile counters, inverse slot map [E,C]
+//            mt_start + m-tile experts, GEMM tile counters, inverse slot map [E,C]
 //   [ffn]    H [E,C,h]
 //   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
 struct Carve {
@@ -92,7 +92,7 @@ Carve carve(const Plan& p) {
     c.zpart = take((size_t)p.nb * 4);
     c.psum = take((size_t)p.E * 8);
     c.occ = take((size_t)p.E * 4);
-    c.mt_start = take((size_t)(p.E + 1) * 4);
+    c.mt_start = take(((size_t)p.E + 1 + mtile_table_len(p.E, p.C)) * 4);
     c.ctr = take(kTileCounters * 4);
     c.inv = take((size_t)p.E * p.C * 4);
     c.route_end = o;
@@ -173,6 +173,7 @@ moe_status run_ffn(const Plan& p, const void* xd, const int32_t* a_rows, const v
     GemmParams g{};
     g.occ = occ;
     g.mt_start = mt;
+    g.mt_expert = mt + p.E + 1;
     g.tile_ctr = ctr;
     g.a_rows = a_rows;
     g.E = p.E;

@@ -124,14 +124,17 @@ __global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict_
         losses[0] = (float)((double)E * aux_sum / (Sd * Sd));
         losses[1] = (float)(s_red[0] / Sd);
     }
-    // m-tile prefix
+    // m-tile prefix, then the expert of every m-tile
     int carry = 0;
     for (int base = 0; base < E; base += 256) {
         const int e = base + tid;
         const int v = e < E ? expert_mtiles(occ[e], bm) : 0;
         int total;
         const int ex = block_exclusive_scan(v, s_wave, &total);
-        if (e < E) mt_start[e] = carry + ex;
+        if (e < E) {
+            mt_start[e] = carry + ex;
+            for (int i = 0; i < v; ++i) mt_start[E + 1 + carry + ex + i] = e;
+        }
         carry += total;
     }
     if (tid == 0) mt_start[E] = carry;
@@ -167,7 +170,8 @@ __global__ __launch_bounds__(256) void slot_positions_kernel(const int32_t* __re
     }
 }
 
-// occ[e] = min(sum_r counts[r,e], C) and the m-tile prefix (one block).
+// occ[e] = min(sum_r counts[r,e], C), the m-tile prefix and the expert of
+// every m-tile (one block).
 __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restrict__ counts, int E,
                                                         int k, int C, int bm,
                                                         int32_t* __restrict__ occ,
@@ -187,8 +191,12 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
             occ[e] = o;
         }
         int total;
-        const int ex = block_exclusive_scan(e < E ? expert_mtiles(o, bm) : 0, s_wave, &total);
-        if (e < E) mt_start[e] = carry + ex;
+        const int v = e < E ? expert_mtiles(o, bm) : 0;
+        const int ex = block_exclusive_scan(v, s_wave, &total);
+        if (e < E) {
+            mt_start[e] = carry + ex;
+            for (int i = 0; i < v; ++i) mt_start[E + 1 + carry + ex + i] = e;
+        }
         carry += total;
     }
     if (tid == 0) mt_start[E] = carry;
