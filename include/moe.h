@@ -164,9 +164,10 @@ moe_status moe_combine(const moe_config *cfg, const void *out, const int32_t *to
  * both.  With bf16 activations, xd NULL and S*d*2 < 2^32 bytes, no dispatch
  * buffer is written at all: the first expert GEMM reads each slot's row
  * straight from x through an inverse slot map (same results bit for bit;
- * the dispatch stage then takes no time).  stage_events: NULL, or
- * MOE_NUM_STAGE_EVENTS events created by the caller, recorded on `stream`
- * between the steps (for timing). */
+ * the dispatch stage then takes no time).  stage_events: NULL, or an array
+ * of MOE_NUM_STAGE_EVENTS events created by the caller, recorded on `stream`
+ * between the steps (for timing); NULL entries are skipped (each recorded
+ * event costs a few microseconds of queue time between two kernels). */
 moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *w_gate,
                              const float *gate_bias, const void *w1, const void *b1,
                              const void *w2, const void *b2, void *y, float *logits,

@@ -200,7 +200,8 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
                   topk_idx=None, topk_w=None, slot=None, counts=None, losses=None, xd=None,
                   out=None, events=None, stream=None):
     """Whole forward pass (``moe_layer_forward``).  ``events``: None or a list
-    of MOE_NUM_STAGE_EVENTS torch.cuda.Event objects already created."""
+    of MOE_NUM_STAGE_EVENTS entries, each None (boundary not recorded) or a
+    torch.cuda.Event already created."""
     C = capacity(cfg)
     S, d, h, E, k = cfg.S, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     at = cfg.torch_dtype
@@ -209,8 +210,8 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
     if events is not None:
         if len(events) != MOE_NUM_STAGE_EVENTS:
             raise ValueError(f"events must hold {MOE_NUM_STAGE_EVENTS} events")
-        handles = [e.cuda_event for e in events]
-        if not all(handles):
+        handles = [None if e is None else e.cuda_event for e in events]
+        if not all(h for e, h in zip(events, handles) if e is not None):
             raise ValueError("events must be created (recorded once) before use")
         ev = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
     st = library().moe_layer_forward(

@@ -118,7 +118,7 @@ float refine_tau(int d) { return (float)(ldexp(32.0, -24) * sqrt((double)d)); }
     } while (0)
 
 void record(hipEvent_t* ev, int i, hipStream_t st) {
-    if (ev) (void)hipEventRecord(ev[i], st);
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], st);
 }
 
 // Router + slots for a planned layer.  logits: device array (input when

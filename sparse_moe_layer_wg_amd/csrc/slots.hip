@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict_
     __shared__ double s_red[256];
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
-    if (tid < n_ctr) ctr[tid] = 0;
+    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
     double term = 0.0;
     for (int j = tid; j < E; j += 256) term += (double)counts[j] * psum[j];
     s_red[tid] = term;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ ctr, int n_ctr) {
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
-    if (tid < n_ctr) ctr[tid] = 0;
+    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
     int carry = 0;
     for (int base = 0; base < E; base += 256) {
         const int e = base + tid;
