@@ -101,22 +101,28 @@ def test_dispatch_and_combine(dtype, S, d, E, k, cf):
 # 256-row m-tiles take up to 32 more rows in an expert's last tile: 256..288
 # rows run as one tile, 289 as 256 + 33, 544 as 256 + 288, 545 as three.
 STRIP_OCC = [256, 257, 270, 288, 289, 300, 544, 545, 600, 0]
+# Small and nearly empty last m-tiles around the 32-row sub-tile and strip
+# boundaries, with K and N (320) not multiples of the 256-wide tiles.
+SMALL_OCC = [1, 31, 33, 63, 64, 65, 289, 320, 321, 352, 0]
 
 
 @pytest.mark.parametrize("dtype,E,C,d,h,bias", [("bf16", 5, 300, 256, 384, True),
                                                 ("bf16", 3, 130, 128, 64, False),
                                                 ("bf16", 10, 600, 128, 192, True),
+                                                ("bf16", 11, 400, 320, 320, True),
                                                 ("f32", 4, 70, 68, 132, True)])
 def test_expert_ffn_ragged_occupancy(dtype, E, C, d, h, bias):
     """moe_expert_ffn over ragged occupancies (empty, partial tile, full C,
-    and every boundary of the extra rows an expert's last m-tile may take);
-    every filled row is also checked on its own."""
+    every boundary of the extra rows an expert's last m-tile may take, small
+    last tiles with K and N not multiples of 256); every filled row is also
+    checked on its own."""
     print(f"\n[ffn] {dtype} E={E} C={C} d={d} h={h} bias={bias}", flush=True)
     torch.manual_seed(2)
     at = torch.bfloat16 if dtype == "bf16" else torch.float32
     k = 1
     cfg = moe.config(E * C, d, h, E, k, capacity=C, dtype=dtype)
-    occ = np.array(STRIP_OCC if E == len(STRIP_OCC) else [C, 0, 1, C - 1, 129][:E], np.int32)
+    occ = np.array(STRIP_OCC if E == len(STRIP_OCC) else
+                   SMALL_OCC if E == len(SMALL_OCC) else [C, 0, 1, C - 1, 129][:E], np.int32)
     counts = torch.from_numpy(occ[None, :].copy()).cuda()
     xd = torch.randn((E, C, d), device="cuda").to(at)
     w1 = (torch.randn((E, h, d), device="cuda") / d ** 0.5).to(at)
