@@ -39,7 +39,8 @@
 //   inverse slot map (the dispatch permute fused into the loads).
 //   Tiles come from a compact list: expert e owns m-tiles
 //   [mt_start[e], mt_start[e+1]) (built on the device from the occupancies),
-//   ordered (expert, n-tile, m-tile).  The grid is persistent, one block per
+//   ordered by expert, then in groups of 4 n-tiles (m-tile-major inside a
+//   group, n-tile fastest).  The grid is persistent, one block per
 //   CU; block b runs on XCD b % 8, XCD x owns the x-th eighth of the list and
 //   its blocks take that chunk's tiles in order from an atomic counter, so
 //   the blocks of one XCD work on neighbouring tiles (sharing A and B tiles
@@ -113,9 +114,17 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         const int e = __builtin_amdgcn_readfirstlane(p.mt_expert[q]);
         const int mt0 = __builtin_amdgcn_readfirstlane(p.mt_start[e]);
         const int mtiles = __builtin_amdgcn_readfirstlane(p.mt_start[e + 1]) - mt0;
+        // Within an expert, tiles run in groups of GN n-tiles: n-tile fastest
+        // inside a group, then m-tile, then the next group, so each A panel
+        // serves GN neighbouring tiles and each B panel all m-tiles of a group
+        // while they are in L2.
+        constexpr int GN = 4;
         const int local = t - mt0 * NT;
-        const int mi = local % mtiles;
-        const int m0 = mi * BM, n0 = (local / mtiles) * BN;
+        const int ng = local / (mtiles * GN);
+        const int gsize = min(GN, NT - ng * GN);
+        const int r = local - ng * mtiles * GN;
+        const int mi = r / gsize;
+        const int m0 = mi * BM, n0 = (ng * GN + r % gsize) * BN;
         const int M = __builtin_amdgcn_readfirstlane(p.occ[e]);
         const bool strip = SR > 0 && mi == mtiles - 1 && M - m0 > BM;
         const char* __restrict__ Ab = reinterpret_cast<const char*>(
