@@ -112,41 +112,39 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 // Router logits for bf16 activations on the MFMA units.  Each fp32 router
 // weight is split exactly into three bf16 terms, w = hi + lo1 + lo2 (hi is w
 // rounded to bf16, lo1 the rounded remainder, lo2 what is left; 3 x 8
-// significand bits cover fp32's 24).  A bf16 x bf16 product is exact in fp32,
+// significand bits cover fp32's 24), once per call into three planes.  A bf16 x bf16 product is exact in fp32,
 // so x . w = x . hi + x . (lo1 + lo2) with fp32 accumulation throughout:
 // v_mfma_f32_32x32x16_bf16 accumulates x . hi in one accumulator and the two
 // small terms in another, which are added (with the bias) at the end.
 // Block tile 64 tokens x 64 experts x 64 k, 4 waves of 32 x 32; operands are
-// staged through registers into two LDS buffers (x as is, the weight as three
-// bf16 planes, XOR-swizzled by row like the expert GEMMs).  Rows past S or E
+// staged through registers into two LDS buffers (x and the three weight
+// planes, XOR-swizzled by row).  Rows past S or E
 // load a clamped valid row and are never stored.
 namespace {
 constexpr int GM_BM = 64, GM_BN = 64, GM_BK = 64, GM_CH = GM_BK / 8;
 
 __device__ __forceinline__ int gm_swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
 
-// Exact three-way bf16 split of 8 fp32 values into three 16-byte chunks.
-__device__ __forceinline__ void split3(const f32x4_t& a, const f32x4_t& b, u32x4_t& hi,
-                                       u32x4_t& l1, u32x4_t& l2) {
-    float w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    bf16_t h[8], m[8], t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h[i] = f32_to_bf16(w[i]);
-        const float r1 = w[i] - bf16_to_f32(h[i]);
-        m[i] = f32_to_bf16(r1);
-        t[i] = f32_to_bf16(r1 - bf16_to_f32(m[i]));
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        hi[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
-        l1[q] = (uint32_t)m[2 * q] | ((uint32_t)m[2 * q + 1] << 16);
-        l2[q] = (uint32_t)t[2 * q] | ((uint32_t)t[2 * q + 1] << 16);
+// Exact three-way bf16 split of the router weight, once per call: plane 0
+// holds hi = bf16(w), plane 1 lo1 = bf16(w - hi), plane 2 lo2 = w - hi - lo1
+// (exact in bf16), each [E,d].
+__global__ __launch_bounds__(256) void split_router_weight_kernel(const float* __restrict__ wg,
+                                                                  size_t n,
+                                                                  bf16_t* __restrict__ planes) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const float w = wg[i];
+        const bf16_t h = f32_to_bf16(w);
+        const float r1 = w - bf16_to_f32(h);
+        const bf16_t m = f32_to_bf16(r1);
+        planes[i] = h;
+        planes[n + i] = m;
+        planes[2 * n + i] = f32_to_bf16(r1 - bf16_to_f32(m));
     }
 }
 
 __global__ __launch_bounds__(256, 2) void gate_logits_mfma_kernel(const bf16_t* __restrict__ x,
-                                                                  const float* __restrict__ wg,
+                                                                  const bf16_t* __restrict__ wp,
                                                                   const float* __restrict__ bg,
                                                                   float* __restrict__ logits,
                                                                   int S, int d, int E) {
@@ -157,28 +155,28 @@ __global__ __launch_bounds__(256, 2) void gate_logits_mfma_kernel(const bf16_t* 
     const int wm = wave >> 1, wn = wave & 1;
     const int s0 = blockIdx.x * GM_BM, j0 = blockIdx.y * GM_BN;
 
-    // loader: x chunks c = tid + 256*i (i < 2): row c/8, chunk c%8;
-    // weight chunk-pairs c = tid + 256*i (i < 2): row c/8, k chunk c%8
-    // (two float4 = 8 consecutive k, split into three bf16 chunks)
+    // loader: x and weight-plane chunks c = tid + 256*i (i < 2): row c/8,
+    // chunk c%8 (8 consecutive k)
+    const size_t plane = (size_t)E * d;
     const bf16_t* xa[2];
-    const float* wb[2];
+    const bf16_t* wb[2];
     int ald[2], bld[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
         xa[i] = x + (size_t)min(s0 + row, S - 1) * d + ch * 8;
-        wb[i] = wg + (size_t)min(j0 + row, E - 1) * d + ch * 8;
+        wb[i] = wp + (size_t)min(j0 + row, E - 1) * d + ch * 8;
         ald[i] = row * GM_CH + gm_swz(row, ch);
         bld[i] = A_SZ + row * GM_CH + gm_swz(row, ch);
     }
-    u32x4_t rx[2];
-    f32x4_t rw[2][2];
+    u32x4_t rx[2], rw[2][3];
     auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
-            rw[i][0] = *reinterpret_cast<const f32x4_t*>(wb[i] + k0);
-            rw[i][1] = *reinterpret_cast<const f32x4_t*>(wb[i] + k0 + 4);
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                rw[i][q] = *reinterpret_cast<const u32x4_t*>(wb[i] + q * plane + k0);
         }
     };
     auto sstore = [&](int buf) {
@@ -186,11 +184,8 @@ __global__ __launch_bounds__(256, 2) void gate_logits_mfma_kernel(const bf16_t* 
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             st[ald[i]] = rx[i];
-            u32x4_t h, l1, l2;
-            split3(rw[i][0], rw[i][1], h, l1, l2);
-            st[bld[i]] = h;
-            st[bld[i] + B_SZ] = l1;
-            st[bld[i] + 2 * B_SZ] = l2;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) st[bld[i] + q * B_SZ] = rw[i][q];
         }
     };
 
@@ -236,11 +231,19 @@ __global__ __launch_bounds__(256, 2) void gate_logits_mfma_kernel(const bf16_t* 
 }
 }  // namespace
 
+bool gate_uses_split(bool x_bf16, int d) { return x_bf16 && d % GM_BK == 0; }
+
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
-                              float* logits, int S, int d, int E, hipStream_t st) {
-    if (x_bf16 && d % GM_BK == 0) {
+                              float* logits, int S, int d, int E, void* split,
+                              hipStream_t st) {
+    if (gate_uses_split(x_bf16, d)) {
+        bf16_t* planes = static_cast<bf16_t*>(split);
+        const size_t n = (size_t)E * d;
+        const int64_t nblk = ceil_div((int64_t)n, 256);
+        split_router_weight_kernel<<<(unsigned)(nblk < 2048 ? nblk : 2048), 256, 0, st>>>(wg, n,
+                                                                                          planes);
         dim3 grid((unsigned)ceil_div(S, GM_BM), (unsigned)ceil_div(E, GM_BN));
-        gate_logits_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), wg, bg,
+        gate_logits_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), planes, bg,
                                                       logits, S, d, E);
     } else {
         dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
@@ -253,9 +256,11 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const
 }
 
 // ---------------------------------------------------------------------------
-// Route: one wavefront per token at a time; a block of 16 waves (4 when
-// E > 512) owns one 64-token routing tile.  Lane l holds the logits of
-// experts l, l+64, ...
+// Route.  For E <= 256, route_fast_kernel gives each token 1 to 8 lanes and
+// hands only near-tie tokens to the wave router below.  Otherwise (and
+// for those tokens) one wavefront routes one token at a time; a block of 16
+// waves (4 when E > 512) owns one 64-token routing tile.  Lane l holds the
+// logits of experts l, l+64, ...
 //
 // Top-k uses a 64-bit key per logit: the order-preserving uint32 image of
 // the fp32 value (with -0 folded onto +0) above the bitwise complement of
@@ -376,6 +381,128 @@ __device__ __forceinline__ void apply_refined(float (&v)[EQ], float* lrow, const
     }
 }
 
+// Routes token s with the whole wave (lane l holds experts l, l+64, ...):
+// top-k with near-tie refinement, softmax, renormalised weights, outputs and
+// the histogram; adds the token's probabilities to pacc and lse^2 to zacc.
+// s_cand: kMaxSel ints of LDS private to this wave.
+template <int EQ>
+__device__ void route_token_wave(const RouteParams& p, int s, int lane, int* s_hist, int* s_cand,
+                                 float (&pacc)[EQ], float& zacc) {
+    const int E = p.E, k = p.k;
+    const int nsel = k + 1 <= E ? k + 1 : E;
+    float* lrow = p.logits + (size_t)s * E;
+    float v[EQ];
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+        const int j = lane + kWave * q;
+        v[q] = j < E ? lrow[j] : 0.f;
+    }
+    // top[r]: key of the r-th largest logit (wave-uniform)
+    uint64_t top[kMaxSel];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxK + 1; ++r)
+        if (r < nsel) top[r] = select_next<EQ>(v, E, lane, taken);
+
+    if (p.tau > 0.f && nsel > 1) {
+        // Pair r joins sorted positions r and r+1 and is "close" when their
+        // difference is below tau.  Pairs r < k decide the ordered top-k.
+        bool need = false;
+#pragma unroll
+        for (int r = 0; r < kMaxK; ++r)
+            if (r < k && r + 1 < nsel)
+                need |= key_value(top[r]) - key_value(top[r + 1]) < p.tau;
+        if (need) {
+            // follow a chain of close pairs past position k
+            int n = nsel;
+#pragma unroll
+            for (int r = 2; r < kMaxSel; ++r) {
+                if (r == n && n < E && key_value(top[r - 2]) - key_value(top[r - 1]) < p.tau) {
+                    top[r] = select_next<EQ>(v, E, lane, taken);
+                    ++n;
+                }
+            }
+            const bool overflow =
+                n == kMaxSel && n < E &&
+                key_value(top[kMaxSel - 2]) - key_value(top[kMaxSel - 1]) < p.tau;
+            int ncand = 0;
+            if (!overflow) {
+                // members of the close chains that contain a pair r < k
+                uint32_t closebits = 0;
+#pragma unroll
+                for (int r = 0; r + 1 < kMaxSel; ++r)
+                    if (r + 1 < n && key_value(top[r]) - key_value(top[r + 1]) < p.tau)
+                        closebits |= 1u << r;
+                uint32_t members = 0;
+                int r = 0;
+                while (r + 1 < n) {
+                    if (!((closebits >> r) & 1u)) {
+                        ++r;
+                        continue;
+                    }
+                    const int a = r;
+                    while (r + 1 < n && ((closebits >> r) & 1u)) ++r;
+                    if (a < k) members |= ((2u << r) - 1u) & ~((1u << a) - 1u);
+                }
+#pragma unroll
+                for (int q = 0; q < kMaxSel; ++q) {
+                    if ((members >> q) & 1u) {
+                        s_cand[ncand] = key_index(top[q]);
+                        ++ncand;
+                    }
+                }
+            }
+            // a chain longer than kMaxSel: refine every logit of the token
+            const int total = overflow ? E : ncand;
+            for (int g = 0; g < total; g += 4) {
+                int js[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    js[u] = g + u < total ? (overflow ? g + u : s_cand[g + u]) : -1;
+                float nv[4];
+                refine_group(p, s, js, nv);
+                apply_refined<EQ>(v, lrow, js, nv, lane);
+            }
+            taken = 0;
+#pragma unroll
+            for (int r = 0; r < kMaxK; ++r)
+                if (r < k) top[r] = select_next<EQ>(v, E, lane, taken);
+        }
+    }
+
+    // softmax over all E logits, stabilised by the largest
+    const float m = key_value(top[0]);
+    float ev[EQ], part = 0.f;
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+        const int j = lane + kWave * q;
+        ev[q] = j < E ? expf(v[q] - m) : 0.f;
+        part += ev[q];
+    }
+    const float sum = wave_sum_f32(part);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) pacc[q] += ev[q] * inv;
+    const float lse = m + logf(sum);
+    zacc += lse * lse;
+
+    // renormalised top-k weights: p_r / sum_r' p_r' = e_r / sum_r' e_r'
+    float den = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r)
+        if (r < k) den += expf(key_value(top[r]) - m);
+    if (lane < k) {
+        uint64_t mine = top[0];
+#pragma unroll
+        for (int r = 1; r < kMaxK; ++r)
+            if (r == lane) mine = top[r];
+        const int j = key_index(mine);
+        p.topk_idx[(size_t)s * k + lane] = j;
+        p.topk_w[(size_t)s * k + lane] = expf(key_value(mine) - m) / den;
+        atomicAdd(&s_hist[lane * E + j], 1);
+    }
+}
+
 // NW waves per block share one 64-token routing tile, 64/NW tokens each.
 template <int EQ, int NW>
 __global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
@@ -395,122 +522,11 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
 #pragma unroll
     for (int q = 0; q < EQ; ++q) pacc[q] = 0.f;
     float zacc = 0.f;
-    const int nsel = k + 1 <= E ? k + 1 : E;
 
     for (int t = 0; t < kTokBlock / NW; ++t) {
         const int s = b * kTokBlock + wave * (kTokBlock / NW) + t;
         if (s >= p.S) break;
-        float* lrow = p.logits + (size_t)s * E;
-        float v[EQ];
-#pragma unroll
-        for (int q = 0; q < EQ; ++q) {
-            const int j = lane + kWave * q;
-            v[q] = j < E ? lrow[j] : 0.f;
-        }
-        // top[r]: key of the r-th largest logit (wave-uniform)
-        uint64_t top[kMaxSel];
-        uint32_t taken = 0;
-#pragma unroll
-        for (int r = 0; r < kMaxK + 1; ++r)
-            if (r < nsel) top[r] = select_next<EQ>(v, E, lane, taken);
-
-        if (p.tau > 0.f && nsel > 1) {
-            // Pair r joins sorted positions r and r+1 and is "close" when their
-            // difference is below tau.  Pairs r < k decide the ordered top-k.
-            bool need = false;
-#pragma unroll
-            for (int r = 0; r < kMaxK; ++r)
-                if (r < k && r + 1 < nsel)
-                    need |= key_value(top[r]) - key_value(top[r + 1]) < p.tau;
-            if (need) {
-                // follow a chain of close pairs past position k
-                int n = nsel;
-#pragma unroll
-                for (int r = 2; r < kMaxSel; ++r) {
-                    if (r == n && n < E && key_value(top[r - 2]) - key_value(top[r - 1]) < p.tau) {
-                        top[r] = select_next<EQ>(v, E, lane, taken);
-                        ++n;
-                    }
-                }
-                const bool overflow =
-                    n == kMaxSel && n < E &&
-                    key_value(top[kMaxSel - 2]) - key_value(top[kMaxSel - 1]) < p.tau;
-                int ncand = 0;
-                if (!overflow) {
-                    // members of the close chains that contain a pair r < k
-                    uint32_t closebits = 0;
-#pragma unroll
-                    for (int r = 0; r + 1 < kMaxSel; ++r)
-                        if (r + 1 < n && key_value(top[r]) - key_value(top[r + 1]) < p.tau)
-                            closebits |= 1u << r;
-                    uint32_t members = 0;
-                    int r = 0;
-                    while (r + 1 < n) {
-                        if (!((closebits >> r) & 1u)) {
-                            ++r;
-                            continue;
-                        }
-                        const int a = r;
-                        while (r + 1 < n && ((closebits >> r) & 1u)) ++r;
-                        if (a < k) members |= ((2u << r) - 1u) & ~((1u << a) - 1u);
-                    }
-#pragma unroll
-                    for (int q = 0; q < kMaxSel; ++q) {
-                        if ((members >> q) & 1u) {
-                            s_cand[wave][ncand] = key_index(top[q]);
-                            ++ncand;
-                        }
-                    }
-                }
-                // a chain longer than kMaxSel: refine every logit of the token
-                const int total = overflow ? E : ncand;
-                for (int g = 0; g < total; g += 4) {
-                    int js[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        js[u] = g + u < total ? (overflow ? g + u : s_cand[wave][g + u]) : -1;
-                    float nv[4];
-                    refine_group(p, s, js, nv);
-                    apply_refined<EQ>(v, lrow, js, nv, lane);
-                }
-                taken = 0;
-#pragma unroll
-                for (int r = 0; r < kMaxK; ++r)
-                    if (r < k) top[r] = select_next<EQ>(v, E, lane, taken);
-            }
-        }
-
-        // softmax over all E logits, stabilised by the largest
-        const float m = key_value(top[0]);
-        float ev[EQ], part = 0.f;
-#pragma unroll
-        for (int q = 0; q < EQ; ++q) {
-            const int j = lane + kWave * q;
-            ev[q] = j < E ? expf(v[q] - m) : 0.f;
-            part += ev[q];
-        }
-        const float sum = wave_sum_f32(part);
-        const float inv = 1.0f / sum;
-#pragma unroll
-        for (int q = 0; q < EQ; ++q) pacc[q] += ev[q] * inv;
-        const float lse = m + logf(sum);
-        zacc += lse * lse;
-
-        // renormalised top-k weights: p_r / sum_r' p_r' = e_r / sum_r' e_r'
-        float den = 0.f;
-#pragma unroll
-        for (int r = 0; r < kMaxK; ++r)
-            if (r < k) den += expf(key_value(top[r]) - m);
-        if (lane < k) {
-            uint64_t mine = top[0];
-#pragma unroll
-            for (int r = 1; r < kMaxK; ++r)
-                if (r == lane) mine = top[r];
-            const int j = key_index(mine);
-            p.topk_idx[(size_t)s * k + lane] = j;
-            p.topk_w[(size_t)s * k + lane] = expf(key_value(mine) - m) / den;
-            atomicAdd(&s_hist[lane * E + j], 1);
-        }
+        route_token_wave<EQ>(p, s, lane, s_hist, s_cand[wave], pacc, zacc);
     }
 
     // deterministic block reduction of the probability and lse^2 partials
@@ -540,6 +556,236 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
     }
 }
 
+// Fast route for E <= 32*L (L = 1, 2, 4 or 8): one block per 64-token tile
+// with L lanes per token (64*L threads).  Lane l of a token holds the
+// logits of experts 4*(l + L*i) + u (i < 8, u < 4), keeps its own top-K1
+// (K1 >= k+1) in registers sorted by (logit descending, index ascending),
+// and the token's lanes merge their lists with shuffles.  A token whose
+// top-k has a near tie (a sorted pair r < k closer than tau) is routed
+// afterwards by route_token_wave, which refines and decides it exactly as
+// route_kernel does; it contributes nothing to the fast pass.  Per-expert
+// probability sums run through LDS in token order, so the partials stay
+// deterministic.
+template <int L, int K1>
+__global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
+    constexpr int NT = 64 * L, EQ = (L + 1) / 2;   // threads; wave-router experts per lane
+    extern __shared__ unsigned char smem[];
+    const int E = p.E, k = p.k, nb = p.nb;
+    const int EP = E + 4;                                        // padded row of s_pt
+    int* s_hist = reinterpret_cast<int*>(smem);                  // [k][E]
+    float* s_pt = reinterpret_cast<float*>(s_hist + k * E);      // [64][EP] probabilities
+    float* s_slow = s_pt + kTokBlock * EP;                       // [L][E] slow-path sums
+    __shared__ float s_lse2[kTokBlock], s_z[L];
+    __shared__ int s_flag[kTokBlock], s_list[kTokBlock], s_nlist;
+    __shared__ int s_cand[L][kMaxSel];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t = tid / L, l = tid % L;                          // token of the tile, part
+    const int b = blockIdx.x;
+    const int s = b * kTokBlock + t;
+    const bool live = s < p.S;
+    for (int i = tid; i < k * E; i += NT) s_hist[i] = 0;
+
+    // this lane's logits (16-byte loads when every row is 16-byte aligned)
+    float v[32];
+    const float* lrow = p.logits + (size_t)(live ? s : 0) * E;
+    const bool vec = (E & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int j0 = 4 * (l + L * i);
+        if (vec && live && j0 + 3 < E) {
+            const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(lrow + j0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[4 * i + u] = q4[u];
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[4 * i + u] = live && j0 + u < E ? lrow[j0 + u] : 0.f;
+        }
+    }
+    // Local top-K1.  Experts are visited in decreasing index order, so a new
+    // entry has a lower index than every listed one and an entry carried down
+    // sorted above its neighbours: ">=" on the key alone orders by (key
+    // descending, index ascending).  Padding experts (key 0) fill the list
+    // first and are displaced by any real logit.
+    const int nsel = k + 1 <= E ? k + 1 : E;
+    uint32_t tk[K1];
+    int ti[K1];
+#pragma unroll
+    for (int r = 0; r < K1; ++r) {
+        tk[r] = 0u;
+        ti[r] = 0x7fffffff;
+    }
+#pragma unroll
+    for (int i = 7; i >= 0; --i)
+#pragma unroll
+        for (int u = 3; u >= 0; --u) {
+            const int j = 4 * (l + L * i) + u;
+            uint32_t key = j < E ? float_order_key(v[4 * i + u]) : 0u;
+            int idx = j;
+#pragma unroll
+            for (int r = 0; r < K1; ++r) {
+                const bool gt = key >= tk[r];
+                const uint32_t kk = gt ? tk[r] : key;
+                const int ii = gt ? ti[r] : idx;
+                tk[r] = gt ? key : tk[r];
+                ti[r] = gt ? idx : ti[r];
+                key = kk;
+                idx = ii;
+            }
+        }
+    // merge the token's L lists: nsel rounds of a group maximum
+    uint32_t gk[K1];
+    int gi[K1];
+#pragma unroll
+    for (int r = 0; r < K1; ++r) {
+        gk[r] = 0u;
+        gi[r] = 0x7fffffff;
+        if (r < nsel) {
+            uint32_t bk = tk[0];
+            int bi = ti[0];
+#pragma unroll
+            for (int m = 1; m < L; m <<= 1) {
+                const uint32_t ok = __shfl_xor(bk, m);
+                const int oi = __shfl_xor(bi, m);
+                const bool take = ok > bk || (ok == bk && oi < bi);
+                bk = take ? ok : bk;
+                bi = take ? oi : bi;
+            }
+            gk[r] = bk;
+            gi[r] = bi;
+            if (ti[0] == bi) {   // this lane owned it: pop its head
+#pragma unroll
+                for (int q = 0; q + 1 < K1; ++q) {
+                    tk[q] = tk[q + 1];
+                    ti[q] = ti[q + 1];
+                }
+                tk[K1 - 1] = 0u;
+                ti[K1 - 1] = 0x7fffffff;
+            }
+        }
+    }
+    auto kval = [](uint32_t u) {
+        return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+    };
+    bool flag = false;
+    if (p.tau > 0.f && nsel > 1) {
+#pragma unroll
+        for (int r = 0; r + 1 < K1; ++r)
+            if (r < k && r + 1 < nsel) flag |= kval(gk[r]) - kval(gk[r + 1]) < p.tau;
+    }
+    const bool fast = live && !flag;
+
+    // softmax over the token's E logits, stabilised by the largest
+    // (__expf: the hardware exp2 of x*log2(e), within ~2e-6 relative here)
+    const float m = kval(gk[0]);
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = 4 * (l + L * i) + u;
+            v[4 * i + u] = j < E ? __expf(v[4 * i + u] - m) : 0.f;
+            part += v[4 * i + u];
+        }
+#pragma unroll
+    for (int msk = 1; msk < L; msk <<= 1) part += __shfl_xor(part, msk);
+    const float inv = 1.0f / part;
+    // probabilities of this token to its LDS row (zeros unless fast)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = 4 * (l + L * i) + u;
+            if (j < E) s_pt[t * EP + j] = fast ? v[4 * i + u] * inv : 0.f;
+        }
+    if (l == 0) {
+        const float lse = m + logf(part);
+        s_lse2[t] = fast ? lse * lse : 0.f;
+        s_flag[t] = live && flag;
+    }
+    __syncthreads();   // s_hist cleared; rows and flags written
+    if (fast) {
+        // renormalised top-k weights: p_r / sum_r' p_r' = e_r / sum_r' e_r'
+        float den = 0.f;
+#pragma unroll
+        for (int r = 0; r + 1 < K1; ++r)
+            if (r < k) den += __expf(kval(gk[r]) - m);
+#pragma unroll
+        for (int r = 0; r + 1 < K1; ++r) {
+            if (r < k && r % L == l) {
+                p.topk_idx[(size_t)s * k + r] = gi[r];
+                p.topk_w[(size_t)s * k + r] = __expf(kval(gk[r]) - m) / den;
+                atomicAdd(&s_hist[r * E + gi[r]], 1);
+            }
+        }
+    }
+    // flagged tokens, in token order, go to the wave router
+    if (wave == 0) {
+        const bool f = s_flag[lane] != 0;
+        const uint64_t bal = __ballot(f);
+        if (f) s_list[__popcll(bal & ((1ull << lane) - 1ull))] = lane;
+        if (lane == 0) s_nlist = __popcll(bal);
+    }
+    __syncthreads();
+    float pacc[EQ];
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) pacc[q] = 0.f;
+    float zacc = 0.f;
+    const int nl = s_nlist;
+    for (int f = wave; f < nl; f += L)
+        route_token_wave<EQ>(p, b * kTokBlock + s_list[f], lane, s_hist, s_cand[wave], pacc, zacc);
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+        const int j = lane + 64 * q;
+        if (j < E) s_slow[wave * E + j] = pacc[q];
+    }
+    if (lane == 0) s_z[wave] = zacc;
+    __syncthreads();
+
+    // deterministic partials: fast tokens in a fixed order, then the waves'
+    for (int j = tid; j < E; j += NT) {
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int q = 0; q < kTokBlock; q += 4)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a4[u] += s_pt[(q + u) * EP + j];
+        float a = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+#pragma unroll
+        for (int w = 0; w < L; ++w) a += s_slow[w * E + j];
+        p.ppart[(size_t)b * E + j] = a;
+    }
+    if (wave == 0) {
+        float a = wave_sum_f32(s_lse2[lane]);
+        if (lane == 0) {
+#pragma unroll
+            for (int w = 0; w < L; ++w) a += s_z[w];
+            p.zpart[b] = a;
+        }
+    }
+    const int T = k * nb;
+    for (int i = tid; i < k * E; i += NT) {
+        const int r = i / E, e = i - r * E;
+        p.hist[(size_t)e * T + (size_t)r * nb + b] = s_hist[i];
+    }
+}
+
+template <int L, int K1>
+hipError_t launch_route_fast_t(const RouteParams& p, hipStream_t st) {
+    const size_t lds = sizeof(int) * (size_t)p.k * p.E +
+                       sizeof(float) * ((size_t)kTokBlock * (p.E + 4) + (size_t)L * p.E);
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_fast_kernel<L, K1>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    route_fast_kernel<L, K1><<<p.nb, 64 * L, lds, st>>>(p);
+    return hipGetLastError();
+}
+template <int L>
+hipError_t launch_route_fast_k(const RouteParams& p, hipStream_t st) {
+    if (p.k <= 2) return launch_route_fast_t<L, 3>(p, st);
+    if (p.k <= 4) return launch_route_fast_t<L, 5>(p, st);
+    return launch_route_fast_t<L, kMaxK + 1>(p, st);
+}
+
 template <int EQ, int NW>
 hipError_t launch_route_t(const RouteParams& p, hipStream_t st) {
     const size_t lds = sizeof(int) * (size_t)p.k * p.E + sizeof(float) * NW * (size_t)p.E;
@@ -553,6 +799,11 @@ hipError_t launch_route_t(const RouteParams& p, hipStream_t st) {
 
 hipError_t launch_route(const RouteParams& p, hipStream_t st) {
     const int eq = (int)ceil_div(p.E, kWave);
+    const int lanes = (int)ceil_div(p.E, 32);   // fast route: 32 logits per lane
+    if (lanes <= 1) return launch_route_fast_k<1>(p, st);
+    if (lanes <= 2) return launch_route_fast_k<2>(p, st);
+    if (lanes <= 4) return launch_route_fast_k<4>(p, st);
+    if (lanes <= 8) return launch_route_fast_k<8>(p, st);
     if (eq <= 1) return launch_route_t<1, 16>(p, st);
     if (eq <= 2) return launch_route_t<2, 16>(p, st);
     if (eq <= 4) return launch_route_t<4, 16>(p, st);

@@ -63,11 +63,13 @@ constexpr int kTileCounters = 16;
 
 // Workspace layout, every region 256-byte aligned:
 //   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
-//            mt_start + m-tile experts, GEMM tile counters, inverse slot map [E,C]
+//            mt_start + m-tile experts, GEMM tile counters, inverse slot map [E,C],
+//            router weight split into three bf16 planes [3,E,d] (bf16 x)
 //   [ffn]    H [E,C,h]
 //   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
 struct Carve {
-    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, ctr, inv;
+    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, ctr, inv,
+        wsplit;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -95,6 +97,7 @@ Carve carve(const Plan& p) {
     c.mt_start = take(((size_t)p.E + 1 + mtile_table_len(p.E, p.C)) * 4);
     c.ctr = take(kTileCounters * 4);
     c.inv = take((size_t)p.E * p.C * 4);
+    c.wsplit = gate_uses_split(p.bf16, p.d) ? take((size_t)3 * p.E * p.d * 2) : o;
     c.route_end = o;
     c.H = take((size_t)p.E * p.C * p.h * p.es);
     c.ffn_end = o;
@@ -134,7 +137,9 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     double* psum = at<double>(ws, cv.psum);
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
-    if (!logits_in) MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, st));
+    if (!logits_in)
+        MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, at<void>(ws, cv.wsplit),
+                                   st));
     record(ev, 1, st);
     RouteParams rp{};
     rp.logits = logits;
