@@ -105,7 +105,7 @@ typedef struct moe_config {
 
 /* Number of events moe_layer_forward records when stage_events != NULL:
  * [0] start, [1] after router logits, [2] after softmax/top-k, [3] after
- * slot scan and losses, [4] after slot positions, [5] after dispatch,
+ * the slot scan, [4] after slot positions and losses, [5] after dispatch,
  * [6] after expert GEMM 1, [7] after expert GEMM 2, [8] after combine. */
 #define MOE_NUM_STAGE_EVENTS 9
 

@@ -40,14 +40,17 @@ hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t*
                             int32_t* occ, const float* ppart, double* psum, hipStream_t st);
 // losses = {aux, z}; mt_start[e] = sum_{e'<e} ceil(occ[e']/bm) (E+1 entries);
 // zeroes the n_ctr GEMM tile counters.
-hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
-                           const int32_t* occ, int S, int E, int nb, int bm, float* losses,
-                           int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st);
-// slot[s,r] from the scanned tile bases and stable in-tile ranks; with inv
-// non-null also the inverse map inv[e*C + slot] = s of every kept assignment.
-hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
-                                 int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
-                                 hipStream_t st);
+// slot[s,r] from the scanned tile bases and stable in-tile ranks (with inv
+// non-null also the inverse map inv[e*C + slot] = s of every kept
+// assignment); in the same launch, aux = E * sum_j f_j P_j and z = mean
+// lse^2 into losses, the GEMM m-tile prefix (m-tile height bm) into
+// mt_start, and n_ctr tile counters zeroed.
+hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* hist_base, int S,
+                                     int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
+                                     const double* psum, const float* zpart,
+                                     const int32_t* counts, const int32_t* occ, int bm,
+                                     float* losses, int32_t* mt_start, int32_t* ctr, int n_ctr,
+                                     hipStream_t st);
 // Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN);
 // zeroes the n_ctr GEMM tile counters.
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,

@@ -161,11 +161,10 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     MOE_TRY(launch_route(rp, st));
     record(ev, 2, st);
     MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, ppart, psum, st));
-    MOE_TRY(launch_finalize(psum, zpart, counts, occ, p.S, p.E, p.nb,
-                            gemm_block_m(p.bf16, p.S, p.E, p.k), losses, mt,
-                            at<int32_t>(ws, cv.ctr), kTileCounters, st));
     record(ev, 3, st);
-    MOE_TRY(launch_slot_positions(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, inv, st));
+    MOE_TRY(launch_positions_finalize(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, inv, psum,
+                                      zpart, counts, occ, gemm_block_m(p.bf16, p.S, p.E, p.k),
+                                      losses, mt, at<int32_t>(ws, cv.ctr), kTileCounters, st));
     record(ev, 4, st);
     return MOE_OK;
 }

@@ -89,14 +89,11 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hi
 // z = (sum of the block partials of lse^2) / S.  Sums run in a fixed order
 // in fp64, so the result is deterministic.  Also the per-expert m-tile
 // prefix for the expert GEMMs.
-__global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict__ psum,
-                                                       const float* __restrict__ zpart,
-                                                       const int32_t* __restrict__ counts,
-                                                       const int32_t* __restrict__ occ, int S,
-                                                       int E, int nb, int bm,
-                                                       float* __restrict__ losses,
-                                                       int32_t* __restrict__ mt_start,
-                                                       int32_t* __restrict__ ctr, int n_ctr) {
+__device__ void finalize_block(const double* __restrict__ psum, const float* __restrict__ zpart,
+                               const int32_t* __restrict__ counts,
+                               const int32_t* __restrict__ occ, int S, int E, int nb, int bm,
+                               float* __restrict__ losses, int32_t* __restrict__ mt_start,
+                               int32_t* __restrict__ ctr, int n_ctr) {
     __shared__ double s_red[256];
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
@@ -141,14 +138,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(const double* __restrict_
 }
 
 // One block (4 waves) per token block; wave w takes ranks w, w+4, ...
-__global__ __launch_bounds__(256) void slot_positions_kernel(const int32_t* __restrict__ topk_idx,
-                                                             const int32_t* __restrict__ hist_base,
-                                                             int S, int E, int k, int nb, int C,
-                                                             int nbits,
-                                                             int32_t* __restrict__ slot,
-                                                             int32_t* __restrict__ inv) {
+__device__ void positions_block(int b, const int32_t* __restrict__ topk_idx,
+                                const int32_t* __restrict__ hist_base, int S, int E, int k,
+                                int nb, int C, int nbits, int32_t* __restrict__ slot,
+                                int32_t* __restrict__ inv) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x;
     const int s = b * kTokBlock + lane;
     const bool valid = s < S;
     const int T = k * nb;
@@ -216,21 +210,33 @@ hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t*
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const double* psum, const float* zpart, const int32_t* counts,
-                           const int32_t* occ, int S, int E, int nb, int bm, float* losses,
-                           int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st) {
-    finalize_kernel<<<1, 256, 0, st>>>(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start,
-                                       ctr, n_ctr);
-    return hipGetLastError();
+// Slot positions (blocks 0..nb-1) and, in one extra block, the losses, the
+// GEMM m-tile prefix and the tile counters: the latter need only the slot
+// scan's results, so both run in one launch.
+__global__ __launch_bounds__(256) void positions_finalize_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ hist_base, int S, int E,
+    int k, int nb, int C, int nbits, int32_t* __restrict__ slot, int32_t* __restrict__ inv,
+    const double* __restrict__ psum, const float* __restrict__ zpart,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ occ, int bm,
+    float* __restrict__ losses, int32_t* __restrict__ mt_start, int32_t* __restrict__ ctr,
+    int n_ctr) {
+    if ((int)blockIdx.x < nb)
+        positions_block(blockIdx.x, topk_idx, hist_base, S, E, k, nb, C, nbits, slot, inv);
+    else
+        finalize_block(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start, ctr, n_ctr);
 }
 
-hipError_t launch_slot_positions(const int32_t* topk_idx, const int32_t* hist_base, int S,
-                                 int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
-                                 hipStream_t st) {
+hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* hist_base, int S,
+                                     int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
+                                     const double* psum, const float* zpart,
+                                     const int32_t* counts, const int32_t* occ, int bm,
+                                     float* losses, int32_t* mt_start, int32_t* ctr, int n_ctr,
+                                     hipStream_t st) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    slot_positions_kernel<<<nb, 256, 0, st>>>(topk_idx, hist_base, S, E, k, nb, C, nbits, slot,
-                                              inv);
+    positions_finalize_kernel<<<nb + 1, 256, 0, st>>>(topk_idx, hist_base, S, E, k, nb, C, nbits,
+                                                      slot, inv, psum, zpart, counts, occ, bm,
+                                                      losses, mt_start, ctr, n_ctr);
     return hipGetLastError();
 }
 
