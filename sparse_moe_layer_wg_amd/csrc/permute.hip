@@ -101,8 +101,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
         for (int q = 0; q < NE; ++q) acc[q] = 0.f;
         u32x4_t v[kMaxK];
 #pragma unroll
-        for (int r = 0; r < kMaxK; ++r)
-            if (src[r] >= 0) v[r] = out[src[r] + i];
+        for (int r = 0; r < kMaxK; ++r)   // each (expert, slot) row is read once
+            if (src[r] >= 0) v[r] = __builtin_nontemporal_load(out + src[r] + i);
 #pragma unroll
         for (int r = 0; r < kMaxK; ++r) {
             if (src[r] >= 0) {
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             o[q] = BF16 ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : __float_as_uint(acc[q]);
-        dst[i] = o;
+        __builtin_nontemporal_store(o, dst + i);   // y is not read again here
     }
 }
 
