@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="balanced_bf16", choices=mw.ORDER)
+    ap.add_argument("--dropless", action="store_true",
+                    help="no capacity limit: compact [S*k,d] expert segments, no drops")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -101,8 +103,12 @@ def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float) -> dict:
     def run(n):
         C = oracle.capacity(n, w.E, w.k, w.capacity_factor)
         t0 = time.perf_counter()
-        oracle.layer(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"], host["w2"],
-                     host["b2"], w.k, C)
+        if w.dropless:
+            oracle.layer_dropless(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
+                                  host["w2"], host["b2"], w.k)
+        else:
+            oracle.layer(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
+                         host["w2"], host["b2"], w.k, C)
         return time.perf_counter() - t0
 
     n0 = min(w.S, 256)
@@ -113,8 +119,9 @@ def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float) -> dict:
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {w.S} tokens of the same workload (same E, d, h, k, "
-                      f"capacity_factor; C scaled with the sample), full fp64 oracle layer "
-                      f"from logits to y, {t:.1f} s"}
+                      + ("dropless routing" if w.dropless else
+                         "capacity_factor; C scaled with the sample")
+                      + f"), full fp64 oracle layer from logits to y, {t:.1f} s"}
 
 
 def main():
@@ -125,8 +132,11 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = mw.get(a.workload)
+    if a.dropless:
+        w = w.with_(dropless=True, name=w.name + "_dropless")
     inputs = mw.generate(w, "cuda")
-    cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype)
+    cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype,
+                     dropless=w.dropless)
     layer = MoELayer.from_inputs(cfg, inputs, keep=False)
     x = inputs["x"]
     stream = torch.cuda.current_stream()
@@ -233,7 +243,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "S": w.S, "d_model": w.d, "d_ff": w.h, "E": w.E,
-                   "k": w.k, "capacity_factor": w.capacity_factor, "C": probe_C(cfg),
+                   "k": w.k, "capacity_factor": None if w.dropless else w.capacity_factor,
+                   "C": None if w.dropless else probe_C(cfg), "dropless": w.dropless,
                    "seed": w.seed},
         "roofline": roof,
         "ffn_mfma_frac": ffn_flops / ffn_s / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),

@@ -42,7 +42,8 @@
  *     asynchronous: outputs are valid once the stream has been synchronised.
  *     The library performs no host<->device copies and no synchronisation.
  *   Layouts.  Row-major, no padding:  x, y [S,d];  Wg [E,d] fp32;  bg [E]
- *     fp32;  W1 [E,h,d];  b1 [E,h];  W2 [E,d,h];  b2 [E,d];  xd, out [E,C,d];
+ *     fp32;  W1 [E,h,d];  b1 [E,h];  W2 [E,d,h];  b2 [E,d];  xd, out [E,C,d]
+ *     ([S*k,d] with MOE_CFG_DROPLESS);
  *     logits [S,E] fp32;  topk_idx, slot [S,k] int32;  topk_w [S,k] fp32;
  *     counts [k,E] int32 (assignments of rank r to expert e before capacity);
  *     losses [2] fp32 = {aux, z}.
@@ -86,7 +87,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * capacity_factor > 0 when capacity == 0; capacity >= 0.
  * Supported by the kernels (else MOE_ERR_UNSUPPORTED): E <= 2048, k <= 8,
  * k * E <= 16384, d_model and d_ff multiples of 64 for bf16 and of 4 for
- * fp32, and E * C * max(d_model, d_ff) < 2^31. */
+ * fp32, and R * max(d_model, d_ff) < 2^31 with R = moe_dispatch_rows. */
 typedef struct moe_config {
     int32_t S;               /* tokens on this GPU                         */
     int32_t d_model;         /* d: model width                             */
@@ -96,8 +97,24 @@ typedef struct moe_config {
     int32_t capacity;        /* C per expert; 0 = ceil(cf * k * S / E)     */
     double capacity_factor;  /* cf                                         */
     int32_t act_dtype;       /* moe_dtype                                  */
-    uint32_t reserved;       /* must be 0                                  */
+    uint32_t flags;          /* MOE_CFG_* bits; all others must be 0       */
 } moe_config;
+
+/* moe_config.flags: dropless routing.  No assignment is dropped and no
+ * capacity padding exists: the dispatch buffer xd and the expert output out
+ * hold S*k rows [S*k,d], one per (token, rank) assignment, in variable-length
+ * expert segments.  Segment e starts at row seg_e = sum_{e'<e} n_e' (n_e =
+ * sum_r counts[r,e]), experts in index order; inside a segment rows follow
+ * the capacity mode's slot order (rank by rank, tokens in order).  slot[s,r]
+ * is then the assignment's global row seg_e + position (never -1), and the
+ * expert step reads and writes row seg_e + c for c < n_e.  capacity must be 0
+ * and capacity_factor is ignored.  Same arithmetic as the capacity mode with
+ * a capacity no expert can reach, without its E*C-row buffers.  Source:
+ * "GShard: Scaling Giant Models with Conditional Computation and Automatic
+ * Sharding" (inference-research paper card), method paragraph: the token
+ * dropping of capacity-limited routing is what the later MegaBlocks work
+ * removes. */
+#define MOE_CFG_DROPLESS 1u
 
 /* moe_gate flag: read `logits` as an input instead of computing them from x,
  * Wg and bg (x, w_gate and gate_bias may then be NULL). */
@@ -109,9 +126,14 @@ typedef struct moe_config {
  * [6] after expert GEMM 1, [7] after expert GEMM 2, [8] after combine. */
 #define MOE_NUM_STAGE_EVENTS 9
 
-/* Capacity C of the config (capacity if > 0, else ceil(cf*k*S/E)), or -1 if
- * the config is invalid. */
+/* Capacity C of the config (capacity if > 0, else ceil(cf*k*S/E); S with
+ * MOE_CFG_DROPLESS, which no expert can exceed), or -1 if the config is
+ * invalid. */
 int32_t moe_capacity(const moe_config *cfg);
+
+/* Rows of the dispatch buffer xd and the expert output out: E*C in capacity
+ * mode, S*k with MOE_CFG_DROPLESS; -1 if the config is invalid. */
+int64_t moe_dispatch_rows(const moe_config *cfg);
 
 /* Device workspace bytes that moe_layer_forward needs (enough for every
  * other entry point too) when all of its optional outputs are NULL. */
@@ -125,7 +147,8 @@ const char *moe_status_string(int32_t status);
  *      (all unused with MOE_GATE_LOGITS_IN).
  * Out: logits [S,E] fp32 (input with MOE_GATE_LOGITS_IN; may be NULL
  *      otherwise, then kept in ws), topk_idx [S,k], topk_w [S,k],
- *      slot [S,k] (-1 = dropped), counts [k,E], losses [2].
+ *      slot [S,k] (-1 = dropped; with MOE_CFG_DROPLESS the global row in
+ *      xd/out), counts [k,E], losses [2].
  * Logits within a small margin of a top-k decision are re-evaluated in fp64
  * and rounded once to fp32, and the stored logits hold those values. */
 moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,
@@ -135,14 +158,19 @@ moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,
 
 /* Permute token rows into per-expert capacity buffers (the local stand-in
  * for the dispatch all-to-all): xd[idx[s,r], slot[s,r], :] = x[s, :] for
- * every slot[s,r] >= 0.  Bit-exact copy.  Needs no workspace. */
+ * every slot[s,r] >= 0 (with MOE_CFG_DROPLESS: xd[slot[s,r], :] = x[s, :]).
+ * Bit-exact copy.  Needs no workspace. */
 moe_status moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                         const int32_t *slot, void *xd, hipStream_t stream);
 
 /* Expert FFNs over the filled slots: for e < E and c < occ_e =
  * min(sum_r counts[r,e], C): out[e,c] = ReLU(xd[e,c] W1_e^T + b1_e) W2_e^T
  * + b2_e, fp32 accumulation; the hidden activations are rounded to act_dtype
- * (they live in ws).  Rows c >= occ_e of out are not written. */
+ * (they live in ws).  Rows c >= occ_e of out are not written.  With
+ * MOE_CFG_DROPLESS, occ_e = n_e and row (e,c) is row seg_e + c of the
+ * [S*k,d] buffers (seg_e as defined at MOE_CFG_DROPLESS); counts are those
+ * moe_gate wrote (they total S*k): a segment that would reach past row S*k
+ * is cut there, so no access leaves the buffers. */
 moe_status moe_expert_ffn(const moe_config *cfg, const void *xd, const int32_t *counts,
                           const void *w1, const void *b1, const void *w2, const void *b2,
                           void *out, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -150,8 +178,8 @@ moe_status moe_expert_ffn(const moe_config *cfg, const void *xd, const int32_t *
 /* Gate-weighted combine back to token order (the local stand-in for the
  * second all-to-all): y[s] = sum over slot[s,r] >= 0 of
  * topk_w[s,r] * out[topk_idx[s,r], slot[s,r]], fp32 accumulation, rounded
- * to act_dtype; y[s] = 0 when every assignment of s was dropped.  Needs no
- * workspace. */
+ * to act_dtype; y[s] = 0 when every assignment of s was dropped.  With
+ * MOE_CFG_DROPLESS the row read is out[slot[s,r]].  Needs no workspace. */
 moe_status moe_combine(const moe_config *cfg, const void *out, const int32_t *topk_idx,
                        const int32_t *slot, const float *topk_w, void *y,
                        hipStream_t stream);

@@ -40,6 +40,7 @@ class Workload:
     seed: int
     gate_bias: str | None = None    # None or "zipf1.2"
     ffn_bias: str | None = None     # None or "zeros"
+    dropless: bool = False          # no capacity limit, compact expert segments
 
     @property
     def torch_dtype(self):

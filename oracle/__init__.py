@@ -191,6 +191,51 @@ def token_output(tokens, x, w1, b1, w2, b2, idx, slot, w) -> np.ndarray:
     return y
 
 
+def compact_rows(idx: np.ndarray, E: int) -> np.ndarray:
+    """Dropless layout: the row of each assignment (s, r) in compact expert
+    segments.  Assignments are numbered 0..S*k-1 in the order (expert, rank,
+    token): expert segments back to back in expert order, and inside a
+    segment the slot order of capacity routing (every first choice before
+    any second choice, tokens in order).  A reading of the paper card
+    "GShard: Scaling Giant Models with Conditional Computation and Automatic
+    Sharding", method paragraph (dropless routing, as in MegaBlocks, keeps
+    every assignment); the pages fix no layout.  A plain sort."""
+    idx = np.asarray(idx)
+    S, k = idx.shape
+    assert S == 0 or (idx.min() >= 0 and idx.max() < E)
+    tok = np.repeat(np.arange(S), k)
+    rank = np.tile(np.arange(k), S)
+    order = np.lexsort((tok, rank, idx.reshape(-1)))  # last key is the primary one
+    rows = np.empty(S * k, np.int64)
+    rows[order] = np.arange(S * k)
+    return rows.reshape(S, k)
+
+
+def layer_dropless(x, wg, bg, w1, b1, w2, b2, k: int, lg: np.ndarray | None = None) -> dict:
+    """Whole forward pass with no capacity limit (every assignment kept):
+    y[s] = sum_r w[s,r] FFN_{idx[s,r]}(x[s]), the dense top-k sum.  Routing,
+    weights and losses are those of capacity routing (a capacity of S cannot
+    be reached, as a token's k experts are distinct).  Also returns the
+    compact layout: ``rows`` [S,k] and the expert outputs ``out_rows``
+    [S*k,d] (fp64) and dispatched inputs ``xd_rows`` [S*k,d] in row order."""
+    x_act, _ = _act(x)
+    S = x_act.shape[0]
+    if lg is None:
+        lg = logits(x, wg, bg)
+    E = lg.shape[1]
+    res = layer(x, wg, bg, w1, b1, w2, b2, k, max(S, 1), lg=lg)
+    assert (res["slot"] >= 0).all()
+    rows = compact_rows(res["idx"], E)
+    d = x_act.shape[1]
+    out_rows = np.zeros((S * k, d), np.float64)
+    xd_rows = np.zeros((S * k, d), x_act.dtype)
+    flat = rows.reshape(-1)
+    out_rows[flat] = res["out"][res["idx"].reshape(-1), res["slot"].reshape(-1)]
+    xd_rows[flat] = np.repeat(x_act, k, axis=0)
+    res.update(rows=rows, out_rows=out_rows, xd_rows=xd_rows)
+    return res
+
+
 def layer(x, wg, bg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray | None = None) -> dict:
     """Whole forward pass.  With ``lg`` given, routing starts from those fp32
     logits instead of computing them (used to compare against a device that

@@ -7,6 +7,7 @@ loudly when ``libmoe.so`` has not been built: there is no fallback.
 """
 from ._lib import (  # noqa: F401
     MOE_BF16,
+    MOE_CFG_DROPLESS,
     MOE_F32,
     MOE_GATE_LOGITS_IN,
     MOE_NUM_STAGE_EVENTS,
@@ -16,6 +17,7 @@ from ._lib import (  # noqa: F401
     combine,
     config,
     dispatch,
+    dispatch_rows,
     expert_ffn,
     gate,
     layer_forward,

@@ -17,6 +17,7 @@ library_path = os.path.join(_PKG, "libmoe.so")
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_GATE_LOGITS_IN = 1
+MOE_CFG_DROPLESS = 1
 MOE_NUM_STAGE_EVENTS = 9
 
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
@@ -39,19 +40,26 @@ class MoeConfig(ctypes.Structure):
         ("capacity", ctypes.c_int32),
         ("capacity_factor", ctypes.c_double),
         ("act_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32),
     ]
 
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.act_dtype == MOE_BF16 else torch.float32
 
+    @property
+    def dropless(self) -> bool:
+        return bool(self.flags & MOE_CFG_DROPLESS)
 
-def config(S, d_model, d_ff, E, k, capacity_factor=1.0, capacity=0, dtype="bf16") -> MoeConfig:
+
+def config(S, d_model, d_ff, E, k, capacity_factor=1.0, capacity=0, dtype="bf16",
+           dropless=False) -> MoeConfig:
+    """Layer shape.  ``dropless``: no capacity limit; xd/out are compact
+    [S*k, d] expert segments and ``slot`` holds global rows."""
     dt = {"bf16": MOE_BF16, "f32": MOE_F32, torch.bfloat16: MOE_BF16,
           torch.float32: MOE_F32}[dtype]
     return MoeConfig(int(S), int(d_model), int(d_ff), int(E), int(k), int(capacity),
-                     float(capacity_factor), dt, 0)
+                     float(capacity_factor), dt, MOE_CFG_DROPLESS if dropless else 0)
 
 
 _lib = None
@@ -71,6 +79,8 @@ def library():
     vp, cfgp = ctypes.c_void_p, ctypes.POINTER(MoeConfig)
     lib.moe_capacity.argtypes = [cfgp]
     lib.moe_capacity.restype = ctypes.c_int32
+    lib.moe_dispatch_rows.argtypes = [cfgp]
+    lib.moe_dispatch_rows.restype = ctypes.c_int64
     lib.moe_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_status_string.argtypes = [ctypes.c_int32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -94,6 +104,11 @@ def _check(status: int, where: str):
 
 def capacity(cfg: MoeConfig) -> int:
     return int(library().moe_capacity(ctypes.byref(cfg)))
+
+
+def dispatch_rows(cfg: MoeConfig) -> int:
+    """Rows of xd/out: E*C, or S*k for a dropless config."""
+    return int(library().moe_dispatch_rows(ctypes.byref(cfg)))
 
 
 def workspace_bytes(cfg: MoeConfig) -> int:
@@ -157,39 +172,39 @@ def gate(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, loss
 
 
 def dispatch(cfg, x, topk_idx, slot, xd, stream=None):
-    """Permute token rows into [E,C,d] (``moe_dispatch``)."""
-    C = capacity(cfg)
+    """Permute token rows into [E,C,d] or compact [S*k,d] (``moe_dispatch``)."""
+    R = dispatch_rows(cfg)
     at = cfg.torch_dtype
     st = library().moe_dispatch(
         ctypes.byref(cfg), _arg(x, "x", at, cfg.S * cfg.d_model),
         _arg(topk_idx, "topk_idx", torch.int32, cfg.S * cfg.k),
         _arg(slot, "slot", torch.int32, cfg.S * cfg.k),
-        _arg(xd, "xd", at, cfg.E * C * cfg.d_model), _stream(stream))
+        _arg(xd, "xd", at, R * cfg.d_model), _stream(stream))
     _check(st, "moe_dispatch")
 
 
 def expert_ffn(cfg, xd, counts, w1, b1, w2, b2, out, ws, stream=None):
     """Expert ReLU FFNs over filled slots (``moe_expert_ffn``)."""
-    C = capacity(cfg)
+    R = dispatch_rows(cfg)
     E, d, h = cfg.E, cfg.d_model, cfg.d_ff
     at = cfg.torch_dtype
     wsp, wsb = _ws(ws)
     st = library().moe_expert_ffn(
-        ctypes.byref(cfg), _arg(xd, "xd", at, E * C * d),
+        ctypes.byref(cfg), _arg(xd, "xd", at, R * d),
         _arg(counts, "counts", torch.int32, cfg.k * E),
         _arg(w1, "w1", at, E * h * d), _arg(b1, "b1", at, E * h, required=False),
         _arg(w2, "w2", at, E * d * h), _arg(b2, "b2", at, E * d, required=False),
-        _arg(out, "out", at, E * C * d), wsp, wsb, _stream(stream))
+        _arg(out, "out", at, R * d), wsp, wsb, _stream(stream))
     _check(st, "moe_expert_ffn")
 
 
 def combine(cfg, out, topk_idx, slot, topk_w, y, stream=None):
     """Gate-weighted combine back to token order (``moe_combine``)."""
-    C = capacity(cfg)
+    R = dispatch_rows(cfg)
     at = cfg.torch_dtype
     S, k = cfg.S, cfg.k
     st = library().moe_combine(
-        ctypes.byref(cfg), _arg(out, "out", at, cfg.E * C * cfg.d_model),
+        ctypes.byref(cfg), _arg(out, "out", at, R * cfg.d_model),
         _arg(topk_idx, "topk_idx", torch.int32, S * k), _arg(slot, "slot", torch.int32, S * k),
         _arg(topk_w, "topk_w", torch.float32, S * k), _arg(y, "y", at, S * cfg.d_model),
         _stream(stream))
@@ -202,7 +217,7 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
     """Whole forward pass (``moe_layer_forward``).  ``events``: None or a list
     of MOE_NUM_STAGE_EVENTS entries, each None (boundary not recorded) or a
     torch.cuda.Event already created."""
-    C = capacity(cfg)
+    R = dispatch_rows(cfg)
     S, d, h, E, k = cfg.S, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     at = cfg.torch_dtype
     wsp, wsb = _ws(ws)
@@ -226,7 +241,7 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
         _arg(slot, "slot", torch.int32, S * k, required=False),
         _arg(counts, "counts", torch.int32, k * E, required=False),
         _arg(losses, "losses", torch.float32, 2, required=False),
-        _arg(xd, "xd", at, E * C * d, required=False),
-        _arg(out, "out", at, E * C * d, required=False),
+        _arg(xd, "xd", at, R * d, required=False),
+        _arg(out, "out", at, R * d, required=False),
         wsp, wsb, ev, _stream(stream))
     _check(st, "moe_layer_forward")

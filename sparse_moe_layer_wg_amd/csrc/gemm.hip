@@ -36,7 +36,9 @@
 //   and bf16 rounding are applied there and the tile leaves through LDS as
 //   16-byte row-contiguous stores.
 //   With a_rows set, A rows are gathered from the token rows through the
-//   inverse slot map (the dispatch permute fused into the loads).
+//   inverse slot map (the dispatch permute fused into the loads).  With row0
+//   set, expert e's rows start at row0[e] instead of e*C: the compact expert
+//   segments of dropless routing, laid end to end with no padding.
 //   Tiles come from a compact list: expert e owns m-tiles
 //   [mt_start[e], mt_start[e+1]) (built on the device from the occupancies),
 //   ordered by expert, then in groups of 4 n-tiles (m-tile-major inside a
@@ -127,9 +129,12 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         const int m0 = mi * BM, n0 = (ng * GN + r % gsize) * BN;
         const int M = __builtin_amdgcn_readfirstlane(p.occ[e]);
         const bool strip = SR > 0 && mi == mtiles - 1 && M - m0 > BM;
+        // first row of expert e: e*C in padded buffers, row0[e] in compact ones
+        const size_t row_e = p.row0 ? (size_t)__builtin_amdgcn_readfirstlane(p.row0[e])
+                                    : (size_t)e * p.C;
         const char* __restrict__ Ab = reinterpret_cast<const char*>(
-            static_cast<const bf16_t*>(p.A) + (p.a_rows ? (size_t)0 : (size_t)e * p.C * K));
-        const int32_t* __restrict__ arow = p.a_rows ? p.a_rows + (size_t)e * p.C : nullptr;
+            static_cast<const bf16_t*>(p.A) + (p.a_rows ? (size_t)0 : row_e * K));
+        const int32_t* __restrict__ arow = p.a_rows ? p.a_rows + row_e : nullptr;
         const char* __restrict__ Bb =
             reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.B) + (size_t)e * N * K);
 
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         // applied there; the bf16 results pass through LDS (the stage
         // buffers are free after the k-loop's last barrier; each wave uses
         // its own region) and leave as 16-byte row-contiguous stores.
-        bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) + (size_t)e * p.C * N;
+        bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) + row_e * N;
         const bf16_t* bias = p.bias ? static_cast<const bf16_t*>(p.bias) + (size_t)e * N : nullptr;
         auto finish4 = [&](const f32x16_t& a, int q, int n) {
             float v[4];
@@ -382,7 +387,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     const int N = p.N, K = p.K;
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     const int lrow = tid / 4, lk = (tid % 4) * 4;
-    const float* __restrict__ A = static_cast<const float*>(p.A) + (size_t)e * p.C * K;
+    const size_t row_e = p.row0 ? (size_t)p.row0[e] : (size_t)e * p.C;  // expert's first row
+    const float* __restrict__ A = static_cast<const float*>(p.A) + row_e * K;
     const float* __restrict__ B = static_cast<const float*>(p.B) + (size_t)e * N * K;
 
     float acc[4][4];
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
                 for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
         }
     }
-    float* __restrict__ Cout = static_cast<float*>(p.Cout) + (size_t)e * p.C * N;
+    float* __restrict__ Cout = static_cast<float*>(p.Cout) + row_e * N;
     const float* bias = p.bias ? static_cast<const float*>(p.bias) + (size_t)e * N : nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

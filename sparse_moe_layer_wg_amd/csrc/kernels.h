@@ -41,38 +41,49 @@ hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t*
 // losses = {aux, z}; mt_start[e] = sum_{e'<e} ceil(occ[e']/bm) (E+1 entries);
 // zeroes the n_ctr GEMM tile counters.
 // slot[s,r] from the scanned tile bases and stable in-tile ranks (with inv
-// non-null also the inverse map inv[e*C + slot] = s of every kept
-// assignment); in the same launch, aux = E * sum_j f_j P_j and z = mean
-// lse^2 into losses, the GEMM m-tile prefix (m-tile height bm) into
-// mt_start, and n_ctr tile counters zeroed.
+// non-null also the inverse map inv[row] = s of every kept assignment); in
+// the same launch, aux = E * sum_j f_j P_j and z = mean lse^2 into losses,
+// the GEMM m-tile prefix (m-tile height bm) into mt_start, and n_ctr tile
+// counters zeroed.  Padded rows (compact false): slot = position in the
+// expert, row = e*C + slot.  Compact rows: slot = row = seg[e] + position
+// with seg the exclusive prefix of occ over experts, also written to seg
+// (the expert GEMMs' row0).
 hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* hist_base, int S,
-                                     int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
-                                     const double* psum, const float* zpart,
+                                     int E, int k, int nb, int C, bool compact, int32_t* slot,
+                                     int32_t* inv, const double* psum, const float* zpart,
                                      const int32_t* counts, const int32_t* occ, int bm,
-                                     float* losses, int32_t* mt_start, int32_t* ctr, int n_ctr,
-                                     hipStream_t st);
+                                     float* losses, int32_t* mt_start, int32_t* seg,
+                                     int32_t* ctr, int n_ctr, hipStream_t st);
 // Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN);
-// zeroes the n_ctr GEMM tile counters.
+// zeroes the n_ctr GEMM tile counters; with seg non-null also the exclusive
+// prefix of occ over experts (compact rows), every segment cut to end by row
+// `rows` (the compact buffers' length).
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
-                            int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st);
+                            int32_t* mt_start, int32_t* seg, int rows, int32_t* ctr, int n_ctr,
+                            hipStream_t st);
 // Zero losses and counts (empty input).
 hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st);
 
 // ------------------------------------------------------------------ permute
+// Assignment (s,r) with expert e = topk_idx[s,r] and c = slot[s,r] is row
+// e*stride + c of xd / out, kept when 0 <= e < E and 0 <= c < limit
+// (padded rows: stride = limit = C; compact rows: stride 0, limit S*k).
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, const int32_t* slot,
-                           void* xd, int S, int d, int k, int E, int C, int elem_bytes,
-                           hipStream_t st);
+                           void* xd, int S, int d, int k, int E, int stride, int limit,
+                           int elem_bytes, hipStream_t st);
 hipError_t launch_combine(const void* out, const int32_t* topk_idx, const int32_t* slot,
-                          const float* topk_w, void* y, int S, int d, int k, int E, int C,
-                          bool bf16, hipStream_t st);
+                          const float* topk_w, void* y, int S, int d, int k, int E, int stride,
+                          int limit, bool bf16, hipStream_t st);
 
 // ------------------------------------------------------------------ expert GEMMs
 // Per expert e, rows m < occ[e]:
 //   Cout[e,m,n] = act(sum_k A[e,m,k] * B[e,n,k] + bias[e,n]),  act = ReLU or id.
 // A [E,C,K], B [E,N,K], bias [E,N] or NULL, Cout [E,C,N]; all act dtype.
-// With a_rows non-null, row m of expert e is instead row a_rows[e*C + m] of
-// A [*,K] (a gather straight from the token rows: the dispatch permute fused
-// into the loads).
+// With row0 non-null, expert e's rows start at row row0[e] of A, a_rows and
+// Cout instead of e*C (compact expert segments).  With a_rows non-null, row m
+// of expert e is instead row a_rows[e*C + m] (a_rows[row0[e] + m]) of A [*,K]
+// (a gather straight from the token rows: the dispatch permute fused into the
+// loads).
 struct GemmParams {
     const void* A;
     const void* B;
@@ -81,7 +92,8 @@ struct GemmParams {
     const int32_t* occ;
     const int32_t* mt_start;
     const int32_t* mt_expert;  // expert of each m-tile (mt_start[E] entries)
-    const int32_t* a_rows;  // NULL, or [E*C] token row of each filled slot
+    const int32_t* a_rows;  // NULL, or the token row of each filled row
+    const int32_t* row0;    // NULL (row e*C), or [E] first row of each expert
     int32_t* tile_ctr;      // 8 counters (one per XCD chunk), zero at launch
     int E, C, N, K;
     bool relu;
@@ -97,8 +109,13 @@ __host__ __device__ inline int expert_mtiles(int occ, int bm) {
     return occ <= bm + extra ? 1 : (occ - extra + bm - 1) / bm;
 }
 // The m-tile prefix mt_start [E+1] is followed in memory by the expert of
-// every m-tile; room for both: (E + 1) + mtile_table_len(E, C) int32.
-inline size_t mtile_table_len(int E, int C) { return (size_t)E * ((C + 63) / 64); }
+// every m-tile; room for both: (E + 1) + mtile_table_len(E, C, rows) int32,
+// where rows bounds the filled rows of all experts together (m-tiles are at
+// least 64 rows high).
+inline size_t mtile_table_len(int E, int C, size_t rows) {
+    const size_t per_expert = (size_t)E * ((C + 63) / 64), total = (rows + 63) / 64 + E;
+    return per_expert < total ? per_expert : total;
+}
 // m-tile height the expert GEMMs use for a layer shape (the m-tile prefix
 // mt_start must be built with the same value).
 int gemm_block_m(bool bf16, int S, int E, int k);

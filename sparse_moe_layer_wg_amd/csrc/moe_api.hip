@@ -14,22 +14,35 @@ using namespace moe;
 struct Plan {
     int S, d, h, E, k, C, nb;
     bool bf16;
-    size_t es;  // bytes per activation element
+    bool dropless;  // compact expert segments, no drops (C = S bounds every expert)
+    size_t rows;    // rows of the dispatch buffer / expert output: E*C or S*k
+    size_t es;      // bytes per activation element
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Row of assignment (e, slot) in xd/out is e*row_stride + slot, valid for
+// slot < row_limit: padded buffers [E,C,d], or compact ones where the slot is
+// already the global row.
+int row_stride(const Plan& p) { return p.dropless ? 0 : p.C; }
+int row_limit(const Plan& p) { return p.dropless ? (int)p.rows : p.C; }
 
 // Validates the config; fills the plan.  INVALID_ARG for values outside the
 // definition, UNSUPPORTED for valid shapes the kernels do not handle.
 moe_status make_plan(const moe_config* c, Plan* pl) {
     if (!c) return MOE_ERR_INVALID_ARG;
-    if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
+    if (c->flags & ~MOE_CFG_DROPLESS) return MOE_ERR_INVALID_ARG;
+    const bool dropless = (c->flags & MOE_CFG_DROPLESS) != 0;
     if (c->S < 0 || c->d_model < 1 || c->d_ff < 1 || c->E < 1 || c->k < 1 || c->k > c->E)
         return MOE_ERR_INVALID_ARG;
     if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (c->capacity < 0) return MOE_ERR_INVALID_ARG;
     double C;
-    if (c->capacity > 0) {
+    if (dropless) {
+        // Top-k experts are distinct, so no expert receives more than S rows.
+        if (c->capacity != 0) return MOE_ERR_INVALID_ARG;
+        C = c->S;
+    } else if (c->capacity > 0) {
         C = c->capacity;
     } else {
         if (!(c->capacity_factor > 0.0) || !isfinite(c->capacity_factor))
@@ -43,7 +56,8 @@ moe_status make_plan(const moe_config* c, Plan* pl) {
     const int q = bf16 ? 64 : 4;
     if (c->d_model % q != 0 || c->d_ff % q != 0) return MOE_ERR_UNSUPPORTED;
     const double wide = (double)(c->d_model > c->d_ff ? c->d_model : c->d_ff);
-    if ((double)c->E * C * wide >= 2147483648.0) return MOE_ERR_UNSUPPORTED;
+    const double rows = dropless ? (double)c->S * c->k : (double)c->E * C;
+    if (rows * wide >= 2147483648.0) return MOE_ERR_UNSUPPORTED;
     if ((double)c->S * wide >= 2147483648.0 || (double)c->S * c->E >= 2147483648.0)
         return MOE_ERR_UNSUPPORTED;
     pl->S = c->S;
@@ -54,6 +68,8 @@ moe_status make_plan(const moe_config* c, Plan* pl) {
     pl->C = (int)C;
     pl->nb = (int)ceil_div(c->S, kTokBlock);
     pl->bf16 = bf16;
+    pl->dropless = dropless;
+    pl->rows = (size_t)rows;
     pl->es = bf16 ? 2 : 4;
     return MOE_OK;
 }
@@ -63,13 +79,15 @@ constexpr int kTileCounters = 16;
 
 // Workspace layout, every region 256-byte aligned:
 //   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
-//            mt_start + m-tile experts, GEMM tile counters, inverse slot map [E,C],
-//            router weight split into three bf16 planes [3,E,d] (bf16 x)
-//   [ffn]    H [E,C,h]
-//   [layer]  one [E,C,d] buffer (dispatch buffer and expert output)
+//            mt_start + m-tile experts, expert segment starts [E], GEMM tile
+//            counters, inverse slot map [R], router weight split into three
+//            bf16 planes [3,E,d] (bf16 x)
+//   [ffn]    H [R,h]
+//   [layer]  one [R,d] buffer (dispatch buffer and expert output)
+// with R = rows: E*C padded, S*k compact (dropless).
 struct Carve {
-    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, ctr, inv,
-        wsplit;
+    size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, seg, ctr,
+        inv, wsplit;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -94,14 +112,15 @@ Carve carve(const Plan& p) {
     c.zpart = take((size_t)p.nb * 4);
     c.psum = take((size_t)p.E * 8);
     c.occ = take((size_t)p.E * 4);
-    c.mt_start = take(((size_t)p.E + 1 + mtile_table_len(p.E, p.C)) * 4);
+    c.mt_start = take(((size_t)p.E + 1 + mtile_table_len(p.E, p.C, p.rows)) * 4);
+    c.seg = take((size_t)p.E * 4);
     c.ctr = take(kTileCounters * 4);
-    c.inv = take((size_t)p.E * p.C * 4);
+    c.inv = take(p.rows * 4);
     c.wsplit = gate_uses_split(p.bf16, p.d) ? take((size_t)3 * p.E * p.d * 2) : o;
     c.route_end = o;
-    c.H = take((size_t)p.E * p.C * p.h * p.es);
+    c.H = take(p.rows * p.h * p.es);
     c.ffn_end = o;
-    c.xo = take((size_t)p.E * p.C * p.d * p.es);
+    c.xo = take(p.rows * p.d * p.es);
     c.end = o;
     return c;
 }
@@ -162,20 +181,25 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     record(ev, 2, st);
     MOE_TRY(launch_slot_scan(hist, p.E, p.k, p.nb, p.C, counts, occ, ppart, psum, st));
     record(ev, 3, st);
-    MOE_TRY(launch_positions_finalize(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, slot, inv, psum,
-                                      zpart, counts, occ, gemm_block_m(p.bf16, p.S, p.E, p.k),
-                                      losses, mt, at<int32_t>(ws, cv.ctr), kTileCounters, st));
+    MOE_TRY(launch_positions_finalize(topk_idx, hist, p.S, p.E, p.k, p.nb, p.C, p.dropless, slot,
+                                      inv, psum, zpart, counts, occ,
+                                      gemm_block_m(p.bf16, p.S, p.E, p.k), losses, mt,
+                                      at<int32_t>(ws, cv.seg), at<int32_t>(ws, cv.ctr),
+                                      kTileCounters, st));
     record(ev, 4, st);
     return MOE_OK;
 }
 
 // Both expert GEMMs.  a_rows: NULL (GEMM 1 reads the dispatch buffer xd) or
 // the inverse slot map (GEMM 1 gathers its rows from the token rows in xd).
+// seg: the experts' first rows in compact (dropless) buffers.
 moe_status run_ffn(const Plan& p, const void* xd, const int32_t* a_rows, const void* w1,
                    const void* b1, const void* w2, const void* b2, void* out, const int32_t* occ,
-                   const int32_t* mt, int32_t* ctr, void* H, hipEvent_t* ev, hipStream_t st) {
+                   const int32_t* mt, const int32_t* seg, int32_t* ctr, void* H, hipEvent_t* ev,
+                   hipStream_t st) {
     GemmParams g{};
     g.occ = occ;
+    g.row0 = p.dropless ? seg : nullptr;
     g.mt_start = mt;
     g.mt_expert = mt + p.E + 1;
     g.tile_ctr = ctr;
@@ -215,11 +239,25 @@ int32_t moe_capacity(const moe_config* cfg) {
     if (s == MOE_ERR_INVALID_ARG) return -1;
     if (s != MOE_OK) {
         // Valid but unsupported configs still have a capacity.
+        if (cfg->flags & MOE_CFG_DROPLESS) return cfg->S;
         if (cfg->capacity > 0) return cfg->capacity;
         double C = ceil(cfg->capacity_factor * (double)cfg->k * (double)cfg->S / (double)cfg->E);
         return C > 2147483647.0 ? -1 : (int32_t)C;
     }
     return p.C;
+}
+
+int64_t moe_dispatch_rows(const moe_config* cfg) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s == MOE_ERR_INVALID_ARG) return -1;
+    if (s != MOE_OK) {
+        const int32_t C = moe_capacity(cfg);
+        if (C < 0) return -1;
+        return (cfg->flags & MOE_CFG_DROPLESS) ? (int64_t)cfg->S * cfg->k
+                                               : (int64_t)cfg->E * C;
+    }
+    return (int64_t)p.rows;
 }
 
 moe_status moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
@@ -275,7 +313,8 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* top
     if (p.S == 0) return MOE_OK;
     if (!x || !topk_idx || !slot || !xd) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(xd, 16)) return MOE_ERR_INVALID_ARG;
-    MOE_TRY(launch_dispatch(x, topk_idx, slot, xd, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
+    MOE_TRY(launch_dispatch(x, topk_idx, slot, xd, p.S, p.d, p.k, p.E, row_stride(p),
+                            row_limit(p), (int)p.es, stream));
     return MOE_OK;
 }
 
@@ -295,10 +334,12 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* 
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
     int32_t* ctr = at<int32_t>(ws, cv.ctr);
+    int32_t* seg = at<int32_t>(ws, cv.seg);
     MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16, p.S, p.E, p.k), occ, mt,
-                             ctr, kTileCounters, stream));
-    return run_ffn(p, xd, nullptr, w1, b1, w2, b2, out, occ, mt, ctr, at<void>(ws, cv.H), nullptr,
-                   stream);
+                             p.dropless ? seg : nullptr, (int)p.rows, ctr, kTileCounters,
+                             stream));
+    return run_ffn(p, xd, nullptr, w1, b1, w2, b2, out, occ, mt, seg, ctr, at<void>(ws, cv.H),
+                   nullptr, stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* out, const int32_t* topk_idx,
@@ -309,7 +350,8 @@ moe_status moe_combine(const moe_config* cfg, const void* out, const int32_t* to
     if (p.S == 0) return MOE_OK;
     if (!out || !topk_idx || !slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
     if (!aligned(out, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
-    MOE_TRY(launch_combine(out, topk_idx, slot, topk_w, y, p.S, p.d, p.k, p.E, p.C, p.bf16, stream));
+    MOE_TRY(launch_combine(out, topk_idx, slot, topk_w, y, p.S, p.d, p.k, p.E, row_stride(p),
+                           row_limit(p), p.bf16, stream));
     return MOE_OK;
 }
 
@@ -353,13 +395,16 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     int32_t* inv = fuse ? at<int32_t>(ws, cv.inv) : nullptr;
     s = run_gate(p, cv, x, w_gate, gate_bias, L, false, idx, w, sl, cnt, los, ws, inv, ev, stream);
     if (s != MOE_OK) return s;
-    if (!fuse) MOE_TRY(launch_dispatch(x, idx, sl, XD, p.S, p.d, p.k, p.E, p.C, (int)p.es, stream));
+    if (!fuse)
+        MOE_TRY(launch_dispatch(x, idx, sl, XD, p.S, p.d, p.k, p.E, row_stride(p), row_limit(p),
+                                (int)p.es, stream));
     record(ev, 5, stream);
     s = run_ffn(p, fuse ? x : XD, inv, w1, b1, w2, b2, OUT, at<int32_t>(ws, cv.occ),
-                at<int32_t>(ws, cv.mt_start), at<int32_t>(ws, cv.ctr), at<void>(ws, cv.H), ev,
-                stream);
+                at<int32_t>(ws, cv.mt_start), at<int32_t>(ws, cv.seg), at<int32_t>(ws, cv.ctr),
+                at<void>(ws, cv.H), ev, stream);
     if (s != MOE_OK) return s;
-    MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, p.C, p.bf16, stream));
+    MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, row_stride(p), row_limit(p),
+                           p.bf16, stream));
     record(ev, 8, stream);
     return MOE_OK;
 }

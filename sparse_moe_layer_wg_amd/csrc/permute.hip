@@ -4,8 +4,9 @@
 // sent to the devices holding their experts by an all-to-all and returned;
 // research-vault claim IX2-0404, section "WideEP", "Evidence": the results
 // come back by a second all-to-all.  On one GPU the first exchange becomes a
-// permute of token rows into per-expert capacity buffers [E,C,d] and the
-// second a gate-weighted gather back to token order.
+// permute of token rows into per-expert capacity buffers [E,C,d] (or, for
+// dropless routing, into compact expert segments [S*k,d]) and the second a
+// gate-weighted gather back to token order.
 //
 // Both kernels are HBM-bound row copies: one wavefront per token, 16-byte
 // vector accesses, rows of 2-14 KB, so every access is fully coalesced
@@ -19,14 +20,14 @@ namespace {
 
 constexpr int kTokPerBlock = 4;  // one token per wave, 4 waves per block
 
-// xd[idx[s,r], slot[s,r], :] = x[s, :] for kept (s,r): each row of x is read
-// once and written to each of its kept destinations.  Pairs outside
-// [0,E) x [0,C) are treated as dropped.
+// xd[idx[s,r]*stride + slot[s,r], :] = x[s, :] for kept (s,r): each row of x
+// is read once and written to each of its kept destinations.  Pairs outside
+// [0,E) x [0,limit) are treated as dropped.
 __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4_t* __restrict__ x,
                                                        const int32_t* __restrict__ topk_idx,
                                                        const int32_t* __restrict__ slot,
                                                        u32x4_t* __restrict__ xd, int S, int nvec,
-                                                       int k, int E, int C) {
+                                                       int k, int E, int stride, int limit) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
     if (s >= S) return;
@@ -38,7 +39,8 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4_t* __restrict
         if (r < k) {
             const int c = slot[(size_t)s * k + r];
             const int e = topk_idx[(size_t)s * k + r];
-            if (c >= 0 && c < C && e >= 0 && e < E) dst[r] = ((int64_t)e * C + c) * nvec;
+            if (c >= 0 && c < limit && e >= 0 && e < E)
+                dst[r] = ((int64_t)e * stride + c) * nvec;
         }
     }
     const u32x4_t* src = x + (size_t)s * nvec;
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4_t* __restrict
     }
 }
 
-// y[s] = sum over kept r of w[s,r] * out[idx[s,r], slot[s,r]] (fp32
+// y[s] = sum over kept r of w[s,r] * out[idx[s,r]*stride + slot[s,r]] (fp32
 // accumulation in rank order), rounded to the activation dtype.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict__ out,
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
                                                       const int32_t* __restrict__ slot,
                                                       const float* __restrict__ topk_w,
                                                       u32x4_t* __restrict__ y, int S, int nvec,
-                                                      int k, int E, int C) {
+                                                      int k, int E, int stride, int limit) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
     if (s >= S) return;
@@ -87,8 +89,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
         if (r < k) {
             const int c = slot[(size_t)s * k + r];
             const int e = topk_idx[(size_t)s * k + r];
-            if (c >= 0 && c < C && e >= 0 && e < E) {
-                src[r] = ((int64_t)e * C + c) * nvec;
+            if (c >= 0 && c < limit && e >= 0 && e < E) {
+                src[r] = ((int64_t)e * stride + c) * nvec;
                 wt[r] = topk_w[(size_t)s * k + r];
             }
         }
@@ -129,26 +131,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4_t* __restrict_
 }  // namespace
 
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, const int32_t* slot,
-                           void* xd, int S, int d, int k, int E, int C, int elem_bytes,
-                           hipStream_t st) {
+                           void* xd, int S, int d, int k, int E, int stride, int limit,
+                           int elem_bytes, hipStream_t st) {
     const int nvec = d * elem_bytes / 16;
     dispatch_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
-        static_cast<const u32x4_t*>(x), topk_idx, slot, static_cast<u32x4_t*>(xd), S, nvec, k, E, C);
+        static_cast<const u32x4_t*>(x), topk_idx, slot, static_cast<u32x4_t*>(xd), S, nvec, k, E,
+        stride, limit);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const void* out, const int32_t* topk_idx, const int32_t* slot,
-                          const float* topk_w, void* y, int S, int d, int k, int E, int C,
-                          bool bf16, hipStream_t st) {
+                          const float* topk_w, void* y, int S, int d, int k, int E, int stride,
+                          int limit, bool bf16, hipStream_t st) {
     const int nvec = d * (bf16 ? 2 : 4) / 16;
     const unsigned grid = (unsigned)ceil_div(S, kTokPerBlock);
+    const auto* o = static_cast<const u32x4_t*>(out);
+    auto* yy = static_cast<u32x4_t*>(y);
     if (bf16)
-        combine_kernel<true><<<grid, 256, 0, st>>>(static_cast<const u32x4_t*>(out), topk_idx, slot,
-                                                   topk_w, static_cast<u32x4_t*>(y), S, nvec, k, E, C);
+        combine_kernel<true><<<grid, 256, 0, st>>>(o, topk_idx, slot, topk_w, yy, S, nvec, k, E,
+                                                   stride, limit);
     else
-        combine_kernel<false><<<grid, 256, 0, st>>>(static_cast<const u32x4_t*>(out), topk_idx,
-                                                    slot, topk_w, static_cast<u32x4_t*>(y), S, nvec,
-                                                    k, E, C);
+        combine_kernel<false><<<grid, 256, 0, st>>>(o, topk_idx, slot, topk_w, yy, S, nvec, k, E,
+                                                    stride, limit);
     return hipGetLastError();
 }
 

@@ -39,6 +39,34 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
     return before + incl - v;
 }
 
+// m-tile prefix mt_start [E+1] of the experts' filled rows occ, then the
+// expert of every m-tile; with seg non-null also seg[e] = sum_{e'<e} occ[e']
+// (compact rows).  All 256 threads of the block call it.
+__device__ void tile_prefix(const int32_t* __restrict__ occ, int E, int bm, int* s_wave,
+                            int32_t* __restrict__ mt_start, int32_t* __restrict__ seg) {
+    const int tid = threadIdx.x;
+    int carry = 0, rcarry = 0;
+    for (int base = 0; base < E; base += 256) {
+        const int e = base + tid;
+        const int o = e < E ? occ[e] : 0;
+        const int v = expert_mtiles(o, bm);
+        int total;
+        const int ex = block_exclusive_scan(v, s_wave, &total);
+        if (e < E) {
+            mt_start[e] = carry + ex;
+            for (int i = 0; i < v; ++i) mt_start[E + 1 + carry + ex + i] = e;
+        }
+        carry += total;
+        if (seg) {
+            int rtotal;
+            const int rex = block_exclusive_scan(o, s_wave, &rtotal);
+            if (e < E) seg[e] = rcarry + rex;
+            rcarry += rtotal;
+        }
+    }
+    if (tid == 0) mt_start[E] = carry;
+}
+
 // One block per expert: hist[e][0..T) becomes the exclusive positions;
 // counts[r,e] and occ[e] follow.  The block also sums the router's per-block
 // probability partials of expert e into psum[e] (fixed assignment of blocks to
@@ -93,7 +121,8 @@ __device__ void finalize_block(const double* __restrict__ psum, const float* __r
                                const int32_t* __restrict__ counts,
                                const int32_t* __restrict__ occ, int S, int E, int nb, int bm,
                                float* __restrict__ losses, int32_t* __restrict__ mt_start,
-                               int32_t* __restrict__ ctr, int n_ctr) {
+                               int32_t* __restrict__ seg, int32_t* __restrict__ ctr,
+                               int n_ctr) {
     __shared__ double s_red[256];
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
@@ -121,27 +150,30 @@ __device__ void finalize_block(const double* __restrict__ psum, const float* __r
         losses[0] = (float)((double)E * aux_sum / (Sd * Sd));
         losses[1] = (float)(s_red[0] / Sd);
     }
-    // m-tile prefix, then the expert of every m-tile
-    int carry = 0;
-    for (int base = 0; base < E; base += 256) {
-        const int e = base + tid;
-        const int v = e < E ? expert_mtiles(occ[e], bm) : 0;
-        int total;
-        const int ex = block_exclusive_scan(v, s_wave, &total);
-        if (e < E) {
-            mt_start[e] = carry + ex;
-            for (int i = 0; i < v; ++i) mt_start[E + 1 + carry + ex + i] = e;
-        }
-        carry += total;
-    }
-    if (tid == 0) mt_start[E] = carry;
+    tile_prefix(occ, E, bm, s_wave, mt_start, seg);
 }
 
 // One block (4 waves) per token block; wave w takes ranks w, w+4, ...
+// Compact rows: the block first scans occ into its own copy of the segment
+// starts (E <= kMaxE), so it needs nothing from the finalize block.
 __device__ void positions_block(int b, const int32_t* __restrict__ topk_idx,
                                 const int32_t* __restrict__ hist_base, int S, int E, int k,
-                                int nb, int C, int nbits, int32_t* __restrict__ slot,
+                                int nb, int C, int nbits, const int32_t* __restrict__ occ,
+                                bool compact, int32_t* __restrict__ slot,
                                 int32_t* __restrict__ inv) {
+    __shared__ int s_seg[kMaxE];
+    __shared__ int s_wave[4];
+    if (compact) {
+        int carry = 0;
+        for (int base = 0; base < E; base += 256) {
+            const int e = base + threadIdx.x;
+            int total;
+            const int ex = block_exclusive_scan(e < E ? occ[e] : 0, s_wave, &total);
+            if (e < E) s_seg[e] = carry + ex;
+            carry += total;
+        }
+        __syncthreads();
+    }
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int s = b * kTokBlock + lane;
     const bool valid = s < S;
@@ -158,42 +190,52 @@ __device__ void positions_block(int b, const int32_t* __restrict__ topk_idx,
         const int before = __popcll(same & lt_mask);
         if (valid) {
             const int pos = hist_base[(size_t)e * T + (size_t)r * nb + b] + before;
-            slot[(size_t)s * k + r] = pos < C ? pos : -1;
-            if (inv && pos < C) inv[(size_t)e * C + pos] = s;
+            const bool kept = pos < C;
+            const int row = compact ? s_seg[e] + pos : e * C + pos;
+            slot[(size_t)s * k + r] = kept ? (compact ? row : pos) : -1;
+            if (inv && kept) inv[row] = s;
         }
     }
 }
 
 // occ[e] = min(sum_r counts[r,e], C), the m-tile prefix and the expert of
-// every m-tile (one block).
+// every m-tile (one block); with seg non-null also the compact segment
+// starts, the segments held within `rows` rows.
 __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restrict__ counts, int E,
                                                         int k, int C, int bm,
                                                         int32_t* __restrict__ occ,
                                                         int32_t* __restrict__ mt_start,
+                                                        int32_t* __restrict__ seg, int rows,
                                                         int32_t* __restrict__ ctr, int n_ctr) {
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
     for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
-    int carry = 0;
-    for (int base = 0; base < E; base += 256) {
-        const int e = base + tid;
-        int o = 0;
-        if (e < E) {
-            long long n = 0;
-            for (int r = 0; r < k; ++r) n += counts[(size_t)r * E + e];
-            o = n < C ? (int)n : C;
-            occ[e] = o;
-        }
-        int total;
-        const int v = e < E ? expert_mtiles(o, bm) : 0;
-        const int ex = block_exclusive_scan(v, s_wave, &total);
-        if (e < E) {
-            mt_start[e] = carry + ex;
-            for (int i = 0; i < v; ++i) mt_start[E + 1 + carry + ex + i] = e;
-        }
-        carry += total;
+    for (int e = tid; e < E; e += 256) {
+        long long n = 0;
+        for (int r = 0; r < k; ++r) n += counts[(size_t)r * E + e];
+        occ[e] = n < 0 ? 0 : n < C ? (int)n : C;
     }
-    if (tid == 0) mt_start[E] = carry;
+    __syncthreads();  // each thread reads other threads' occ below
+    if (seg) {
+        // Compact segments end to end; counts totalling more than `rows` are
+        // invalid, and a segment that would pass row `rows` is cut there.
+        int carry = 0;
+        for (int base = 0; base < E; base += 256) {
+            const int e = base + tid;
+            const int o = e < E ? occ[e] : 0;
+            int total;
+            const int ex = block_exclusive_scan(o, s_wave, &total);
+            if (e < E) {
+                const long long start = (long long)carry + ex;
+                seg[e] = start < rows ? (int)start : rows;
+                const long long room = start < rows ? rows - start : 0;
+                occ[e] = o < room ? o : (int)room;
+            }
+            carry = carry + total < rows ? carry + total : rows;
+        }
+        __syncthreads();
+    }
+    tile_prefix(occ, E, bm, s_wave, mt_start, nullptr);
 }
 
 __global__ void zero_outputs_kernel(int32_t* counts, int n, float* losses) {
@@ -215,34 +257,38 @@ hipError_t launch_slot_scan(int32_t* hist, int E, int k, int nb, int C, int32_t*
 // scan's results, so both run in one launch.
 __global__ __launch_bounds__(256) void positions_finalize_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ hist_base, int S, int E,
-    int k, int nb, int C, int nbits, int32_t* __restrict__ slot, int32_t* __restrict__ inv,
-    const double* __restrict__ psum, const float* __restrict__ zpart,
+    int k, int nb, int C, int nbits, bool compact, int32_t* __restrict__ slot,
+    int32_t* __restrict__ inv, const double* __restrict__ psum, const float* __restrict__ zpart,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ occ, int bm,
-    float* __restrict__ losses, int32_t* __restrict__ mt_start, int32_t* __restrict__ ctr,
-    int n_ctr) {
+    float* __restrict__ losses, int32_t* __restrict__ mt_start, int32_t* __restrict__ seg,
+    int32_t* __restrict__ ctr, int n_ctr) {
     if ((int)blockIdx.x < nb)
-        positions_block(blockIdx.x, topk_idx, hist_base, S, E, k, nb, C, nbits, slot, inv);
+        positions_block(blockIdx.x, topk_idx, hist_base, S, E, k, nb, C, nbits, occ, compact,
+                        slot, inv);
     else
-        finalize_block(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start, ctr, n_ctr);
+        finalize_block(psum, zpart, counts, occ, S, E, nb, bm, losses, mt_start,
+                       compact ? seg : nullptr, ctr, n_ctr);
 }
 
 hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* hist_base, int S,
-                                     int E, int k, int nb, int C, int32_t* slot, int32_t* inv,
-                                     const double* psum, const float* zpart,
+                                     int E, int k, int nb, int C, bool compact, int32_t* slot,
+                                     int32_t* inv, const double* psum, const float* zpart,
                                      const int32_t* counts, const int32_t* occ, int bm,
-                                     float* losses, int32_t* mt_start, int32_t* ctr, int n_ctr,
-                                     hipStream_t st) {
+                                     float* losses, int32_t* mt_start, int32_t* seg,
+                                     int32_t* ctr, int n_ctr, hipStream_t st) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    positions_finalize_kernel<<<nb + 1, 256, 0, st>>>(topk_idx, hist_base, S, E, k, nb, C, nbits,
-                                                      slot, inv, psum, zpart, counts, occ, bm,
-                                                      losses, mt_start, ctr, n_ctr);
+    positions_finalize_kernel<<<nb + 1, 256, 0, st>>>(
+        topk_idx, hist_base, S, E, k, nb, C, nbits, compact, slot, inv, psum, zpart, counts, occ,
+        bm, losses, mt_start, seg, ctr, n_ctr);
     return hipGetLastError();
 }
 
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
-                            int32_t* mt_start, int32_t* ctr, int n_ctr, hipStream_t st) {
-    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, occ, mt_start, ctr, n_ctr);
+                            int32_t* mt_start, int32_t* seg, int rows, int32_t* ctr, int n_ctr,
+                            hipStream_t st) {
+    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, occ, mt_start, seg, rows, ctr,
+                                        n_ctr);
     return hipGetLastError();
 }
 

@@ -16,6 +16,10 @@ class MoELayer:
                  keep: bool = True, device="cuda", dispatch_buffer: bool = True):
         self.cfg = cfg
         self.C = _lib.capacity(cfg)
+        # rows of the dispatch buffer / expert output: [E,C] padded, or S*k
+        # compact expert segments for a dropless config
+        self.rows = _lib.dispatch_rows(cfg)
+        rshape = (cfg.S * cfg.k,) if cfg.dropless else (cfg.E, self.C)
         self.w_gate, self.gate_bias = w_gate, gate_bias
         self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
         dev = torch.device(device)
@@ -33,9 +37,9 @@ class MoELayer:
             self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
             # Without a dispatch buffer the first expert GEMM gathers token
             # rows straight from x (bf16); with one, x is first permuted into it.
-            self.xd = torch.empty((E, self.C, d), dtype=at, device=dev) if dispatch_buffer \
+            self.xd = torch.empty((*rshape, d), dtype=at, device=dev) if dispatch_buffer \
                 else None
-            self.out = torch.empty((E, self.C, d), dtype=at, device=dev)
+            self.out = torch.empty((*rshape, d), dtype=at, device=dev)
         else:
             self.logits = self.topk_idx = self.topk_w = self.slot = None
             self.counts = self.losses = self.xd = self.out = None

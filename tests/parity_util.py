@@ -37,7 +37,8 @@ def as_f64(t) -> np.ndarray:
 
 
 def cfg_of(w: mw.Workload):
-    return moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype)
+    return moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype,
+                      dropless=w.dropless)
 
 
 def run_layer(w: mw.Workload, inputs=None, dispatch_buffer=True):
@@ -54,46 +55,29 @@ def run_layer(w: mw.Workload, inputs=None, dispatch_buffer=True):
 def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, seed: int = 0,
                 report: dict | None = None):
     """Compare one finished layer run with the oracle.  ``full`` runs the
-    oracle over every slot; otherwise rows are sampled."""
+    oracle over every slot; otherwise rows are sampled.  A dropless layer is
+    routed with a capacity of S (never reached) and its slots are the compact
+    rows of the oracle's (expert, rank, token) order."""
     rep = {} if report is None else report
     S, E, k = w.S, w.E, w.k
     C = layer.C
+    if w.dropless:
+        assert C == S
     tol = TOL[w.dtype]
-    host = {n: mw.to_numpy(t) for n, t in inputs.items()}
-
-    lg = layer.logits.cpu().numpy()
-    idx = layer.topk_idx.cpu().numpy()
-    slot = layer.slot.cpu().numpy()
-    tw = layer.topk_w.cpu().numpy()
-    counts = layer.counts.cpu().numpy()
-    losses = layer.losses.cpu().numpy()
 
     # routing from the GPU's own fp32 logits: integer outputs bit-exact
-    r = oracle.route(lg, k, C)
+    r = oracle.route(layer.logits.cpu().numpy(), k, C)
+    idx = layer.topk_idx.cpu().numpy()
+    slot = layer.slot.cpu().numpy()
     assert np.array_equal(idx, r["idx"]), "top-k indices differ from the oracle"
+    if w.dropless:
+        assert (r["slot"] >= 0).all()
+        assert np.array_equal(slot, oracle.compact_rows(r["idx"], E)), \
+            "dropless rows differ from the oracle"
+        return _check_dropless(w, inputs, layer, r, full, n_sample, seed, rep)
     assert np.array_equal(slot, r["slot"]), "slots / drop mask differ from the oracle"
-    assert np.array_equal(counts, r["counts"]), "per-rank counts differ from the oracle"
-    rep["w_rel"] = rel_fro(tw, r["w"])
-    assert rep["w_rel"] <= 1e-5
-    rep["aux"], rep["z"] = float(losses[0]), float(losses[1])
-    assert abs(losses[0] - r["aux"]) <= LOSS_TOL * abs(r["aux"]), (losses[0], r["aux"])
-    assert abs(losses[1] - r["z"]) <= LOSS_TOL * abs(r["z"]), (losses[1], r["z"])
+    host = _check_routing_outputs(w, inputs, layer, r, rep)
     rep["drops"] = int((slot < 0).sum())
-
-    # end to end: the oracle's own logits and routing
-    lg_or = oracle.logits(host["x"], host["wg"], host["bg"])
-    rep["logit_max_abs_err"] = float(np.abs(lg.astype(np.float64) - lg_or).max())
-    # The router re-evaluates in fp64 every top-k decision closer than
-    # tau = 32 * sqrt(d) * 2^-24; that is exact only while the logit error
-    # stays well below tau / 2.
-    tau = 32.0 * np.sqrt(w.d) * 2.0 ** -24
-    rep["logit_err_over_tau"] = rep["logit_max_abs_err"] / tau
-    assert rep["logit_err_over_tau"] < 0.25, rep
-    r_or = oracle.route(lg_or, k, C)
-    agree = np.all(idx == r_or["idx"], axis=1)
-    rep["topk_agreement"] = float(agree.mean())
-    rep["topk_mismatches"] = int((~agree).sum())
-    assert rep["topk_agreement"] >= AGREEMENT, rep
 
     occ = oracle.occupancy(r["counts"], C)
     xd_gpu = layer.xd
@@ -130,6 +114,67 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
             if c >= 0:
                 row = mw.to_numpy(xd_gpu[r["idx"][s, rr], c])
                 assert np.array_equal(row, host["x"][s]), "dispatch row differs"
+    y_or = oracle.token_output(tok, host["x"], host["w1"], host["b1"], host["w2"], host["b2"],
+                               r["idx"], r["slot"], r["w"])
+    rep["y_rel"] = rel_fro(y_gpu[tok], y_or)
+    assert rep["y_rel"] <= tol, rep
+    return rep
+
+
+def _check_routing_outputs(w, inputs, layer, r, rep):
+    """Counts, weights and losses given the GPU's logits, and end-to-end top-k
+    agreement with the oracle's own logits."""
+    host = {n: mw.to_numpy(t) for n, t in inputs.items()}
+    counts = layer.counts.cpu().numpy()
+    losses = layer.losses.cpu().numpy()
+    assert np.array_equal(counts, r["counts"]), "per-rank counts differ from the oracle"
+    rep["w_rel"] = rel_fro(layer.topk_w.cpu().numpy(), r["w"])
+    assert rep["w_rel"] <= 1e-5
+    rep["aux"], rep["z"] = float(losses[0]), float(losses[1])
+    assert abs(losses[0] - r["aux"]) <= LOSS_TOL * abs(r["aux"]), (losses[0], r["aux"])
+    assert abs(losses[1] - r["z"]) <= LOSS_TOL * abs(r["z"]), (losses[1], r["z"])
+    lg = layer.logits.cpu().numpy()
+    lg_or = oracle.logits(host["x"], host["wg"], host["bg"])
+    rep["logit_max_abs_err"] = float(np.abs(lg.astype(np.float64) - lg_or).max())
+    # The router re-evaluates in fp64 every top-k decision closer than
+    # tau = 32 * sqrt(d) * 2^-24; that is exact only while the logit error
+    # stays well below tau / 2.
+    tau = 32.0 * np.sqrt(w.d) * 2.0 ** -24
+    rep["logit_err_over_tau"] = rep["logit_max_abs_err"] / tau
+    assert rep["logit_err_over_tau"] < 0.25, rep
+    r_or = oracle.route(lg_or, w.k, layer.C)
+    agree = np.all(layer.topk_idx.cpu().numpy() == r_or["idx"], axis=1)
+    rep["topk_agreement"] = float(agree.mean())
+    rep["topk_mismatches"] = int((~agree).sum())
+    assert rep["topk_agreement"] >= AGREEMENT, rep
+    return host
+
+
+def _check_dropless(w, inputs, layer, r, full, n_sample, seed, rep):
+    """Dropless run: every assignment kept; compact [S*k,d] buffers."""
+    tol = TOL[w.dtype]
+    host = _check_routing_outputs(w, inputs, layer, r, rep)
+    rep["drops"] = 0
+    rows = oracle.compact_rows(r["idx"], w.E)
+    y_gpu = as_f64(layer.y)
+    if full:
+        res = oracle.layer_dropless(host["x"], host["wg"], host["bg"], host["w1"], host["b1"],
+                                    host["w2"], host["b2"], w.k, lg=layer.logits.cpu().numpy())
+        assert np.array_equal(res["rows"], rows)
+        if layer.xd is not None:
+            assert np.array_equal(mw.to_numpy(layer.xd), res["xd_rows"]), \
+                "compact dispatch buffer is not a bit copy"
+        rep["out_rel"] = rel_fro(as_f64(layer.out), res["out_rows"])
+        assert rep["out_rel"] <= tol, rep
+        rep["y_rel"] = rel_fro(y_gpu, res["y"])
+        assert rep["y_rel"] <= tol, rep
+        return rep
+    rng = np.random.default_rng(seed)
+    tok = np.sort(rng.choice(w.S, size=min(n_sample, w.S), replace=False))
+    if layer.xd is not None:
+        for s in tok[:32]:
+            for rr in range(w.k):
+                assert np.array_equal(mw.to_numpy(layer.xd[rows[s, rr]]), host["x"][s])
     y_or = oracle.token_output(tok, host["x"], host["w1"], host["b1"], host["w2"], host["b2"],
                                r["idx"], r["slot"], r["w"])
     rep["y_rel"] = rel_fro(y_gpu[tok], y_or)

@@ -46,6 +46,25 @@ def test_capacity_formula():
     assert moe.capacity(moe.config(100, 64, 64, 8, 2, 1.0, capacity=7)) == 7
 
 
+def test_dropless_rows_and_workspace():
+    # padded: E*C rows; dropless: S*k compact rows whatever capacity_factor says
+    pad = moe.config(1000, 256, 512, 16, 2, 1.0)
+    assert moe.dispatch_rows(pad) == 16 * 125
+    for cf in (0.0, 1.0, 7.5):
+        free = moe.config(1000, 256, 512, 16, 2, cf, dropless=True)
+        assert free.dropless and moe.dispatch_rows(free) == 2000
+        assert moe.capacity(free) == 1000      # no expert can receive more than S
+    # the dropless workspace is sized by S*k, not by E*S
+    many = moe.config(4096, 256, 512, 256, 2, dropless=True)
+    assert moe.workspace_bytes(many) < 2 * 4096 * 2 * (256 + 512) * 2
+    assert moe.workspace_bytes(many) >= 4096 * 2 * (256 + 512) * 2
+    # the size limit applies to the compact rows: E*S*h would overflow 2^31,
+    # S*k*h does not
+    big = moe.config(65536, 1024, 4096, 256, 2, dropless=True)
+    assert moe.workspace_bytes(big) > 0
+    assert moe.dispatch_rows(big) == 131072
+
+
 def _status(fn, *args):
     return fn(*args)
 
@@ -66,11 +85,13 @@ def test_invalid_configs_rejected_on_host():
     c.act_dtype = 7
     bad.append(c)
     c = moe.config(10, 64, 64, 4, 2)
-    c.reserved = 1
+    c.flags = 2                            # unknown config flag
     bad.append(c)
+    bad.append(moe.config(10, 64, 64, 4, 2, capacity=3, dropless=True))
     for cfg in bad:
         assert lib.moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 1
         assert lib.moe_capacity(ctypes.byref(cfg)) == -1
+        assert lib.moe_dispatch_rows(ctypes.byref(cfg)) == -1
     assert lib.moe_workspace_bytes(None, ctypes.byref(n)) == 1
 
 

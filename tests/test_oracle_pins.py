@@ -155,6 +155,66 @@ def test_unbounded_capacity_equals_dense_topk_sum():
     assert np.allclose(res["y"], want, rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- dropless layout
+def brute_compact_rows(idx):
+    """row[s,r] = #{(s',r'): (idx[s',r'], r', s') < (idx[s,r], r, s)}: an
+    O((S k)^2) count straight from the (expert, rank, token) order."""
+    S, k = idx.shape
+    rows = np.empty((S, k), np.int64)
+    for s in range(S):
+        for r in range(k):
+            key = (idx[s, r], r, s)
+            rows[s, r] = sum((idx[s2, r2], r2, s2) < key for s2 in range(S) for r2 in range(k))
+    return rows
+
+
+@pytest.mark.parametrize("S,E,k,seed", [(1, 1, 1, 0), (9, 3, 2, 1), (17, 5, 3, 2), (30, 4, 4, 3),
+                                        (12, 8, 1, 4)])
+def test_compact_rows_brute_force(S, E, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(S)]).astype(np.int32)
+    rows = oracle.compact_rows(idx, E)
+    assert np.array_equal(rows, brute_compact_rows(idx))
+    assert np.array_equal(np.sort(rows.reshape(-1)), np.arange(S * k))
+
+
+def test_compact_rows_are_segment_start_plus_capacity_slot():
+    """Inside an expert's segment, rows follow the capacity mode's slot order:
+    row = (assignments of lower experts) + slot with a capacity of S."""
+    rng = np.random.default_rng(11)
+    S, E, k = 200, 6, 3
+    lg = (rng.standard_normal((S, E)) + np.array([1.5, 0, 0, -1, 0, 0.5])).astype(np.float32)
+    r = oracle.route(lg, k, S)
+    assert (r["slot"] >= 0).all()
+    n = r["counts"].sum(axis=0)
+    seg = np.concatenate([[0], np.cumsum(n)[:-1]])
+    rows = oracle.compact_rows(r["idx"], E)
+    assert np.array_equal(rows, seg[r["idx"]] + r["slot"])
+
+
+def test_dropless_layer_is_dense_topk_sum_where_capacity_drops():
+    rng = np.random.default_rng(12)
+    S, d, h, E, k = 48, 12, 20, 4, 2
+    x, wg, bg, w1, b1, w2, b2 = rand_layer(rng, S, d, h, E)
+    bg = np.array([2.0, 0.0, -1.0, 0.0], np.float32)   # skew: expert 0 overflows at cf 1
+    capped = oracle.layer(x, wg, bg, w1, b1, w2, b2, k, oracle.capacity(S, E, k, 1.0))
+    assert (capped["slot"] < 0).any()
+    res = oracle.layer_dropless(x, wg, bg, w1, b1, w2, b2, k)
+    want = np.zeros((S, d))
+    for s in range(S):
+        for r in range(k):
+            e = res["idx"][s, r]
+            f = ffn64(x[s:s + 1], w1[e], b1[e], w2[e], b2[e])[0]
+            want[s] += res["w"][s, r] * f
+            assert np.allclose(res["out_rows"][res["rows"][s, r]], f, rtol=1e-12, atol=1e-12)
+            assert np.array_equal(res["xd_rows"][res["rows"][s, r]], x[s])
+    assert np.allclose(res["y"], want, rtol=1e-12, atol=1e-12)
+    # routing and losses do not depend on the capacity
+    assert np.array_equal(res["idx"], capped["idx"])
+    assert np.array_equal(res["counts"], capped["counts"])
+    assert res["aux"] == capped["aux"] and res["z"] == capped["z"]
+
+
 def test_token_output_matches_buffered_path_with_drops():
     rng = np.random.default_rng(2)
     S, d, h, E, k = 64, 16, 24, 4, 2
