@@ -44,7 +44,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     vp = ctypes.c_void_p
@@ -57,8 +57,11 @@ def _load():
     lib.oracle_expert_ffn.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp]
     lib.oracle_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_token_output.argtypes = [i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    f64 = ctypes.c_double
+    lib.oracle_layer_backward.argtypes = [i32] * 6 + [vp, i32, vp, vp, vp, vp, vp, vp, vp, f64, f64] \
+        + [vp] * 9
     for name in ("oracle_logits", "oracle_route", "oracle_dispatch", "oracle_expert_ffn",
-                 "oracle_combine", "oracle_token_output"):
+                 "oracle_combine", "oracle_token_output", "oracle_layer_backward"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -251,3 +254,29 @@ def layer(x, wg, bg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray | None = Non
     y = combine(out, r["idx"], r["slot"], r["w"], S)
     r.update(logits=lg, xd=xd, occ=occ, out=out, y=y)
     return r
+
+
+def layer_backward(x, wg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray, dy: np.ndarray,
+                   g_aux: float = 0.0, g_z: float = 0.0) -> dict:
+    """fp64 gradients of L = sum(dy * y) + g_aux * aux + g_z * z with the
+    routing that the fp32 logits ``lg`` select (capacity C; C = S for
+    dropless routing, which no expert can exceed).  Returns dx [S,d],
+    dwg [E,d], dbg [E], dw1 [E,h,d], db1 [E,h], dw2 [E,d,h], db2 [E,d],
+    dl [S,E] (gradient of the logits) and dw [S,k] (of the top-k weights)."""
+    x, dt = _act(x)
+    S, d = x.shape
+    h = w1.shape[1]
+    lg = np.ascontiguousarray(lg, dtype=np.float32)
+    E = lg.shape[1]
+    w1, b1, w2, b2, dy = _same_dtype(dt, w1, b1, w2, b2, dy)
+    assert w1.shape == (E, h, d) and w2.shape == (E, d, h) and dy.shape == (S, d)
+    wg = np.ascontiguousarray(wg, dtype=np.float32)
+    assert wg.shape == (E, d) and 1 <= k <= E and C >= 1
+    out = dict(dx=np.empty((S, d)), dwg=np.empty((E, d)), dbg=np.empty(E),
+               dw1=np.empty((E, h, d)), db1=np.empty((E, h)), dw2=np.empty((E, d, h)),
+               db2=np.empty((E, d)), dl=np.empty((S, E)), dw=np.empty((S, k)))
+    _load().oracle_layer_backward(
+        S, d, h, E, k, C, _ptr(x), dt, _ptr(wg), _ptr(lg), _ptr(w1), _ptr(b1), _ptr(w2),
+        _ptr(b2), _ptr(dy), float(g_aux), float(g_z),
+        *[_ptr(out[n]) for n in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2", "dl", "dw")])
+    return out

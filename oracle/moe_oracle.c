@@ -323,3 +323,197 @@ void oracle_token_output(int ns, const int64_t *tokens, int d, int h, int k,
         free(hid);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass of the layer (training is the pages' setting: [card] method
+ * paragraph trains with the auxiliary loss and the z-loss; [blog] "Core
+ * Components" and "Performance Analysis" describe training the sparse layer).
+ *
+ * The routing (top-k set, ranks, slots, drops) and f_j are piecewise
+ * constant in the inputs; the gradient is that of the smooth function they
+ * select, for the loss
+ *     L = sum_s dy[s] . y[s] + g_aux * aux + g_z * z.
+ * Per kept assignment (s,r) with e = idx[s,r], row u = pre-activation:
+ *     u = W1_e x_s + b1_e,  a = max(u, 0),  o = W2_e a + b2_e,
+ *     y_s += w[s,r] o.
+ * Chain rule, written out:
+ *     dO = w[s,r] dy_s;              dw[s,r] = dy_s . o  (0 when dropped)
+ *     dW2_e += dO a^T;  db2_e += dO;  da = W2_e^T dO;  du = da * [u > 0]
+ *     dW1_e += du x_s^T; db1_e += du;  dx_s += W1_e^T du.
+ * Router: w[s,.] is the softmax of the k selected logits (the renormalised
+ * probabilities p_j / sum_sel p), so
+ *     dl[s, idx[s,r]] += w[s,r] (dw[s,r] - sum_r' w[s,r'] dw[s,r']);
+ * aux = E sum_j f_j P_j with f_j fixed and P_j = (1/S) sum_s p[s,j], so with
+ * a_j = E f_j / S:  dl[s,j] += g_aux p[s,j] (a_j - sum_j' p[s,j'] a_j');
+ * z = (1/S) sum_s lse_s^2:  dl[s,j] += g_z (2/S) lse_s p[s,j].
+ * Then dWg = sum_s dl_s x_s^T, dbg = sum_s dl_s, dx_s += Wg^T dl_s.
+ * The logits' fp32 rounding is treated as the identity.
+ *
+ * Inputs as in the forward; logits [S,E] fp32 fix the routing; dy [S,d] in
+ * the activation dtype.  Outputs (fp64, all required): dx [S,d], dwg [E,d],
+ * dbg [E], dw1 [E,h,d], db1 [E,h], dw2 [E,d,h], db2 [E,d], dl [S,E],
+ * dw [S,k]. */
+void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
+                           const void *x, int dtype, const float *wg, const float *logits,
+                           const void *w1, const void *b1, const void *w2, const void *b2,
+                           const void *dy, double g_aux, double g_z,
+                           double *dx, double *dwg, double *dbg, double *dw1, double *db1,
+                           double *dw2, double *db2, double *dl, double *dw)
+{
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)k * E);
+    double *w = (double *)malloc(sizeof(double) * ((size_t)S * k + 1));
+    double *lse = (double *)malloc(sizeof(double) * ((size_t)S + 1));
+    double *psum = (double *)malloc(sizeof(double) * (size_t)E);
+    double losses[2];
+    oracle_route(S, E, k, C, logits, idx, w, slot, counts, lse, psum, losses);
+
+    /* per-assignment hidden activations a and pre-activation gradients du */
+    size_t nas = (size_t)S * k;
+    double *a_all = (double *)calloc(nas * (size_t)h + 1, sizeof(double));
+    double *du_all = (double *)calloc(nas * (size_t)h + 1, sizeof(double));
+    memset(dx, 0, sizeof(double) * (size_t)S * d);
+
+    #pragma omp parallel
+    {
+        double *u = (double *)malloc(sizeof(double) * (size_t)h);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        double *da = (double *)malloc(sizeof(double) * (size_t)h);
+        #pragma omp for schedule(dynamic, 1)
+        for (int s = 0; s < S; ++s) {
+            for (int r = 0; r < k; ++r) {
+                size_t q = (size_t)s * k + r;
+                dw[q] = 0.0;
+                if (slot[q] < 0)
+                    continue;
+                int e = idx[q];
+                double *a = a_all + q * h;
+                double *du = du_all + q * h;
+                for (int j = 0; j < h; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += act_at(w1, dtype, ((size_t)e * h + j) * d + i) *
+                               act_at(x, dtype, (size_t)s * d + i);
+                    if (b1)
+                        acc += act_at(b1, dtype, (size_t)e * h + j);
+                    u[j] = acc;
+                    a[j] = acc > 0.0 ? acc : 0.0;
+                }
+                double dwq = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        acc += act_at(w2, dtype, ((size_t)e * d + i) * h + j) * a[j];
+                    if (b2)
+                        acc += act_at(b2, dtype, (size_t)e * d + i);
+                    o[i] = acc;
+                    dwq += act_at(dy, dtype, (size_t)s * d + i) * acc;
+                }
+                dw[q] = dwq;
+                for (int j = 0; j < h; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += act_at(w2, dtype, ((size_t)e * d + i) * h + j) *
+                               (w[q] * act_at(dy, dtype, (size_t)s * d + i));
+                    da[j] = acc;
+                    du[j] = u[j] > 0.0 ? acc : 0.0;
+                }
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        acc += act_at(w1, dtype, ((size_t)e * h + j) * d + i) * du[j];
+                    dx[(size_t)s * d + i] += acc;
+                }
+            }
+        }
+        free(u);
+        free(o);
+        free(da);
+    }
+
+    /* expert weight gradients, one expert per task */
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int e = 0; e < E; ++e) {
+        for (size_t t = 0; t < (size_t)d * h; ++t)
+            dw2[(size_t)e * d * h + t] = 0.0;
+        for (size_t t = 0; t < (size_t)h * d; ++t)
+            dw1[(size_t)e * h * d + t] = 0.0;
+        for (int i = 0; i < d; ++i)
+            db2[(size_t)e * d + i] = 0.0;
+        for (int j = 0; j < h; ++j)
+            db1[(size_t)e * h + j] = 0.0;
+        for (int s = 0; s < S; ++s) {
+            for (int r = 0; r < k; ++r) {
+                size_t q = (size_t)s * k + r;
+                if (slot[q] < 0 || idx[q] != e)
+                    continue;
+                const double *a = a_all + q * h;
+                const double *du = du_all + q * h;
+                for (int i = 0; i < d; ++i) {
+                    double dO = w[q] * act_at(dy, dtype, (size_t)s * d + i);
+                    db2[(size_t)e * d + i] += dO;
+                    for (int j = 0; j < h; ++j)
+                        dw2[((size_t)e * d + i) * h + j] += dO * a[j];
+                }
+                for (int j = 0; j < h; ++j) {
+                    db1[(size_t)e * h + j] += du[j];
+                    for (int i = 0; i < d; ++i)
+                        dw1[((size_t)e * h + j) * d + i] += du[j] * act_at(x, dtype, (size_t)s * d + i);
+                }
+            }
+        }
+    }
+
+    /* router: gradient of the logits, then of Wg, bg and x */
+    #pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        const float *l = logits + (size_t)s * E;
+        double *g = dl + (size_t)s * E;
+        double pa = 0.0;
+        for (int j = 0; j < E; ++j) {
+            double p = exp((double)l[j] - lse[s]);
+            double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
+            pa += p * a_j;
+        }
+        for (int j = 0; j < E; ++j) {
+            double p = exp((double)l[j] - lse[s]);
+            double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
+            g[j] = g_aux * p * (a_j - pa) + g_z * 2.0 / (double)S * lse[s] * p;
+        }
+        double wdw = 0.0;
+        for (int r = 0; r < k; ++r)
+            wdw += w[(size_t)s * k + r] * dw[(size_t)s * k + r];
+        for (int r = 0; r < k; ++r) {
+            size_t q = (size_t)s * k + r;
+            g[idx[q]] += w[q] * (dw[q] - wdw);
+        }
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < E; ++j)
+                acc += g[j] * (double)wg[(size_t)j * d + i];
+            dx[(size_t)s * d + i] += acc;
+        }
+    }
+    #pragma omp parallel for schedule(static)
+    for (int j = 0; j < E; ++j) {
+        double bacc = 0.0;
+        for (int s = 0; s < S; ++s)
+            bacc += dl[(size_t)s * E + j];
+        dbg[j] = bacc;
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int s = 0; s < S; ++s)
+                acc += dl[(size_t)s * E + j] * act_at(x, dtype, (size_t)s * d + i);
+            dwg[(size_t)j * d + i] = acc;
+        }
+    }
+    free(idx);
+    free(slot);
+    free(counts);
+    free(w);
+    free(lse);
+    free(psum);
+    free(a_all);
+    free(du_all);
+}
