@@ -204,6 +204,46 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
                              void *ws, size_t ws_bytes, hipEvent_t *stage_events,
                              hipStream_t stream);
 
+/* ---------------------------------------------------------------- backward
+ * The pages' setting is training: the layer is trained with its auxiliary
+ * loss and z-loss ("GShard: Scaling Giant Models with Conditional Computation
+ * and Automatic Sharding" (inference-research paper card), method
+ * paragraph).  moe_layer_backward returns the gradients of
+ *     L = sum_s dy[s] . y[s] + g_aux * aux + g_z * z
+ * for the routing a forward call chose (top-k set, slots and drops, and the
+ * first-choice fractions f_j, which are piecewise constant, are held fixed):
+ *   per kept assignment (s,r) of expert e at row u, with a = ReLU(W1_e x_s +
+ *   b1_e) and o = out[u]:  dO = w[s,r] dy_s;  dw[s,r] = dy_s . o;
+ *   dW2_e += dO a^T;  db2_e += dO;  du = (W2_e^T dO) * [a > 0];
+ *   dW1_e += du x_s^T;  db1_e += du;  dx_s += W1_e^T du;
+ *   the renormalised top-k weights are the softmax of the k selected logits:
+ *   dl[s, idx_r] += w_r (dw_r - sum_r' w_r' dw_r');
+ *   aux: dl[s,j] += g_aux p_sj (a_j - sum_j' p_sj' a_j'), a_j = E f_j / S;
+ *   z:   dl[s,j] += g_z (2/S) lse_s p_sj;
+ *   dWg = sum_s dl_s x_s^T;  dbg = sum_s dl_s;  dx_s += Wg^T dl_s.
+ * Supported for bf16 activations with S*d*2 < 2^32 bytes (else
+ * MOE_ERR_UNSUPPORTED), in capacity and dropless modes.
+ * In:  x, w_gate, w1, b1 (NULL = 0), w2 as given to the forward; the
+ *      forward's outputs logits, topk_idx, topk_w, slot, counts and out
+ *      (the expert outputs, [E,C,d] or [S*k,d]); dy [S,d] act; the loss
+ *      weights g_aux and g_z (finite).
+ * Out: dx [S,d] act, dw_gate [E,d] fp32, db_gate [E] fp32 (NULL = not
+ *      wanted), dw1 [E,h,d] act, db1 [E,h] act (NULL = not wanted),
+ *      dw2 [E,d,h] act, db2 [E,d] act (NULL = not wanted).
+ * Precision: fp32 accumulation everywhere; the hidden activations are
+ * recomputed (bf16, as in the forward), dO, du and the expert-side input
+ * gradient are rounded to bf16 once; the router side is fp32.
+ * ws: at least moe_backward_workspace_bytes() bytes, 256-byte aligned. */
+moe_status moe_backward_workspace_bytes(const moe_config *cfg, size_t *bytes);
+moe_status moe_layer_backward(const moe_config *cfg, const void *x, const float *w_gate,
+                              const void *w1, const void *b1, const void *w2,
+                              const float *logits, const int32_t *topk_idx,
+                              const float *topk_w, const int32_t *slot,
+                              const int32_t *counts, const void *out, const void *dy,
+                              float g_aux, float g_z, void *dx, float *dw_gate,
+                              float *db_gate, void *dw1, void *db1, void *dw2, void *db2,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

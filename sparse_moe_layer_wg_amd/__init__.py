@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MOE_NUM_STAGE_EVENTS,
     MoeConfig,
     MoeError,
+    backward_workspace_bytes,
     capacity,
     combine,
     config,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     dispatch_rows,
     expert_ffn,
     gate,
+    layer_backward,
     layer_forward,
     library,
     library_path,

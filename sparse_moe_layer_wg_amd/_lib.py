@@ -90,8 +90,13 @@ def library():
     lib.moe_expert_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     lib.moe_layer_forward.argtypes = [cfgp] + [vp] * 17 + [ctypes.c_size_t, vp, vp]
+    lib.moe_backward_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    f32 = ctypes.c_float
+    lib.moe_layer_backward.argtypes = [cfgp] + [vp] * 12 + [f32, f32] + [vp] * 8 + \
+        [ctypes.c_size_t, vp]
     for f in ("moe_workspace_bytes", "moe_gate", "moe_dispatch", "moe_expert_ffn",
-              "moe_combine", "moe_layer_forward"):
+              "moe_combine", "moe_layer_forward", "moe_backward_workspace_bytes",
+              "moe_layer_backward"):
         getattr(lib, f).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -245,3 +250,34 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
         _arg(out, "out", at, R * d, required=False),
         wsp, wsb, ev, _stream(stream))
     _check(st, "moe_layer_forward")
+
+
+def backward_workspace_bytes(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().moe_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_backward_workspace_bytes")
+    return int(n.value)
+
+
+def layer_backward(cfg, x, w_gate, w1, b1, w2, logits, topk_idx, topk_w, slot, counts, out, dy,
+                   dx, dw_gate, dw1, dw2, ws, db_gate=None, db1=None, db2=None, g_aux=0.0,
+                   g_z=0.0, stream=None):
+    """Gradients of sum(dy*y) + g_aux*aux + g_z*z (``moe_layer_backward``)."""
+    R = dispatch_rows(cfg)
+    S, d, h, E, k = cfg.S, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
+    at = cfg.torch_dtype
+    wsp, wsb = _ws(ws)
+    st = library().moe_layer_backward(
+        ctypes.byref(cfg), _arg(x, "x", at, S * d), _arg(w_gate, "w_gate", torch.float32, E * d),
+        _arg(w1, "w1", at, E * h * d), _arg(b1, "b1", at, E * h, required=False),
+        _arg(w2, "w2", at, E * d * h), _arg(logits, "logits", torch.float32, S * E),
+        _arg(topk_idx, "topk_idx", torch.int32, S * k),
+        _arg(topk_w, "topk_w", torch.float32, S * k), _arg(slot, "slot", torch.int32, S * k),
+        _arg(counts, "counts", torch.int32, k * E), _arg(out, "out", at, R * d),
+        _arg(dy, "dy", at, S * d), float(g_aux), float(g_z), _arg(dx, "dx", at, S * d),
+        _arg(dw_gate, "dw_gate", torch.float32, E * d),
+        _arg(db_gate, "db_gate", torch.float32, E, required=False),
+        _arg(dw1, "dw1", at, E * h * d), _arg(db1, "db1", at, E * h, required=False),
+        _arg(dw2, "dw2", at, E * d * h), _arg(db2, "db2", at, E * d, required=False),
+        wsp, wsb, _stream(stream))
+    _check(st, "moe_layer_backward")

@@ -1,0 +1,342 @@
+// Backward pass of the layer: everything except the expert GEMMs.
+//
+// Method: the layer is trained with its auxiliary loss and z-loss ("GShard:
+// Scaling Giant Models with Conditional Computation and Automatic Sharding"
+// (paper card), method paragraph).  The routing (top-k set, slots, drops)
+// and the first-choice fractions f_j are piecewise constant; the gradient is
+// that of L = sum dy.y + g_aux * aux + g_z * z with them held fixed:
+//   combine:  dO[u] = w[s,r] dy[s],  dw[s,r] = dy[s] . O[u]   (u = row of (s,r))
+//   router:   the renormalised top-k weights are the softmax of the k
+//             selected logits, so dl[s, idx_r] += w_r (dw_r - sum_r' w_r' dw_r');
+//             aux = E sum_j f_j P_j adds g_aux p_j (a_j - sum_j' p_j' a_j') with
+//             a_j = E f_j / S;  z = mean lse^2 adds g_z (2/S) lse p_j;
+//   gate:     dWg = dl^T x,  dbg = colsum dl,  dx += dl Wg;
+//   dispatch: dx[s] += sum over kept r of dX[u(s,r)].
+// Kernels here are HBM- or latency-bound; one wave per token where a token's
+// rows are touched, fp32 arithmetic, fixed reduction orders (deterministic).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTokPerBlock = 4;  // one token per wave
+
+__global__ void inverse_rows_kernel(const int32_t* __restrict__ topk_idx,
+                                    const int32_t* __restrict__ slot, int S, int k, int E,
+                                    int stride, int limit, int32_t* __restrict__ inv) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)S * k) return;
+    const int c = slot[i], e = topk_idx[i];
+    if (c >= 0 && c < limit && e >= 0 && e < E) inv[(int64_t)e * stride + c] = (int32_t)(i / k);
+}
+
+// Row u of assignment (s,r) in the expert buffers, or -1 when dropped.
+__device__ __forceinline__ int64_t assignment_row(const int32_t* __restrict__ topk_idx,
+                                                  const int32_t* __restrict__ slot, int64_t q,
+                                                  int E, int stride, int limit) {
+    const int c = slot[q], e = topk_idx[q];
+    return (c >= 0 && c < limit && e >= 0 && e < E) ? (int64_t)e * stride + c : -1;
+}
+
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const u32x4_t* __restrict__ dy, const u32x4_t* __restrict__ out,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot,
+    const float* __restrict__ topk_w, u32x4_t* __restrict__ dO, float* __restrict__ dw, int S,
+    int nvec, int k, int E, int stride, int limit) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
+    if (s >= S) return;
+    for (int r = 0; r < k; ++r) {
+        const int64_t q = (int64_t)s * k + r;
+        const int64_t u = assignment_row(topk_idx, slot, q, E, stride, limit);
+        float dot = 0.f;
+        if (u >= 0) {
+            const float w = topk_w[q];
+            const u32x4_t* o = out + u * nvec;
+            u32x4_t* g = dO + u * nvec;
+            const u32x4_t* y = dy + (int64_t)s * nvec;
+            for (int i = lane; i < nvec; i += kWave) {
+                const u32x4_t yv = y[i], ov = o[i];
+                u32x4_t gv;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float y0 = __uint_as_float(yv[c] << 16);
+                    const float y1 = __uint_as_float(yv[c] & 0xffff0000u);
+                    dot = fmaf(y0, __uint_as_float(ov[c] << 16), dot);
+                    dot = fmaf(y1, __uint_as_float(ov[c] & 0xffff0000u), dot);
+                    gv[c] = pack_bf16x2(w * y0, w * y1);
+                }
+                g[i] = gv;
+            }
+            dot = wave_sum_f32(dot);
+        }
+        if (lane == 0) dw[q] = dot;
+    }
+}
+
+// One wave per token; lanes stride over the E logits.
+__global__ __launch_bounds__(256) void router_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const float* __restrict__ dw,
+    const int32_t* __restrict__ counts, float g_aux, float g_z, float* __restrict__ dl, int S,
+    int E, int k) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
+    if (s >= S) return;
+    const float* l = logits + (int64_t)s * E;
+    float m = -INFINITY;
+    for (int j = lane; j < E; j += kWave) m = fmaxf(m, l[j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    float se = 0.f;
+    for (int j = lane; j < E; j += kWave) se += expf(l[j] - m);
+    se = wave_sum_f32(se);
+    const float lse = m + logf(se);
+    // a_j = E f_j / S with f_j = counts[0,j] / S
+    const float a_scale = (float)E / ((float)S * (float)S);
+    float pa = 0.f;
+    for (int j = lane; j < E; j += kWave) pa += expf(l[j] - lse) * (a_scale * (float)counts[j]);
+    pa = wave_sum_f32(pa);
+    const float zc = g_z * 2.f / (float)S * lse;
+    float* g = dl + (int64_t)s * E;
+    for (int j = lane; j < E; j += kWave) {
+        const float p = expf(l[j] - lse);
+        g[j] = g_aux * p * (a_scale * (float)counts[j] - pa) + zc * p;
+    }
+    // selected experts: w_r (dw_r - sum_r' w_r' dw_r'), added after the dense
+    // terms by the lane that wrote them (same lane: j % 64)
+    float wdw = 0.f;
+    for (int r = 0; r < k; ++r) wdw += topk_w[(int64_t)s * k + r] * dw[(int64_t)s * k + r];
+    for (int r = 0; r < k; ++r) {
+        const int j = topk_idx[(int64_t)s * k + r];
+        if ((j & (kWave - 1)) == lane)
+            g[j] += topk_w[(int64_t)s * k + r] * (dw[(int64_t)s * k + r] - wdw);
+    }
+}
+
+// out[e, n] = sum of v over expert e's rows; block = (expert, 512 columns),
+// 4 waves split the rows, partial sums combined in a fixed order.
+__global__ __launch_bounds__(256) void segment_colsum_kernel(const bf16_t* __restrict__ v,
+                                                             const int32_t* __restrict__ occ,
+                                                             const int32_t* __restrict__ row0,
+                                                             int C, int N,
+                                                             bf16_t* __restrict__ out) {
+    __shared__ float part[4][512];
+    const int e = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int n = blockIdx.x * 512 + lane * 8;
+    const int M = occ[e];
+    const int64_t base = row0 ? (int64_t)row0[e] : (int64_t)e * C;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+    if (n < N) {
+        for (int m = wave; m < M; m += 4) {
+            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(v + (base + m) * N + n);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[2 * c] += __uint_as_float(x[c] << 16);
+                acc[2 * c + 1] += __uint_as_float(x[c] & 0xffff0000u);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) part[wave][lane * 8 + c] = acc[c];
+    __syncthreads();
+    const int i = threadIdx.x * 2;  // 256 threads x 2 columns
+    if (blockIdx.x * 512 + i < N) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            s0 += part[w][i];
+            s1 += part[w][i + 1];
+        }
+        *reinterpret_cast<uint32_t*>(out + (int64_t)e * N + blockIdx.x * 512 + i) =
+            pack_bf16x2(s0, s1);
+    }
+}
+
+// fp32 GEMM for the router side, 64x64 tiles, 4x4 results per thread, k-steps
+// of 16 staged in LDS as [k][row].
+//   DX:  C[s, i] = sum_j dl[s, j] wg[j, i]  (+ the token's dX rows, bf16 out)
+//   DW:  C[j, i] = sum_s dl[s, j] x[s, i]   (fp32 out)
+constexpr int RT = 64, RK = 16;
+template <bool DX>
+__global__ __launch_bounds__(256) void router_gemm_kernel(
+    const float* __restrict__ dl, const void* __restrict__ Bsrc, const bf16_t* __restrict__ dX,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot,
+    void* __restrict__ Cout, int S, int d, int E, int k, int stride, int limit) {
+    __shared__ float As[RK][RT + 4];
+    __shared__ float Bs[RK][RT + 4];
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    const int m0 = blockIdx.y * RT, n0 = blockIdx.x * RT;
+    const int M = DX ? S : E, K = DX ? E : S;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += RK) {
+        // A(m, kk): DX: dl[m, kk] (m = token); DW: dl[kk, m] (kk = token)
+        // B(n, kk): DX: wg[kk, n];             DW: x[kk, n] (bf16)
+        // thread loads 4 A and 4 B elements: (kk = tid / 16, col = (tid % 16) * 4 + c)
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float av = 0.f, bv = 0.f;
+            if (DX) {
+                // A is K-contiguous: kk varies fastest across threads
+                const int mm = tid / 4 + 0, kk = (tid % 4) * 4 + c;
+                if (m0 + mm < M && k0 + kk < K) av = dl[(int64_t)(m0 + mm) * E + k0 + kk];
+                As[kk][mm] = av;
+            } else {
+                const int kk = tid / 16, mm = (tid % 16) * 4 + c;
+                if (m0 + mm < M && k0 + kk < K) av = dl[(int64_t)(k0 + kk) * E + m0 + mm];
+                As[kk][mm] = av;
+            }
+            const int kk = tid / 16, nn = (tid % 16) * 4 + c;
+            if (n0 + nn < d && k0 + kk < K) {
+                if (DX)
+                    bv = static_cast<const float*>(Bsrc)[(int64_t)(k0 + kk) * d + n0 + nn];
+                else
+                    bv = bf16_to_f32(static_cast<const bf16_t*>(Bsrc)[(int64_t)(k0 + kk) * d + n0 + nn]);
+            }
+            Bs[kk][nn] = bv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < RK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty + 16 * i;
+        if (m >= M) continue;
+        if (DX) {
+            // the token's expert-side input gradient rows, in rank order
+            int64_t u[kMaxK];
+#pragma unroll
+            for (int r = 0; r < kMaxK; ++r)
+                u[r] = r < k ? assignment_row(topk_idx, slot, (int64_t)m * k + r, E, stride, limit)
+                             : -1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + tx + 16 * j;
+                if (n >= d) continue;
+                float v = acc[i][j];
+#pragma unroll
+                for (int r = 0; r < kMaxK; ++r)
+                    if (u[r] >= 0) v += bf16_to_f32(dX[u[r] * d + n]);
+                static_cast<bf16_t*>(Cout)[(int64_t)m * d + n] = f32_to_bf16(v);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + tx + 16 * j;
+                if (n < d) static_cast<float*>(Cout)[(int64_t)m * d + n] = acc[i][j];
+            }
+        }
+    }
+}
+
+// dbg[j] = sum_s dl[s, j]: one thread per expert, tokens in order.
+__global__ void logit_colsum_kernel(const float* __restrict__ dl, int S, int E,
+                                    float* __restrict__ dbg) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= E) return;
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += dl[(int64_t)s * E + j];
+    dbg[j] = acc;
+}
+
+// n bytes, n even (every array here holds 2- or 4-byte elements).
+__global__ void zero_bytes_kernel(uint32_t* __restrict__ p, size_t n) {
+    const size_t words = n / 4;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+    if ((n & 2) && blockIdx.x == 0 && threadIdx.x == 0)
+        reinterpret_cast<uint16_t*>(p)[2 * words] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_inverse_rows(const int32_t* topk_idx, const int32_t* slot, int S, int k,
+                               int E, int stride, int limit, int32_t* inv, hipStream_t st) {
+    const int64_t n = (int64_t)S * k;
+    if (n == 0) return hipSuccess;
+    inverse_rows_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(topk_idx, slot, S, k, E,
+                                                                    stride, limit, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dy, const void* out, const int32_t* topk_idx,
+                              const int32_t* slot, const float* topk_w, void* dO, float* dw,
+                              int S, int d, int k, int E, int stride, int limit,
+                              hipStream_t st) {
+    if (S == 0) return hipSuccess;
+    combine_bwd_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
+        static_cast<const u32x4_t*>(dy), static_cast<const u32x4_t*>(out), topk_idx, slot,
+        topk_w, static_cast<u32x4_t*>(dO), dw, S, d / 8, k, E, stride, limit);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
+                             const float* dw, const int32_t* counts, float g_aux, float g_z,
+                             float* dl, int S, int E, int k, hipStream_t st) {
+    if (S == 0) return hipSuccess;
+    router_bwd_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
+        logits, topk_idx, topk_w, dw, counts, g_aux, g_z, dl, S, E, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_colsum(const void* v, const int32_t* occ, const int32_t* row0, int E,
+                                 int C, int N, void* out, hipStream_t st) {
+    if (E == 0 || N == 0) return hipSuccess;
+    dim3 grid((unsigned)ceil_div(N, 512), (unsigned)E);
+    segment_colsum_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(v), occ, row0, C, N,
+                                                static_cast<bf16_t*>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
+                            const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
+                            int E, int k, int stride, int limit, hipStream_t st) {
+    if (S == 0) return hipSuccess;
+    dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(S, RT));
+    router_gemm_kernel<true><<<grid, 256, 0, st>>>(dl, wg, static_cast<const bf16_t*>(dX),
+                                                   topk_idx, slot, dx, S, d, E, k, stride, limit);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,
+                            int E, hipStream_t st) {
+    dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(E, RT));
+    router_gemm_kernel<false><<<grid, 256, 0, st>>>(dl, x, nullptr, nullptr, nullptr, dwg, S, d,
+                                                    E, 1, 0, 0);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (dbg) {
+        logit_colsum_kernel<<<(unsigned)ceil_div(E, 256), 256, 0, st>>>(dl, S, E, dbg);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st) {
+    if (!p || n == 0) return hipSuccess;
+    const size_t words = n / 4;
+    const unsigned grid = (unsigned)(words / 256 + 1 < 4096 ? words / 256 + 1 : 4096);
+    zero_bytes_kernel<<<grid, 256, 0, st>>>(static_cast<uint32_t*>(p), n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

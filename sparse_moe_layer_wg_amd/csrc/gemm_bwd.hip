@@ -1,0 +1,281 @@
+// Expert GEMMs of the backward pass: data gradients (dgrad) and weight
+// gradients (wgrad) over the same variable-occupancy expert rows as the
+// forward.
+//
+// Method: the layer's expert networks are feed-forward networks ("GShard:
+// Scaling Giant Neural Networks with Conditional Computation" (blog), section
+// "Core Components", "Expert Networks"), trained with the layer ("GShard:
+// Scaling Giant Models with Conditional Computation and Automatic Sharding"
+// (paper card), method paragraph).  With O = ReLU(X W1^T + b1) W2^T + b2 per
+// expert, the chain rule gives, per expert e over its filled rows:
+//   dgrad 2:  dU = (dO . W2_e) * [H > 0]      [rows,d] x [d,h]   (K = d)
+//   dgrad 1:  dX = dU . W1_e                  [rows,h] x [h,d]   (K = h)
+//   wgrad 2:  dW2_e = dO^T . H                [d,rows] x [rows,h] (K = rows)
+//   wgrad 1:  dW1_e = dU^T . X                [h,rows] x [rows,d] (K = rows)
+// In the forward both MFMA operands are stored with K contiguous.  Here the
+// weights of a dgrad and both operands of a wgrad are stored with K as the
+// slow index ("K-major": W2_e is [d,h] and dgrad 2 contracts over d).  Such an
+// operand is loaded as 8 K-rows x 4 columns per thread (8-byte loads, a
+// wave covering 256 contiguous columns of each K-row), transposed in
+// registers and written to LDS as K-contiguous rows, the layout the MFMA
+// fragments read.  The rest follows the forward kernel: 256x256x64 tiles,
+// 8 waves of 128x64, v_mfma_f32_32x32x16_bf16 with fp32 accumulation, two LDS
+// stages, the epilogue staged through LDS into 16-byte row stores, and a
+// persistent grid that takes tiles from per-XCD atomic counters.
+//   dgrad tiles follow the forward's m-tile list (ragged rows, weights fixed);
+//   rows past an expert's occupancy load a clamped valid row and are never
+//   stored.  dgrad 2 applies the ReLU mask in its row stores (reading H at
+//   the same place; dU may overwrite H in place).
+//   wgrad tiles cover each expert's full [M,N] weight gradient; the
+//   contraction runs over the expert's filled rows (K = occ[e], any length,
+//   zero included: the tile then stores zeros); rows past the occupancy
+//   load as zero.  X rows may be gathered from the token rows through the
+//   inverse slot map.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NTH = 512;                     // 8 waves: 2 (m) x 4 (n)
+constexpr int WM = 128, WNT = 64;            // wave tile
+constexpr int TM = WM / 32, TN = WNT / 32;   // 32x32 MFMA blocks per wave
+constexpr int RS = BK * 2 + 16;              // LDS row stride (bytes, padded)
+constexpr int BOFF = BM * RS;                // B rows after the A rows
+constexpr int STAGE = (BM + BN) * RS;
+constexpr int EPS = WNT * 2 + 8;             // epilogue staging row (bytes)
+static_assert(NTH / 64 * WM * EPS <= 2 * STAGE, "epilogue staging fits LDS");
+
+// 8 K-rows x 4 bf16 columns -> 4 columns x 8 K values (one 16-byte LDS row
+// chunk each).
+__device__ __forceinline__ void transpose8x4(const uint2 (&v)[8], u32x4_t (&o)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint2 a = v[2 * q], b = v[2 * q + 1];
+        o[0][q] = (a.x & 0xffffu) | (b.x << 16);
+        o[1][q] = (a.x >> 16) | (b.x & 0xffff0000u);
+        o[2][q] = (a.y & 0xffffu) | (b.y << 16);
+        o[3][q] = (a.y >> 16) | (b.y & 0xffff0000u);
+    }
+}
+
+template <bool WGRAD, bool MASK>
+__global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ int s_next;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / 4, wn = wave % 4;
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const int N = p.N;
+    const int NT = (N + BN - 1) / BN;
+    const int MT = WGRAD ? (p.M + BM - 1) / BM : 0;
+    const int T = WGRAD ? p.E * MT * NT : p.mt_start[p.E] * NT;
+    const int per = (T + 7) >> 3;
+    const int xcd = blockIdx.x & 7;
+    const int t_end = min(T, (xcd + 1) * per);
+
+    const int fa_off = (wm * WM + frow) * RS + fhalf * 16;
+    const int fb_off = BOFF + (wn * WNT + frow) * RS + fhalf * 16;
+    // K-contiguous loader (dgrad A): row tid/8 + 64*i, 16-byte chunk tid%8
+    const int r_off = (tid >> 3) * RS + (tid & 7) * 16;
+    // K-major loader: K-rows 8*wave .. 8*wave+7, columns 4*lane .. 4*lane+3
+    const int t_off = (4 * lane) * RS + wave * 16;
+
+    if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
+    for (;;) {
+        __syncthreads();
+        const int t = __builtin_amdgcn_readfirstlane(s_next);
+        if (t >= t_end) break;
+        int e, m0, n0, M, KT, Keff;
+        if constexpr (WGRAD) {
+            e = t / (MT * NT);
+            const int r = t - e * MT * NT;
+            m0 = (r / NT) * BM;
+            n0 = (r % NT) * BN;
+            M = p.M;
+            Keff = __builtin_amdgcn_readfirstlane(p.occ[e]);
+            KT = (Keff + BK - 1) / BK;
+        } else {
+            const int q = t / NT;
+            e = __builtin_amdgcn_readfirstlane(p.mt_expert[q]);
+            const int mt0 = __builtin_amdgcn_readfirstlane(p.mt_start[e]);
+            m0 = (q - mt0) * BM;
+            n0 = (t - q * NT) * BN;
+            M = __builtin_amdgcn_readfirstlane(p.occ[e]);
+            Keff = p.K;
+            KT = p.K / BK;
+        }
+        const size_t row_e = p.row0 ? (size_t)__builtin_amdgcn_readfirstlane(p.row0[e])
+                                    : (size_t)e * p.C;
+        const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
+        const bf16_t* __restrict__ B = static_cast<const bf16_t*>(p.B);
+
+        // ---------------------------------------------------------- loads
+        u32x4_t ra[4];       // dgrad A: 4 K-contiguous 16-byte chunks
+        uint2 va[8], vb[8];  // K-major operands: 8 K-rows x 4 columns
+        // column offsets of this lane's K-major pieces (clamped into range;
+        // clamped columns are never stored)
+        const int ca = WGRAD ? min(m0 + 4 * lane, M - 4) : 0;
+        const int cb = min(n0 + 4 * lane, N - 4);
+        auto gload = [&](int kt) {
+            const int kb = kt * BK;
+            if constexpr (WGRAD) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int k = kb + 8 * wave + r;
+                    va[r] = make_uint2(0u, 0u);
+                    vb[r] = make_uint2(0u, 0u);
+                    if (k < Keff) {
+                        const size_t ar = row_e + k;
+                        const size_t br = p.b_rows ? (size_t)p.b_rows[ar] : ar;
+                        va[r] = *reinterpret_cast<const uint2*>(A + ar * M + ca);
+                        vb[r] = *reinterpret_cast<const uint2*>(B + br * N + cb);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rg = min(m0 + (tid >> 3) + 64 * i, M - 1);
+                    ra[i] = *reinterpret_cast<const u32x4_t*>(A + (row_e + rg) * p.K + kb +
+                                                              (tid & 7) * 8);
+                }
+                const bf16_t* W = B + (size_t)e * p.K * N;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    vb[r] = *reinterpret_cast<const uint2*>(W + (size_t)(kb + 8 * wave + r) * N + cb);
+            }
+        };
+        auto sstore = [&](int buf) {
+            char* st = smem + buf * STAGE;
+            u32x4_t o[4];
+            if constexpr (WGRAD) {
+                transpose8x4(va, o);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(st + t_off + c * RS) = o[c];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4_t*>(st + r_off + i * 64 * RS) = ra[i];
+            }
+            transpose8x4(vb, o);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                *reinterpret_cast<u32x4_t*>(st + BOFF + t_off + c * RS) = o[c];
+        };
+
+        // ---------------------------------------------------------- k-loop
+        f32x16_t acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        if (KT > 0) {
+            gload(0);
+            sstore(0);
+            __syncthreads();
+        }
+        for (int kt = 0; kt < KT; ++kt) {
+            const bool more = kt + 1 < KT;
+            if (more) gload(kt + 1);
+            const char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    fa[i] = *reinterpret_cast<const bf16x8_t*>(st + fa_off + i * 32 * RS + ks * 32);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    fb[j] = *reinterpret_cast<const bf16x8_t*>(st + fb_off + j * 32 * RS + ks * 32);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+            }
+            if (more) sstore((kt + 1) & 1);
+            __syncthreads();
+        }
+
+        int nx = 0;
+        if (tid == 0) nx = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
+        // ---------------------------------------------------------- epilogue
+        // Accumulator block (n x m): lane l holds row m = l%32, register r
+        // column n = 8*(r/4) + 4*(l/32) + r%4.  Rounded to bf16, staged per
+        // wave in LDS, stored as 16-byte row chunks.
+        char* ep = smem + wave * (WM * EPS);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = j * 32 + 8 * q + 4 * fhalf;
+                    const f32x16_t& a = acc[i][j];
+                    *reinterpret_cast<uint2*>(ep + (i * 32 + frow) * EPS + nl * 2) =
+                        make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]),
+                                   pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+                }
+        if (tid == 0) s_next = nx;
+        __builtin_amdgcn_wave_barrier();
+        constexpr int CPR = WNT * 2 / 16;   // 16-byte chunks per staged row
+        constexpr int NIT = WM * CPR / 64;  // chunks per lane
+        const int nw = n0 + wn * WNT;
+        bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) +
+                                    (WGRAD ? (size_t)e * p.M * N : row_e * N);
+        const bf16_t* __restrict__ mk = MASK ? static_cast<const bf16_t*>(p.mask) + row_e * N
+                                             : nullptr;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+            const int m = m0 + wm * WM + row, n = nw + ch * 8;
+            u32x4_t ov = *reinterpret_cast<const u32x4_t*>(ep + row * EPS + ch * 16);
+            if (m < M && n < N) {
+                if constexpr (MASK) {
+                    // dReLU: keep the gradient where the forward's hidden
+                    // value is positive (bf16 > 0: sign clear, not zero)
+                    const u32x4_t hv =
+                        *reinterpret_cast<const u32x4_t*>(mk + (size_t)m * N + n);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t hlo = hv[c] & 0xffffu, hhi = hv[c] >> 16;
+                        const uint32_t keep = ((hlo != 0u && hlo < 0x8000u) ? 0xffffu : 0u) |
+                                              ((hhi != 0u && hhi < 0x8000u) ? 0xffff0000u : 0u);
+                        ov[c] &= keep;
+                    }
+                }
+                *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = ov;
+            }
+        }
+    }  // tile loop
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, bool wgrad, bool mask, hipStream_t st) {
+    if (p.E == 0 || p.N == 0) return hipSuccess;
+    long long tiles;
+    if (wgrad) {
+        if (p.M == 0) return hipSuccess;
+        tiles = (long long)p.E * ceil_div(p.M, BM) * ceil_div(p.N, BN);
+    } else {
+        if (p.C == 0 && !p.row0) return hipSuccess;
+        tiles = (long long)mtile_table_len(p.E, p.C, p.rows) * ceil_div(p.N, BN);
+    }
+    const long long slots = (long long)(device_cus() / 8) * 8;
+    const unsigned grid = (unsigned)(tiles < slots ? ceil_div(tiles, 8) * 8 : slots);
+    if (grid == 0) return hipSuccess;
+    if (wgrad)
+        gemm_bwd_kernel<true, false><<<grid, NTH, 0, st>>>(p);
+    else if (mask)
+        gemm_bwd_kernel<false, true><<<grid, NTH, 0, st>>>(p);
+    else
+        gemm_bwd_kernel<false, false><<<grid, NTH, 0, st>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -54,13 +54,14 @@ hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* his
                                      const int32_t* counts, const int32_t* occ, int bm,
                                      float* losses, int32_t* mt_start, int32_t* seg,
                                      int32_t* ctr, int n_ctr, hipStream_t st);
-// Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN);
-// zeroes the n_ctr GEMM tile counters; with seg non-null also the exclusive
-// prefix of occ over experts (compact rows), every segment cut to end by row
-// `rows` (the compact buffers' length).
-hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
-                            int32_t* mt_start, int32_t* seg, int rows, int32_t* ctr, int n_ctr,
-                            hipStream_t st);
+// Occupancy (and m-tile prefix) straight from counts [k,E] (standalone FFN,
+// backward); zeroes the n_ctr GEMM tile counters; with seg non-null also the
+// exclusive prefix of occ over experts (compact rows), every segment cut to
+// end by row `rows` (the compact buffers' length).  m-tiles are bm rows high
+// and an expert's last one may take `extra` more rows (expert_mtiles).
+hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int extra,
+                            int32_t* occ, int32_t* mt_start, int32_t* seg, int rows,
+                            int32_t* ctr, int n_ctr, hipStream_t st);
 // Zero losses and counts (empty input).
 hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st);
 
@@ -98,16 +99,17 @@ struct GemmParams {
     int E, C, N, K;
     bool relu;
 };
-// m-tiles of an expert with occ filled rows.  Tiles are bm rows high, but
-// with bm = 256 an expert's last m-tile may reach kStripRows further: the
-// GEMM then runs those rows as an extra strip against the weight fragments
-// it already holds instead of as a nearly empty m-tile of their own.
+// m-tiles of an expert with occ filled rows.  Tiles are bm rows high, and an
+// expert's last m-tile may reach `extra` rows further.  The forward GEMM uses
+// extra = kStripRows with bm = 256 (strip_rows): it runs those rows as an
+// extra strip against the weight fragments it already holds instead of as a
+// nearly empty m-tile of their own.  The backward GEMMs use extra = 0.
 constexpr int kStripRows = 32;
-__host__ __device__ inline int expert_mtiles(int occ, int bm) {
+__host__ __device__ inline int expert_mtiles(int occ, int bm, int extra) {
     if (occ <= 0) return 0;
-    const int extra = bm == 256 ? kStripRows : 0;
     return occ <= bm + extra ? 1 : (occ - extra + bm - 1) / bm;
 }
+inline int strip_rows(int bm) { return bm == 256 ? kStripRows : 0; }
 // The m-tile prefix mt_start [E+1] is followed in memory by the expert of
 // every m-tile; room for both: (E + 1) + mtile_table_len(E, C, rows) int32,
 // where rows bounds the filled rows of all experts together (m-tiles are at
@@ -120,5 +122,64 @@ inline size_t mtile_table_len(int E, int C, size_t rows) {
 // mt_start must be built with the same value).
 int gemm_block_m(bool bf16, int S, int E, int k);
 hipError_t launch_expert_gemm(const GemmParams& p, bool bf16, int bm, hipStream_t st);
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// ------------------------------------------------------------------ backward
+// Expert GEMMs of the backward pass (bf16, fp32 accumulation), per expert e
+// with rows r = row0[e] + m (row0 NULL: e*C + m), m < occ[e]:
+//   dgrad:  Cout[r, n] = sum_k A[r, k] * B[e, k, n]     (B is W [E,K,N])
+//           with mask: Cout[r, n] = 0 where mask[r, n] <= 0 (mask may be
+//           Cout itself); m-tiles of 256 rows from mt_start/mt_expert built
+//           with bm = 256, extra = 0.
+//   wgrad:  Cout[e, m, n] = sum over rows r of A[r, m] * B[b(r), n]
+//           (A [*,M], B [*,N] row-major; b(r) = b_rows[r] or r), every
+//           (m, n) < (M, N) written, zero for an empty expert.
+struct BwdGemmParams {
+    const void* A;
+    const void* B;
+    void* Cout;
+    const void* mask;          // dgrad: NULL or [rows, N]
+    const int32_t* occ;
+    const int32_t* mt_start;   // dgrad: m-tile prefix [E+1] ...
+    const int32_t* mt_expert;  // ... and the expert of each m-tile
+    const int32_t* row0;       // NULL (row e*C) or [E]
+    const int32_t* b_rows;     // wgrad: NULL or [rows] token row of each row
+    int32_t* tile_ctr;         // 8 counters, zero at launch
+    int E, C, M, N, K;
+    size_t rows;               // rows of the expert buffers (E*C or S*k)
+};
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, bool wgrad, bool mask, hipStream_t st);
+
+// inv[e*stride + slot[s,r]] = s for every kept assignment (stride 0: the
+// slot is the row).
+hipError_t launch_inverse_rows(const int32_t* topk_idx, const int32_t* slot, int S, int k,
+                               int E, int stride, int limit, int32_t* inv, hipStream_t st);
+// Combine backward: for kept (s,r) at row u, dO[u] = bf16(w[s,r] * dy[s]) and
+// dw[s,r] = dy[s] . out[u] (fp32); dw = 0 for dropped assignments.
+hipError_t launch_combine_bwd(const void* dy, const void* out, const int32_t* topk_idx,
+                              const int32_t* slot, const float* topk_w, void* dO, float* dw,
+                              int S, int d, int k, int E, int stride, int limit,
+                              hipStream_t st);
+// Router backward: gradient of the logits dl [S,E] (fp32) from the top-k
+// weight gradient dw, the aux loss (weight g_aux, first-choice counts) and
+// the z-loss (weight g_z).
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
+                             const float* dw, const int32_t* counts, float g_aux, float g_z,
+                             float* dl, int S, int E, int k, hipStream_t st);
+// out[e, n] = sum over rows r of expert e of v[r, n] (bf16 in, fp32 sums,
+// bf16 out).
+hipError_t launch_segment_colsum(const void* v, const int32_t* occ, const int32_t* row0, int E,
+                                 int C, int N, void* out, hipStream_t st);
+// Router-side fp32 GEMMs:
+//   dx[s, i] = bf16(sum_j dl[s, j] wg[j, i] + sum over kept r of dX[u(s,r), i])
+//   dwg[j, i] = sum_s dl[s, j] x[s, i];  dbg[j] = sum_s dl[s, j]
+hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
+                            const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
+                            int E, int k, int stride, int limit, hipStream_t st);
+hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,
+                            int E, hipStream_t st);
+// Fill n bytes with zero (a kernel, so that it can sit in a captured graph).
+hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st);
 
 }  // namespace moe

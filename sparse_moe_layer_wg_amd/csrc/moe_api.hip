@@ -335,7 +335,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* 
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
     int32_t* ctr = at<int32_t>(ws, cv.ctr);
     int32_t* seg = at<int32_t>(ws, cv.seg);
-    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, gemm_block_m(p.bf16, p.S, p.E, p.k), occ, mt,
+    const int bm = gemm_block_m(p.bf16, p.S, p.E, p.k);
+    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, bm, strip_rows(bm), occ, mt,
                              p.dropless ? seg : nullptr, (int)p.rows, ctr, kTileCounters,
                              stream));
     return run_ffn(p, xd, nullptr, w1, b1, w2, b2, out, occ, mt, seg, ctr, at<void>(ws, cv.H),
@@ -406,6 +407,203 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, row_stride(p), row_limit(p),
                            p.bf16, stream));
     record(ev, 8, stream);
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Tile counters of the backward: GEMM 1 recompute, wgrad 2, dgrad 2, wgrad 1,
+// dgrad 1 (8 each).
+constexpr int kBwdCounters = 40;
+
+// Backward workspace, every region 256-byte aligned:
+//   occ [E], forward m-tile list (E+1 + table), backward m-tile list
+//   (E+1 + table), seg [E], tile counters, inv [R], dw [S,k] fp32,
+//   dl [S,E] fp32, H then dU [R,h], dO then dX [R,d]   (R = rows)
+struct BwdCarve {
+    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, H, G, end;
+};
+
+BwdCarve bwd_carve(const Plan& p) {
+    BwdCarve c{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = up(o + bytes);
+        return at;
+    };
+    const size_t tab = ((size_t)p.E + 1 + mtile_table_len(p.E, p.C, p.rows)) * 4;
+    c.occ = take((size_t)p.E * 4);
+    c.mt_fwd = take(tab);
+    c.mt_bwd = take(tab);
+    c.seg = take((size_t)p.E * 4);
+    c.ctr = take(kBwdCounters * 4);
+    c.inv = take(p.rows * 4);
+    c.dw = take((size_t)p.S * p.k * 4);
+    c.dl = take((size_t)p.S * p.E * 4);
+    c.H = take(p.rows * p.h * 2);
+    c.G = take(p.rows * p.d * 2);
+    c.end = o;
+    return c;
+}
+
+// The backward runs bf16 activations only, and gathers token rows of x with
+// 32-bit offsets (x under 4 GiB), as the fused forward does.
+moe_status bwd_plan(const moe_config* cfg, Plan* p) {
+    moe_status s = make_plan(cfg, p);
+    if (s != MOE_OK) return s;
+    if (!p->bf16) return MOE_ERR_UNSUPPORTED;
+    if ((size_t)p->S * p->d * 2 >= ((size_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_backward_workspace_bytes(const moe_config* cfg, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    Plan p;
+    moe_status s = bwd_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    *bytes = bwd_carve(p).end;
+    return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float* w_gate,
+                              const void* w1, const void* b1, const void* w2,
+                              const float* logits, const int32_t* topk_idx, const float* topk_w,
+                              const int32_t* slot, const int32_t* counts, const void* out,
+                              const void* dy, float g_aux, float g_z, void* dx, float* dw_gate,
+                              float* db_gate, void* dw1, void* db1, void* dw2, void* db2,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    moe_status s = bwd_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (!w_gate || !w1 || !w2 || !dw_gate || !dw1 || !dw2 || !ws) return MOE_ERR_INVALID_ARG;
+    if (p.S > 0 && (!x || !logits || !topk_idx || !topk_w || !slot || !counts || !out || !dy ||
+                    !dx))
+        return MOE_ERR_INVALID_ARG;
+    if (!counts) return MOE_ERR_INVALID_ARG;
+    if (!isfinite(g_aux) || !isfinite(g_z)) return MOE_ERR_INVALID_ARG;
+    for (const void* q : {x, w1, b1, w2, out, dy, (const void*)dx, (const void*)dw1,
+                          (const void*)db1, (const void*)dw2, (const void*)db2})
+        if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+    const BwdCarve cv = bwd_carve(p);
+    if (ws_bytes < cv.end) return MOE_ERR_WORKSPACE;
+    const size_t E = p.E, d = p.d, h = p.h;
+    if (p.S == 0) {
+        // no tokens: every gradient is zero
+        MOE_TRY(launch_zero_bytes(dw_gate, E * d * 4, stream));
+        MOE_TRY(launch_zero_bytes(db_gate, db_gate ? E * 4 : 0, stream));
+        MOE_TRY(launch_zero_bytes(dw1, E * h * d * 2, stream));
+        MOE_TRY(launch_zero_bytes(db1, db1 ? E * h * 2 : 0, stream));
+        MOE_TRY(launch_zero_bytes(dw2, E * d * h * 2, stream));
+        MOE_TRY(launch_zero_bytes(db2, db2 ? E * d * 2 : 0, stream));
+        return MOE_OK;
+    }
+    int32_t* occ = at<int32_t>(ws, cv.occ);
+    int32_t* mt_fwd = at<int32_t>(ws, cv.mt_fwd);
+    int32_t* mt_bwd = at<int32_t>(ws, cv.mt_bwd);
+    int32_t* seg = at<int32_t>(ws, cv.seg);
+    int32_t* ctr = at<int32_t>(ws, cv.ctr);
+    int32_t* inv = at<int32_t>(ws, cv.inv);
+    float* dwk = at<float>(ws, cv.dw);
+    float* dl = at<float>(ws, cv.dl);
+    void* H = at<void>(ws, cv.H);
+    void* G = at<void>(ws, cv.G);
+    const int32_t* row0 = p.dropless ? seg : nullptr;
+    const int stride = row_stride(p), limit = row_limit(p);
+
+    // occupancies, both m-tile lists, segment starts, zeroed tile counters,
+    // and the inverse slot map (row -> token)
+    const int bm = gemm_block_m(true, p.S, p.E, p.k);
+    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, bm, strip_rows(bm), occ, mt_fwd,
+                             p.dropless ? seg : nullptr, (int)p.rows, ctr, kBwdCounters, stream));
+    MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, 256, 0, occ, mt_bwd,
+                             p.dropless ? seg : nullptr, (int)p.rows, nullptr, 0, stream));
+    MOE_TRY(launch_inverse_rows(topk_idx, slot, p.S, p.k, p.E, stride, limit, inv, stream));
+
+    // H = ReLU(x W1^T + b1) again (rows gathered from x), as in the forward
+    GemmParams g{};
+    g.occ = occ;
+    g.mt_start = mt_fwd;
+    g.mt_expert = mt_fwd + p.E + 1;
+    g.tile_ctr = ctr;
+    g.a_rows = inv;
+    g.row0 = row0;
+    g.E = p.E;
+    g.C = p.C;
+    g.A = x;
+    g.B = w1;
+    g.bias = b1;
+    g.Cout = H;
+    g.N = p.h;
+    g.K = p.d;
+    g.relu = true;
+    MOE_TRY(launch_expert_gemm(g, true, bm, stream));
+
+    // combine and router backward
+    MOE_TRY(launch_combine_bwd(dy, out, topk_idx, slot, topk_w, G, dwk, p.S, p.d, p.k, p.E, stride,
+                               limit, stream));
+    MOE_TRY(launch_router_bwd(logits, topk_idx, topk_w, dwk, counts, g_aux, g_z, dl, p.S, p.E, p.k,
+                              stream));
+
+    BwdGemmParams b{};
+    b.occ = occ;
+    b.row0 = row0;
+    b.E = p.E;
+    b.C = p.C;
+    b.rows = p.rows;
+    // dW2 = dO^T H (reads H before dgrad 2 overwrites it)
+    b.A = G;
+    b.B = H;
+    b.b_rows = nullptr;
+    b.Cout = dw2;
+    b.M = p.d;
+    b.N = p.h;
+    b.tile_ctr = ctr + 8;
+    MOE_TRY(launch_bwd_gemm(b, true, false, stream));
+    if (db2) MOE_TRY(launch_segment_colsum(G, occ, row0, p.E, p.C, p.d, db2, stream));
+    // dU = (dO W2) * [H > 0], in place over H
+    b.mt_start = mt_bwd;
+    b.mt_expert = mt_bwd + p.E + 1;
+    b.A = G;
+    b.B = w2;
+    b.mask = H;
+    b.Cout = H;
+    b.N = p.h;
+    b.K = p.d;
+    b.tile_ctr = ctr + 16;
+    MOE_TRY(launch_bwd_gemm(b, false, true, stream));
+    if (db1) MOE_TRY(launch_segment_colsum(H, occ, row0, p.E, p.C, p.h, db1, stream));
+    // dW1 = dU^T X (X rows gathered from x)
+    b.A = H;
+    b.B = x;
+    b.b_rows = inv;
+    b.mask = nullptr;
+    b.Cout = dw1;
+    b.M = p.h;
+    b.N = p.d;
+    b.tile_ctr = ctr + 24;
+    MOE_TRY(launch_bwd_gemm(b, true, false, stream));
+    // dX = dU W1, over dO's buffer (dO is no longer needed)
+    b.A = H;
+    b.B = w1;
+    b.b_rows = nullptr;
+    b.Cout = G;
+    b.N = p.d;
+    b.K = p.h;
+    b.tile_ctr = ctr + 32;
+    MOE_TRY(launch_bwd_gemm(b, false, false, stream));
+
+    // dx = dispatch backward + dl Wg; dWg = dl^T x; dbg = colsum dl
+    MOE_TRY(launch_router_dx(dl, w_gate, G, topk_idx, slot, dx, p.S, p.d, p.E, p.k, stride, limit,
+                             stream));
+    MOE_TRY(launch_router_dw(dl, x, dw_gate, db_gate, p.S, p.d, p.E, stream));
     return MOE_OK;
 }
 

@@ -42,14 +42,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
 // m-tile prefix mt_start [E+1] of the experts' filled rows occ, then the
 // expert of every m-tile; with seg non-null also seg[e] = sum_{e'<e} occ[e']
 // (compact rows).  All 256 threads of the block call it.
-__device__ void tile_prefix(const int32_t* __restrict__ occ, int E, int bm, int* s_wave,
-                            int32_t* __restrict__ mt_start, int32_t* __restrict__ seg) {
+__device__ void tile_prefix(const int32_t* __restrict__ occ, int E, int bm, int extra,
+                            int* s_wave, int32_t* __restrict__ mt_start,
+                            int32_t* __restrict__ seg) {
     const int tid = threadIdx.x;
     int carry = 0, rcarry = 0;
     for (int base = 0; base < E; base += 256) {
         const int e = base + tid;
         const int o = e < E ? occ[e] : 0;
-        const int v = expert_mtiles(o, bm);
+        const int v = expert_mtiles(o, bm, extra);
         int total;
         const int ex = block_exclusive_scan(v, s_wave, &total);
         if (e < E) {
@@ -150,7 +151,7 @@ __device__ void finalize_block(const double* __restrict__ psum, const float* __r
         losses[0] = (float)((double)E * aux_sum / (Sd * Sd));
         losses[1] = (float)(s_red[0] / Sd);
     }
-    tile_prefix(occ, E, bm, s_wave, mt_start, seg);
+    tile_prefix(occ, E, bm, bm == 256 ? kStripRows : 0, s_wave, mt_start, seg);
 }
 
 // One block (4 waves) per token block; wave w takes ranks w, w+4, ...
@@ -202,7 +203,7 @@ __device__ void positions_block(int b, const int32_t* __restrict__ topk_idx,
 // every m-tile (one block); with seg non-null also the compact segment
 // starts, the segments held within `rows` rows.
 __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restrict__ counts, int E,
-                                                        int k, int C, int bm,
+                                                        int k, int C, int bm, int extra,
                                                         int32_t* __restrict__ occ,
                                                         int32_t* __restrict__ mt_start,
                                                         int32_t* __restrict__ seg, int rows,
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
         }
         __syncthreads();
     }
-    tile_prefix(occ, E, bm, s_wave, mt_start, nullptr);
+    tile_prefix(occ, E, bm, extra, s_wave, mt_start, nullptr);
 }
 
 __global__ void zero_outputs_kernel(int32_t* counts, int n, float* losses) {
@@ -284,11 +285,11 @@ hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* his
     return hipGetLastError();
 }
 
-hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int32_t* occ,
-                            int32_t* mt_start, int32_t* seg, int rows, int32_t* ctr, int n_ctr,
-                            hipStream_t st) {
-    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, occ, mt_start, seg, rows, ctr,
-                                        n_ctr);
+hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int extra,
+                            int32_t* occ, int32_t* mt_start, int32_t* seg, int rows,
+                            int32_t* ctr, int n_ctr, hipStream_t st) {
+    occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, extra, occ, mt_start, seg, rows,
+                                        ctr, n_ctr);
     return hipGetLastError();
 }
 
