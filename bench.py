@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="balanced_bf16", choices=mw.ORDER)
     ap.add_argument("--dropless", action="store_true",
                     help="no capacity limit: compact [S*k,d] expert segments, no drops")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step: forward + moe_layer_backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -96,14 +98,21 @@ def algorithmic_work(w: mw.Workload, occ: np.ndarray, kept: int) -> dict:
     }
 
 
-def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float) -> dict:
+def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float, backward=False) -> dict:
     import oracle
     host = {n: mw.to_numpy(t) for n, t in inputs.items()}
+    dy = host["x"][::-1].copy()     # any fixed upstream gradient of the right shape
 
     def run(n):
-        C = oracle.capacity(n, w.E, w.k, w.capacity_factor)
+        C = n if w.dropless else oracle.capacity(n, w.E, w.k, w.capacity_factor)
         t0 = time.perf_counter()
-        if w.dropless:
+        if backward:
+            lg = oracle.logits(host["x"][:n], host["wg"], host["bg"])
+            oracle.layer(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
+                         host["w2"], host["b2"], w.k, max(C, 1), lg=lg)
+            oracle.layer_backward(host["x"][:n], host["wg"], host["w1"], host["b1"], host["w2"],
+                                  host["b2"], w.k, max(C, 1), lg, dy[:n], 0.01, 0.001)
+        elif w.dropless:
             oracle.layer_dropless(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
                                   host["w2"], host["b2"], w.k)
         else:
@@ -121,7 +130,8 @@ def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float) -> dict:
             "sample": f"first {n} of the {w.S} tokens of the same workload (same E, d, h, k, "
                       + ("dropless routing" if w.dropless else
                          "capacity_factor; C scaled with the sample")
-                      + f"), full fp64 oracle layer from logits to y, {t:.1f} s"}
+                      + "), full fp64 oracle layer from logits to y"
+                      + (" plus its backward" if backward else "") + f", {t:.1f} s"}
 
 
 def main():
@@ -137,6 +147,12 @@ def main():
     inputs = mw.generate(w, "cuda")
     cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype,
                      dropless=w.dropless)
+    if a.backward:
+        out = bench_training(a, w, inputs, cfg)
+        if not a.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(w, inputs, a.cpu_seconds, backward=True)
+        print(json.dumps(out), flush=True)
+        return
     layer = MoELayer.from_inputs(cfg, inputs, keep=False)
     x = inputs["x"]
     stream = torch.cuda.current_stream()
@@ -273,6 +289,120 @@ def main():
 
 def probe_C(cfg):
     return moe.capacity(cfg)
+
+
+BWD_STAGES = ["setup", "recompute_h", "combine_router_bwd", "wgrad2", "dgrad2", "wgrad1",
+              "dgrad1", "router_dx_dw"]
+BWD_GEMMS = ("recompute_h", "wgrad2", "dgrad2", "wgrad1", "dgrad1")
+
+
+def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
+    """One step = moe_layer_forward (keeping the routing and expert outputs)
+    + moe_layer_backward of sum(dy*y) + 0.01*aux + 0.001*z."""
+    layer = MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False)
+    x = inputs["x"]
+    S, d, h, E = w.S, w.d, w.h, w.E
+    dev, at = "cuda", w.torch_dtype
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1000)
+    dy = torch.randn((S, d), generator=g, device=dev).to(at)
+    bws = torch.empty(moe.backward_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    gr = dict(dx=torch.empty((S, d), dtype=at, device=dev),
+              dwg=torch.empty((E, d), dtype=torch.float32, device=dev),
+              dbg=torch.empty((E,), dtype=torch.float32, device=dev),
+              dw1=torch.empty((E, h, d), dtype=at, device=dev),
+              db1=torch.empty((E, h), dtype=at, device=dev),
+              dw2=torch.empty((E, d, h), dtype=at, device=dev),
+              db2=torch.empty((E, d), dtype=at, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(bwd_events=None):
+        layer.forward(x)
+        moe.layer_backward(cfg, x, inputs["wg"], inputs["w1"], inputs["b1"], inputs["w2"],
+                           layer.logits, layer.topk_idx, layer.topk_w, layer.slot, layer.counts,
+                           layer.out, dy, gr["dx"], gr["dwg"], gr["dw1"], gr["dw2"], bws,
+                           db_gate=gr["dbg"], db1=gr["db1"], db2=gr["db2"], g_aux=0.01,
+                           g_z=0.001, events=bwd_events)
+
+    def make_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_BWD_EVENTS)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    for _ in range(a.warmup):
+        step()
+    evs = [make_events() for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(a.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / a.steps
+    stage_us = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) * 1000.0 for ev in evs]))
+                for i, n in enumerate(BWD_STAGES)}
+    bwd_ms = float(np.mean([ev[0].elapsed_time(ev[-1]) for ev in evs]))
+
+    counts = layer.counts.cpu().numpy()
+    occ = np.minimum(counts.sum(0), layer.C)
+    kept = int(occ.sum())
+    nonempty = int((occ > 0).sum())
+    es = 2
+    flops = 2.0 * kept * d * h
+    act = kept * (d + h) * es
+    work = {
+        "recompute_h": dict(flops=flops, bytes=nonempty * h * d * es + kept * (d + h) * es),
+        # weight gradients: every expert's [d,h] gradient is written
+        "wgrad2": dict(flops=flops, bytes=E * d * h * es + act),
+        "wgrad1": dict(flops=flops, bytes=E * d * h * es + act),
+        # data gradients: weights of non-empty experts read once, rows in and out
+        "dgrad2": dict(flops=flops, bytes=nonempty * d * h * es + act + kept * h * es),
+        "dgrad1": dict(flops=flops, bytes=nonempty * d * h * es + act),
+    }
+    dom = max(BWD_GEMMS, key=lambda n: stage_us[n])
+    t = stage_us[dom] * 1e-6
+    fl, by = work[dom]["flops"], work[dom]["bytes"]
+    if by / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12):
+        roof = {"bound": "hbm", "achieved": by / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": fl / t / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name + "_training", dom)
+    roof["kernel"] = dom
+    roof["algorithmic_flops"] = fl
+    roof["algorithmic_bytes"] = by
+    roof["avg_launch_us"] = stage_us[dom]
+    gemm_s = sum(stage_us[n] for n in BWD_GEMMS) * 1e-6
+    return {
+        "metric": "MoE-layer training tokens/s (forward + backward)",
+        "value": S / (ms / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "forward+backward", "S": S, "d_model": d,
+                   "d_ff": h, "E": E, "k": w.k,
+                   "capacity_factor": None if w.dropless else w.capacity_factor,
+                   "C": None if w.dropless else layer.C, "dropless": w.dropless,
+                   "seed": w.seed},
+        "roofline": roof,
+        "backward_ms": bwd_ms,
+        "backward_stage_us": stage_us,
+        "backward_gemm_mfma_frac": 5 * flops / gemm_s / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),
+        "routing": {"kept": kept, "nonempty_experts": nonempty},
+        "wall_s": wall,
+    }
 
 
 if __name__ == "__main__":

@@ -233,7 +233,13 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
  * Precision: fp32 accumulation everywhere; the hidden activations are
  * recomputed (bf16, as in the forward), dO, du and the expert-side input
  * gradient are rounded to bf16 once; the router side is fp32.
- * ws: at least moe_backward_workspace_bytes() bytes, 256-byte aligned. */
+ * ws: at least moe_backward_workspace_bytes() bytes, 256-byte aligned.
+ * stage_events: NULL, or MOE_NUM_BWD_EVENTS caller-created events recorded
+ * on `stream` between the steps (NULL entries skipped). */
+#define MOE_NUM_BWD_EVENTS 9 /* [0] start, [1] after occupancy / m-tile lists /
+    inverse map / dispatched rows, [2] after the hidden-activation recompute, [3] after the combine
+    and router backward and db2, [4] after dW2, [5] after dU, [6] after dW1,
+    [7] after the expert-side input gradient, [8] after db1, dx, dWg, dbg */
 moe_status moe_backward_workspace_bytes(const moe_config *cfg, size_t *bytes);
 moe_status moe_layer_backward(const moe_config *cfg, const void *x, const float *w_gate,
                               const void *w1, const void *b1, const void *w2,
@@ -242,7 +248,8 @@ moe_status moe_layer_backward(const moe_config *cfg, const void *x, const float 
                               const int32_t *counts, const void *out, const void *dy,
                               float g_aux, float g_z, void *dx, float *dw_gate,
                               float *db_gate, void *dw1, void *db1, void *dw2, void *db2,
-                              void *ws, size_t ws_bytes, hipStream_t stream);
+                              void *ws, size_t ws_bytes, hipEvent_t *stage_events,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -60,8 +60,12 @@ def _load():
     f64 = ctypes.c_double
     lib.oracle_layer_backward.argtypes = [i32] * 6 + [vp, i32, vp, vp, vp, vp, vp, vp, vp, f64, f64] \
         + [vp] * 9
+    lib.oracle_router_backward.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, f64, f64, vp]
+    lib.oracle_backward_entries.argtypes = [i32] * 6 + [vp, i32, vp, vp, vp, vp, vp, vp, vp] \
+        + [f64, f64, i32, vp, vp, i32, vp, vp, vp, vp, vp]
     for name in ("oracle_logits", "oracle_route", "oracle_dispatch", "oracle_expert_ffn",
-                 "oracle_combine", "oracle_token_output", "oracle_layer_backward"):
+                 "oracle_combine", "oracle_token_output", "oracle_layer_backward",
+                 "oracle_router_backward", "oracle_backward_entries"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -280,3 +284,45 @@ def layer_backward(x, wg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray, dy: np
         _ptr(b2), _ptr(dy), float(g_aux), float(g_z),
         *[_ptr(out[n]) for n in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2", "dl", "dw")])
     return out
+
+
+def router_backward(lg: np.ndarray, idx, w, dw, counts, g_aux: float, g_z: float) -> np.ndarray:
+    """fp64 gradient of the logits [S,E] from the top-k weight gradient dw
+    [S,k] (any source, e.g. dot products with given expert outputs), the aux
+    loss and the z-loss."""
+    lg = np.ascontiguousarray(lg, dtype=np.float32)
+    S, E = lg.shape
+    k = idx.shape[1]
+    idx = np.ascontiguousarray(idx, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    dw = np.ascontiguousarray(dw, np.float64)
+    counts = np.ascontiguousarray(counts, np.int32)
+    assert idx.shape == w.shape == dw.shape == (S, k) and counts.shape == (k, E)
+    dl = np.empty((S, E))
+    _load().oracle_router_backward(S, E, k, _ptr(lg), _ptr(idx), _ptr(w), _ptr(dw), _ptr(counts),
+                                   float(g_aux), float(g_z), _ptr(dl))
+    return dl
+
+
+def backward_entries(x, wg, w1, b1, w2, b2, k: int, C: int, lg, dy, g_aux, g_z, tokens,
+                     entries) -> tuple[np.ndarray, np.ndarray]:
+    """dx rows of ``tokens`` and weight-gradient ``entries`` [(kind, e, a, b)]
+    (kind 1 dW1[e,a,b], 2 dW2[e,a,b], 3 db1[e,a], 4 db2[e,a]) computed one by
+    one, for full-size checks."""
+    x, dt = _act(x)
+    S, d = x.shape
+    h = w1.shape[1]
+    lg = np.ascontiguousarray(lg, dtype=np.float32)
+    E = lg.shape[1]
+    w1, b1, w2, b2, dy = _same_dtype(dt, w1, b1, w2, b2, dy)
+    wg = np.ascontiguousarray(wg, dtype=np.float32)
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    ent = np.ascontiguousarray(np.asarray(entries, np.int32).reshape(-1, 4))
+    kind, ee, ea, eb = (np.ascontiguousarray(ent[:, c]) for c in range(4))
+    dx_rows = np.empty((tokens.size, d))
+    vals = np.empty(len(ent))
+    _load().oracle_backward_entries(
+        S, d, h, E, k, C, _ptr(x), dt, _ptr(wg), _ptr(lg), _ptr(w1), _ptr(b1), _ptr(w2),
+        _ptr(b2), _ptr(dy), float(g_aux), float(g_z), tokens.size, _ptr(tokens), _ptr(dx_rows),
+        len(ent), _ptr(kind), _ptr(ee), _ptr(ea), _ptr(eb), _ptr(vals))
+    return dx_rows, vals

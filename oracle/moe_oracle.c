@@ -353,6 +353,52 @@ void oracle_token_output(int ns, const int64_t *tokens, int d, int h, int k,
  * the activation dtype.  Outputs (fp64, all required): dx [S,d], dwg [E,d],
  * dbg [E], dw1 [E,h,d], db1 [E,h], dw2 [E,d,h], db2 [E,d], dl [S,E],
  * dw [S,k]. */
+/* Gradient of the logits dl [S,E] (fp64) from the gradient dw [S,k] of the
+ * renormalised top-k weights, the aux loss (weight g_aux; counts [k,E] give
+ * f_j from their rank-0 row) and the z-loss (weight g_z):
+ *   dl[s, idx_r] += w_r (dw_r - sum_r' w_r' dw_r')      (softmax of the
+ *                                                       selected logits)
+ *   dl[s, j] += g_aux p_sj (a_j - sum_j' p_sj' a_j'),   a_j = E f_j / S
+ *   dl[s, j] += g_z (2/S) lse_s p_sj
+ * with p and lse from the fp32 logits.  [card] method paragraph (aux loss
+ * and z-loss); [blog] "Mixture-of-Experts Implementation" (softmax gate). */
+void oracle_router_backward(int S, int E, int k, const float *logits, const int32_t *idx,
+                            const double *w, const double *dw, const int32_t *counts,
+                            double g_aux, double g_z, double *dl)
+{
+    #pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        const float *l = logits + (size_t)s * E;
+        double *g = dl + (size_t)s * E;
+        double m = (double)l[0];
+        for (int j = 1; j < E; ++j)
+            if ((double)l[j] > m)
+                m = (double)l[j];
+        double sum = 0.0;
+        for (int j = 0; j < E; ++j)
+            sum += exp((double)l[j] - m);
+        double lse = m + log(sum);
+        double pa = 0.0;
+        for (int j = 0; j < E; ++j) {
+            double p = exp((double)l[j] - lse);
+            double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
+            pa += p * a_j;
+        }
+        for (int j = 0; j < E; ++j) {
+            double p = exp((double)l[j] - lse);
+            double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
+            g[j] = g_aux * p * (a_j - pa) + g_z * 2.0 / (double)S * lse * p;
+        }
+        double wdw = 0.0;
+        for (int r = 0; r < k; ++r)
+            wdw += w[(size_t)s * k + r] * dw[(size_t)s * k + r];
+        for (int r = 0; r < k; ++r) {
+            size_t q = (size_t)s * k + r;
+            g[idx[q]] += w[q] * (dw[q] - wdw);
+        }
+    }
+}
+
 void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
                            const void *x, int dtype, const float *wg, const float *logits,
                            const void *w1, const void *b1, const void *w2, const void *b2,
@@ -466,28 +512,10 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
     }
 
     /* router: gradient of the logits, then of Wg, bg and x */
+    oracle_router_backward(S, E, k, logits, idx, w, dw, counts, g_aux, g_z, dl);
     #pragma omp parallel for schedule(static)
     for (int s = 0; s < S; ++s) {
-        const float *l = logits + (size_t)s * E;
-        double *g = dl + (size_t)s * E;
-        double pa = 0.0;
-        for (int j = 0; j < E; ++j) {
-            double p = exp((double)l[j] - lse[s]);
-            double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
-            pa += p * a_j;
-        }
-        for (int j = 0; j < E; ++j) {
-            double p = exp((double)l[j] - lse[s]);
-            double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
-            g[j] = g_aux * p * (a_j - pa) + g_z * 2.0 / (double)S * lse[s] * p;
-        }
-        double wdw = 0.0;
-        for (int r = 0; r < k; ++r)
-            wdw += w[(size_t)s * k + r] * dw[(size_t)s * k + r];
-        for (int r = 0; r < k; ++r) {
-            size_t q = (size_t)s * k + r;
-            g[idx[q]] += w[q] * (dw[q] - wdw);
-        }
+        const double *g = dl + (size_t)s * E;
         for (int i = 0; i < d; ++i) {
             double acc = 0.0;
             for (int j = 0; j < E; ++j)
@@ -516,4 +544,163 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
     free(psum);
     free(a_all);
     free(du_all);
+}
+
+/* Backward entries computed one by one, for full-size checks (same chain
+ * rule as oracle_layer_backward, evaluated only where asked).  Routing comes
+ * from the fp32 logits with capacity C.
+ *   dx rows of the given tokens: expert part sum_r W1_e^T du plus the router
+ *   part Wg^T dl_s, with dw from the token's own expert outputs;
+ *   weight-gradient entries: kind 1 = dW1[e,a,b] (a < h, b < d), 2 = dW2[e,a,b]
+ *   (a < d, b < h), 3 = db1[e,a], 4 = db2[e,a], each a sum over the kept
+ *   assignments of expert e. */
+void oracle_backward_entries(int S, int d, int h, int E, int k, int C,
+                             const void *x, int dtype, const float *wg, const float *logits,
+                             const void *w1, const void *b1, const void *w2, const void *b2,
+                             const void *dy, double g_aux, double g_z,
+                             int ntok, const int64_t *tokens, double *dx_rows,
+                             int nent, const int32_t *kind, const int32_t *ent_e,
+                             const int32_t *ent_a, const int32_t *ent_b, double *ent_val)
+{
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)k * E);
+    double *w = (double *)malloc(sizeof(double) * ((size_t)S * k + 1));
+    double *lse = (double *)malloc(sizeof(double) * ((size_t)S + 1));
+    double *psum = (double *)malloc(sizeof(double) * (size_t)E);
+    double losses[2];
+    oracle_route(S, E, k, C, logits, idx, w, slot, counts, lse, psum, losses);
+
+    /* dx rows */
+    #pragma omp parallel
+    {
+        double *u = (double *)malloc(sizeof(double) * (size_t)h);
+        double *a = (double *)malloc(sizeof(double) * (size_t)h);
+        double *du = (double *)malloc(sizeof(double) * (size_t)h);
+        double dwr[64]; /* k <= 64 */
+        double *dl = (double *)malloc(sizeof(double) * (size_t)E);
+        #pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < ntok; ++t) {
+            int64_t s = tokens[t];
+            double *out = dx_rows + (size_t)t * d;
+            for (int i = 0; i < d; ++i)
+                out[i] = 0.0;
+            for (int r = 0; r < k; ++r) {
+                size_t q = (size_t)s * k + r;
+                dwr[r] = 0.0;
+                if (slot[q] < 0)
+                    continue;
+                int e = idx[q];
+                for (int j = 0; j < h; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += act_at(w1, dtype, ((size_t)e * h + j) * d + i) *
+                               act_at(x, dtype, (size_t)s * d + i);
+                    if (b1)
+                        acc += act_at(b1, dtype, (size_t)e * h + j);
+                    u[j] = acc;
+                    a[j] = acc > 0.0 ? acc : 0.0;
+                }
+                double dwq = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        acc += act_at(w2, dtype, ((size_t)e * d + i) * h + j) * a[j];
+                    if (b2)
+                        acc += act_at(b2, dtype, (size_t)e * d + i);
+                    dwq += act_at(dy, dtype, (size_t)s * d + i) * acc;
+                }
+                dwr[r] = dwq;
+                for (int j = 0; j < h; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += act_at(w2, dtype, ((size_t)e * d + i) * h + j) *
+                               (w[q] * act_at(dy, dtype, (size_t)s * d + i));
+                    du[j] = u[j] > 0.0 ? acc : 0.0;
+                }
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        acc += act_at(w1, dtype, ((size_t)e * h + j) * d + i) * du[j];
+                    out[i] += acc;
+                }
+            }
+            /* the router part needs this token's dl row only: the selected
+             * term from a one-token call (loss weights 0), then the aux and z
+             * terms, which depend on the whole batch through S */
+            oracle_router_backward(1, E, k, logits + (size_t)s * E, idx + (size_t)s * k,
+                                   w + (size_t)s * k, dwr, counts, 0.0, 0.0, dl);
+            {
+                const float *l = logits + (size_t)s * E;
+                double pa = 0.0;
+                for (int j = 0; j < E; ++j)
+                    pa += exp((double)l[j] - lse[s]) * (double)E * (double)counts[j] / (double)S / (double)S;
+                for (int j = 0; j < E; ++j) {
+                    double p = exp((double)l[j] - lse[s]);
+                    double a_j = (double)E * (double)counts[j] / (double)S / (double)S;
+                    dl[j] += g_aux * p * (a_j - pa) + g_z * 2.0 / (double)S * lse[s] * p;
+                }
+            }
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < E; ++j)
+                    acc += dl[j] * (double)wg[(size_t)j * d + i];
+                out[i] += acc;
+            }
+        }
+        free(u);
+        free(a);
+        free(du);
+        free(dl);
+    }
+
+    /* weight-gradient entries */
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < nent; ++t) {
+        int e = ent_e[t], ka = ent_a[t], kb = ent_b[t];
+        double acc = 0.0;
+        for (int s = 0; s < S; ++s) {
+            for (int r = 0; r < k; ++r) {
+                size_t q = (size_t)s * k + r;
+                if (slot[q] < 0 || idx[q] != e)
+                    continue;
+                if (kind[t] == 2 || kind[t] == 4) {
+                    double dO = w[q] * act_at(dy, dtype, (size_t)s * d + ka);
+                    if (kind[t] == 4) {
+                        acc += dO;
+                        continue;
+                    }
+                    double uu = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        uu += act_at(w1, dtype, ((size_t)e * h + kb) * d + i) *
+                              act_at(x, dtype, (size_t)s * d + i);
+                    if (b1)
+                        uu += act_at(b1, dtype, (size_t)e * h + kb);
+                    acc += dO * (uu > 0.0 ? uu : 0.0);
+                } else {
+                    /* du[ka] for this assignment */
+                    double uu = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        uu += act_at(w1, dtype, ((size_t)e * h + ka) * d + i) *
+                              act_at(x, dtype, (size_t)s * d + i);
+                    if (b1)
+                        uu += act_at(b1, dtype, (size_t)e * h + ka);
+                    if (!(uu > 0.0))
+                        continue;
+                    double da = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        da += act_at(w2, dtype, ((size_t)e * d + i) * h + ka) *
+                              (w[q] * act_at(dy, dtype, (size_t)s * d + i));
+                    acc += kind[t] == 3 ? da : da * act_at(x, dtype, (size_t)s * d + kb);
+                }
+            }
+        }
+        ent_val[t] = acc;
+    }
+    free(idx);
+    free(slot);
+    free(counts);
+    free(w);
+    free(lse);
+    free(psum);
 }

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     MOE_CFG_DROPLESS,
     MOE_F32,
     MOE_GATE_LOGITS_IN,
+    MOE_NUM_BWD_EVENTS,
     MOE_NUM_STAGE_EVENTS,
     MoeConfig,
     MoeError,

@@ -19,6 +19,7 @@ MOE_BF16 = 1
 MOE_GATE_LOGITS_IN = 1
 MOE_CFG_DROPLESS = 1
 MOE_NUM_STAGE_EVENTS = 9
+MOE_NUM_BWD_EVENTS = 9
 
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
@@ -93,7 +94,7 @@ def library():
     lib.moe_backward_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     f32 = ctypes.c_float
     lib.moe_layer_backward.argtypes = [cfgp] + [vp] * 12 + [f32, f32] + [vp] * 8 + \
-        [ctypes.c_size_t, vp]
+        [ctypes.c_size_t, vp, vp]
     for f in ("moe_workspace_bytes", "moe_gate", "moe_dispatch", "moe_expert_ffn",
               "moe_combine", "moe_layer_forward", "moe_backward_workspace_bytes",
               "moe_layer_backward"):
@@ -153,6 +154,18 @@ def _ws(ws):
     if ws.device.type != "cuda" or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def _events(events, n):
+    """ctypes array of n hipEvent_t handles (None entries -> NULL), or None."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"events must hold {n} events")
+    handles = [None if e is None else e.cuda_event for e in events]
+    if not all(h for e, h in zip(events, handles) if e is not None):
+        raise ValueError("events must be created (recorded once) before use")
+    return (ctypes.c_void_p * n)(*handles)
 
 
 def gate(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, losses, ws,
@@ -226,14 +239,7 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
     S, d, h, E, k = cfg.S, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     at = cfg.torch_dtype
     wsp, wsb = _ws(ws)
-    ev = None
-    if events is not None:
-        if len(events) != MOE_NUM_STAGE_EVENTS:
-            raise ValueError(f"events must hold {MOE_NUM_STAGE_EVENTS} events")
-        handles = [None if e is None else e.cuda_event for e in events]
-        if not all(h for e, h in zip(events, handles) if e is not None):
-            raise ValueError("events must be created (recorded once) before use")
-        ev = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
+    ev = _events(events, MOE_NUM_STAGE_EVENTS)
     st = library().moe_layer_forward(
         ctypes.byref(cfg), _arg(x, "x", at, S * d), _arg(w_gate, "w_gate", torch.float32, E * d),
         _arg(gate_bias, "gate_bias", torch.float32, E, required=False),
@@ -261,8 +267,9 @@ def backward_workspace_bytes(cfg: MoeConfig) -> int:
 
 def layer_backward(cfg, x, w_gate, w1, b1, w2, logits, topk_idx, topk_w, slot, counts, out, dy,
                    dx, dw_gate, dw1, dw2, ws, db_gate=None, db1=None, db2=None, g_aux=0.0,
-                   g_z=0.0, stream=None):
-    """Gradients of sum(dy*y) + g_aux*aux + g_z*z (``moe_layer_backward``)."""
+                   g_z=0.0, events=None, stream=None):
+    """Gradients of sum(dy*y) + g_aux*aux + g_z*z (``moe_layer_backward``).
+    ``events``: None or MOE_NUM_BWD_EVENTS entries (None or created events)."""
     R = dispatch_rows(cfg)
     S, d, h, E, k = cfg.S, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     at = cfg.torch_dtype
@@ -279,5 +286,5 @@ def layer_backward(cfg, x, w_gate, w1, b1, w2, logits, topk_idx, topk_w, slot, c
         _arg(db_gate, "db_gate", torch.float32, E, required=False),
         _arg(dw1, "dw1", at, E * h * d), _arg(db1, "db1", at, E * h, required=False),
         _arg(dw2, "dw2", at, E * d * h), _arg(db2, "db2", at, E * d, required=False),
-        wsp, wsb, _stream(stream))
+        wsp, wsb, _events(events, MOE_NUM_BWD_EVENTS), _stream(stream))
     _check(st, "moe_layer_backward")

@@ -159,24 +159,31 @@ __global__ __launch_bounds__(256) void segment_colsum_kernel(const bf16_t* __res
 // fp32 GEMM for the router side, 64x64 tiles, 4x4 results per thread, k-steps
 // of 16 staged in LDS as [k][row].
 //   DX:  C[s, i] = sum_j dl[s, j] wg[j, i]  (+ the token's dX rows, bf16 out)
-//   DW:  C[j, i] = sum_s dl[s, j] x[s, i]   (fp32 out)
+//   DW:  C[j, i] = sum_s dl[s, j] x[s, i]   (fp32 out), the tokens split into
+//        gridDim.z chunks of kchunk: chunk z writes its partial sums to
+//        Cout + z*E*d, and the blocks of column tile 0 also the partial
+//        column sums of dl to pdbg + z*E (summed in a fixed order later).
 constexpr int RT = 64, RK = 16;
 template <bool DX>
 __global__ __launch_bounds__(256) void router_gemm_kernel(
     const float* __restrict__ dl, const void* __restrict__ Bsrc, const bf16_t* __restrict__ dX,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot,
-    void* __restrict__ Cout, int S, int d, int E, int k, int stride, int limit) {
+    void* __restrict__ Cout, float* __restrict__ pdbg, int S, int d, int E, int k, int stride,
+    int limit, int kchunk) {
     __shared__ float As[RK][RT + 4];
     __shared__ float Bs[RK][RT + 4];
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     const int m0 = blockIdx.y * RT, n0 = blockIdx.x * RT;
-    const int M = DX ? S : E, K = DX ? E : S;
+    const int M = DX ? S : E;
+    const int kbeg = DX ? 0 : blockIdx.z * kchunk;
+    const int K = DX ? E : min(S, kbeg + kchunk);
     float acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    for (int k0 = 0; k0 < K; k0 += RK) {
+    float csum = 0.f;  // DW, column tile 0: sum of dl[., m0 + tid] over the chunk
+    for (int k0 = kbeg; k0 < K; k0 += RK) {
         // A(m, kk): DX: dl[m, kk] (m = token); DW: dl[kk, m] (kk = token)
         // B(n, kk): DX: wg[kk, n];             DW: x[kk, n] (bf16)
         // thread loads 4 A and 4 B elements: (kk = tid / 16, col = (tid % 16) * 4 + c)
@@ -204,6 +211,10 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
             Bs[kk][nn] = bv;
         }
         __syncthreads();
+        if (!DX && blockIdx.x == 0 && tid < RT) {
+#pragma unroll
+            for (int kk = 0; kk < RK; ++kk) csum += As[kk][tid];
+        }
 #pragma unroll
         for (int kk = 0; kk < RK; ++kk) {
             float a[4], b[4];
@@ -239,23 +250,34 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
                 static_cast<bf16_t*>(Cout)[(int64_t)m * d + n] = f32_to_bf16(v);
             }
         } else {
+            float* part = static_cast<float*>(Cout) + (int64_t)blockIdx.z * E * d;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = n0 + tx + 16 * j;
-                if (n < d) static_cast<float*>(Cout)[(int64_t)m * d + n] = acc[i][j];
+                if (n < d) part[(int64_t)m * d + n] = acc[i][j];
             }
         }
     }
+    if (!DX && blockIdx.x == 0 && tid < RT && m0 + tid < E)
+        pdbg[(int64_t)blockIdx.z * E + m0 + tid] = csum;
 }
 
-// dbg[j] = sum_s dl[s, j]: one thread per expert, tokens in order.
-__global__ void logit_colsum_kernel(const float* __restrict__ dl, int S, int E,
-                                    float* __restrict__ dbg) {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= E) return;
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += dl[(int64_t)s * E + j];
-    dbg[j] = acc;
+// dwg = sum over chunks of the partial products, dbg likewise (chunk order).
+__global__ void router_dw_reduce_kernel(const float* __restrict__ part,
+                                        const float* __restrict__ pdbg, int nsplit, int E, int d,
+                                        float* __restrict__ dwg, float* __restrict__ dbg) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n = (int64_t)E * d;
+    if (i < n) {
+        float acc = 0.f;
+        for (int z = 0; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
+        dwg[i] = acc;
+    }
+    if (dbg && i < E) {
+        float acc = 0.f;
+        for (int z = 0; z < nsplit; ++z) acc += pdbg[(int64_t)z * E + i];
+        dbg[i] = acc;
+    }
 }
 
 // n bytes, n even (every array here holds 2- or 4-byte elements).
@@ -314,21 +336,39 @@ hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
     if (S == 0) return hipSuccess;
     dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(S, RT));
     router_gemm_kernel<true><<<grid, 256, 0, st>>>(dl, wg, static_cast<const bf16_t*>(dX),
-                                                   topk_idx, slot, dx, S, d, E, k, stride, limit);
+                                                   topk_idx, slot, dx, nullptr, S, d, E, k,
+                                                   stride, limit, 0);
     return hipGetLastError();
 }
 
+int router_dw_splits(int S, int d, int E) {
+    // enough token chunks for ~1024 blocks, chunks of at least 256 tokens
+    const long long tiles = ceil_div(d, RT) * ceil_div(E, RT);
+    long long n = ceil_div(1024, tiles);
+    const long long most = ceil_div(S, 256);
+    if (n > most) n = most;
+    return (int)(n < 1 ? 1 : n);
+}
+
+size_t router_dw_workspace(int S, int d, int E) {
+    const size_t n = (size_t)router_dw_splits(S, d, E);
+    return n * (size_t)E * d * 4 + n * (size_t)E * 4;
+}
+
 hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,
-                            int E, hipStream_t st) {
-    dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(E, RT));
-    router_gemm_kernel<false><<<grid, 256, 0, st>>>(dl, x, nullptr, nullptr, nullptr, dwg, S, d,
-                                                    E, 1, 0, 0);
+                            int E, void* part, hipStream_t st) {
+    const int nsplit = router_dw_splits(S, d, E);
+    const int kchunk = (int)ceil_div(S, nsplit);
+    float* pw = static_cast<float*>(part);
+    float* pb = pw + (size_t)nsplit * E * d;
+    dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(E, RT), (unsigned)nsplit);
+    router_gemm_kernel<false><<<grid, 256, 0, st>>>(dl, x, nullptr, nullptr, nullptr, pw, pb, S,
+                                                    d, E, 1, 0, 0, kchunk);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    if (dbg) {
-        logit_colsum_kernel<<<(unsigned)ceil_div(E, 256), 256, 0, st>>>(dl, S, E, dbg);
-        return hipGetLastError();
-    }
-    return hipSuccess;
+    const int64_t n = (int64_t)E * d;
+    router_dw_reduce_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(pw, pb, nsplit, E, d,
+                                                                        dwg, dbg);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st) {

@@ -177,8 +177,10 @@ hipError_t launch_segment_colsum(const void* v, const int32_t* occ, const int32_
 hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
                             const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
                             int E, int k, int stride, int limit, hipStream_t st);
+// (dwg over token chunks: `part` holds router_dw_workspace bytes of partials)
+size_t router_dw_workspace(int S, int d, int E);
 hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,
-                            int E, hipStream_t st);
+                            int E, void* part, hipStream_t st);
 // Fill n bytes with zero (a kernel, so that it can sit in a captured graph).
 hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st);
 

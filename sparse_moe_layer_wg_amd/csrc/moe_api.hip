@@ -421,9 +421,10 @@ constexpr int kBwdCounters = 40;
 // Backward workspace, every region 256-byte aligned:
 //   occ [E], forward m-tile list (E+1 + table), backward m-tile list
 //   (E+1 + table), seg [E], tile counters, inv [R], dw [S,k] fp32,
-//   dl [S,E] fp32, H then dU [R,h], dO then dX [R,d]   (R = rows)
+//   dl [S,E] fp32, router-gradient partials, H then dU [R,h], dO then dX
+//   [R,d], the dispatched rows of x [R,d]   (R = rows)
 struct BwdCarve {
-    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, H, G, end;
+    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, rpart, H, G, X, end;
 };
 
 BwdCarve bwd_carve(const Plan& p) {
@@ -443,8 +444,10 @@ BwdCarve bwd_carve(const Plan& p) {
     c.inv = take(p.rows * 4);
     c.dw = take((size_t)p.S * p.k * 4);
     c.dl = take((size_t)p.S * p.E * 4);
+    c.rpart = take(router_dw_workspace(p.S, p.d, p.E));
     c.H = take(p.rows * p.h * 2);
     c.G = take(p.rows * p.d * 2);
+    c.X = take(p.rows * p.d * 2);
     c.end = o;
     return c;
 }
@@ -478,7 +481,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
                               const int32_t* slot, const int32_t* counts, const void* out,
                               const void* dy, float g_aux, float g_z, void* dx, float* dw_gate,
                               float* db_gate, void* dw1, void* db1, void* dw2, void* db2,
-                              void* ws, size_t ws_bytes, hipStream_t stream) {
+                              void* ws, size_t ws_bytes, hipEvent_t* stage_events,
+                              hipStream_t stream) {
     Plan p;
     moe_status s = bwd_plan(cfg, &p);
     if (s != MOE_OK) return s;
@@ -495,6 +499,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     const BwdCarve cv = bwd_carve(p);
     if (ws_bytes < cv.end) return MOE_ERR_WORKSPACE;
     const size_t E = p.E, d = p.d, h = p.h;
+    hipEvent_t* ev = stage_events;
+    record(ev, 0, stream);
     if (p.S == 0) {
         // no tokens: every gradient is zero
         MOE_TRY(launch_zero_bytes(dw_gate, E * d * 4, stream));
@@ -503,6 +509,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
         MOE_TRY(launch_zero_bytes(db1, db1 ? E * h * 2 : 0, stream));
         MOE_TRY(launch_zero_bytes(dw2, E * d * h * 2, stream));
         MOE_TRY(launch_zero_bytes(db2, db2 ? E * d * 2 : 0, stream));
+        for (int i = 1; i < MOE_NUM_BWD_EVENTS; ++i) record(ev, i, stream);
         return MOE_OK;
     }
     int32_t* occ = at<int32_t>(ws, cv.occ);
@@ -526,6 +533,12 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, 256, 0, occ, mt_bwd,
                              p.dropless ? seg : nullptr, (int)p.rows, nullptr, 0, stream));
     MOE_TRY(launch_inverse_rows(topk_idx, slot, p.S, p.k, p.E, stride, limit, inv, stream));
+    // the expert rows of x, written once: dW1's K-major operand reads them
+    // as plain rows (a gather there would put a dependent index load in
+    // front of every row load)
+    void* X = at<void>(ws, cv.X);
+    MOE_TRY(launch_dispatch(x, topk_idx, slot, X, p.S, p.d, p.k, p.E, stride, limit, 2, stream));
+    record(ev, 1, stream);
 
     // H = ReLU(x W1^T + b1) again (rows gathered from x), as in the forward
     GemmParams g{};
@@ -545,12 +558,15 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     g.K = p.d;
     g.relu = true;
     MOE_TRY(launch_expert_gemm(g, true, bm, stream));
+    record(ev, 2, stream);
 
     // combine and router backward
     MOE_TRY(launch_combine_bwd(dy, out, topk_idx, slot, topk_w, G, dwk, p.S, p.d, p.k, p.E, stride,
                                limit, stream));
     MOE_TRY(launch_router_bwd(logits, topk_idx, topk_w, dwk, counts, g_aux, g_z, dl, p.S, p.E, p.k,
                               stream));
+    if (db2) MOE_TRY(launch_segment_colsum(G, occ, row0, p.E, p.C, p.d, db2, stream));
+    record(ev, 3, stream);
 
     BwdGemmParams b{};
     b.occ = occ;
@@ -567,7 +583,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.N = p.h;
     b.tile_ctr = ctr + 8;
     MOE_TRY(launch_bwd_gemm(b, true, false, stream));
-    if (db2) MOE_TRY(launch_segment_colsum(G, occ, row0, p.E, p.C, p.d, db2, stream));
+    record(ev, 4, stream);
     // dU = (dO W2) * [H > 0], in place over H
     b.mt_start = mt_bwd;
     b.mt_expert = mt_bwd + p.E + 1;
@@ -579,17 +595,18 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.K = p.d;
     b.tile_ctr = ctr + 16;
     MOE_TRY(launch_bwd_gemm(b, false, true, stream));
-    if (db1) MOE_TRY(launch_segment_colsum(H, occ, row0, p.E, p.C, p.h, db1, stream));
-    // dW1 = dU^T X (X rows gathered from x)
+    record(ev, 5, stream);
+    // dW1 = dU^T X
     b.A = H;
-    b.B = x;
-    b.b_rows = inv;
+    b.B = X;
+    b.b_rows = nullptr;
     b.mask = nullptr;
     b.Cout = dw1;
     b.M = p.h;
     b.N = p.d;
     b.tile_ctr = ctr + 24;
     MOE_TRY(launch_bwd_gemm(b, true, false, stream));
+    record(ev, 6, stream);
     // dX = dU W1, over dO's buffer (dO is no longer needed)
     b.A = H;
     b.B = w1;
@@ -599,11 +616,16 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.K = p.h;
     b.tile_ctr = ctr + 32;
     MOE_TRY(launch_bwd_gemm(b, false, false, stream));
+    record(ev, 7, stream);
 
-    // dx = dispatch backward + dl Wg; dWg = dl^T x; dbg = colsum dl
+    // db1 (dU stays in H's buffer); dx = dispatch backward + dl Wg;
+    // dWg = dl^T x; dbg = colsum dl
+    if (db1) MOE_TRY(launch_segment_colsum(H, occ, row0, p.E, p.C, p.h, db1, stream));
     MOE_TRY(launch_router_dx(dl, w_gate, G, topk_idx, slot, dx, p.S, p.d, p.E, p.k, stride, limit,
                              stream));
-    MOE_TRY(launch_router_dw(dl, x, dw_gate, db_gate, p.S, p.d, p.E, stream));
+    MOE_TRY(launch_router_dw(dl, x, dw_gate, db_gate, p.S, p.d, p.E, at<void>(ws, cv.rpart),
+                             stream));
+    record(ev, 8, stream);
     return MOE_OK;
 }
 

@@ -148,3 +148,30 @@ def test_binding_rejects_host_tensors():
         moe.dispatch(cfg, x, torch.zeros(4, 1, dtype=torch.int32),
                      torch.zeros(4, 1, dtype=torch.int32), torch.zeros(2, 2, 64))
     assert _lib.MOE_NUM_STAGE_EVENTS == 9
+
+
+def test_backward_validation_on_host():
+    lib = moe.library()
+    n = ctypes.c_size_t(0)
+    # bf16 only; fp32 activations are valid but not supported by the backward
+    f32 = moe.config(100, 64, 64, 4, 2, dtype="f32")
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(f32), ctypes.byref(n)) == 2
+    cfg = moe.config(1000, 256, 512, 16, 2, 1.0)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 0
+    # at least H [R,h] and one [R,d] buffer in bf16 with R = E*C rows
+    assert n.value >= 16 * 125 * (512 + 256) * 2
+    need = n.value
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    f = ctypes.c_float
+
+    def call(ws_bytes=need, g_aux=0.0, drop=None):
+        args = [fake] * 12
+        if drop is not None:
+            args[drop] = None
+        return lib.moe_layer_backward(ctypes.byref(cfg), *args, f(g_aux), f(0.0), fake, fake,
+                                      None, fake, None, fake, None, fake, ws_bytes, None, None)
+    assert call(ws_bytes=need - 1) == 3                 # workspace too small
+    assert call(drop=11) == 1                           # dy missing
+    assert call(drop=10) == 1                           # forward expert outputs missing
+    assert call(g_aux=float("nan")) == 1                # loss weight not finite
+    assert moe.backward_workspace_bytes(moe.config(2000, 128, 256, 8, 2, dropless=True)) > 0

@@ -126,8 +126,6 @@ def test_backward_deterministic():
 
 def test_backward_empty_input():
     """S = 0: every weight gradient is zero."""
-    w = mw.Workload("bwd_empty", S=0, d=64, h=128, E=4, k=2, capacity_factor=1.0, dtype="bf16",
-                    seed=1)
     cfg = moe.config(0, 64, 128, 4, 2, dtype="bf16")
     dev = "cuda"
     z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device=dev)
@@ -146,4 +144,73 @@ def test_backward_empty_input():
     torch.cuda.synchronize()
     for key, t in grads.items():
         assert not torch.any(t != 0), key
-    del w
+
+
+@pytest.mark.parametrize("name,ntok", [("balanced_bf16", 24), ("deepseek_bf16", 6)])
+def test_backward_full_size_sampled(name, ntok):
+    """Full-size workloads in the training benchmark's configuration (fused
+    gather in the forward, the benchmark's loss weights).  dx rows of sampled
+    tokens and sampled entries of dW1, dW2, db1, db2 are computed one by one
+    by the oracle; the router gradients dWg (sampled columns) and dbg come
+    from the oracle's logit gradient for all tokens, given the forward's
+    expert outputs."""
+    w = mw.get(name)
+    print(f"\n[bwd full] {w}", flush=True)
+    inputs, layer = run_layer(w, dispatch_buffer=False)
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    g_aux, g_z = 0.01, 0.001
+    grads = run_backward(w, inputs, layer, dy, g_aux, g_z)
+    host = {n: mw.to_numpy(t) for n, t in inputs.items()}
+    lg = layer.logits.cpu().numpy()
+    dy_h = mw.to_numpy(dy)
+    rng = np.random.default_rng(w.seed)
+    tok = np.sort(rng.choice(w.S, ntok, replace=False))
+    counts = layer.counts.cpu().numpy()
+    nonempty = np.nonzero(counts.sum(0) > 0)[0]
+    ents = []
+    for kind, na, nb in ((1, w.h, w.d), (2, w.d, w.h), (3, w.h, 1), (4, w.d, 1)):
+        for _ in range(48):
+            ents.append((kind, int(rng.choice(nonempty)), int(rng.integers(na)),
+                         int(rng.integers(nb))))
+    rows, vals = oracle.backward_entries(host["x"], host["wg"], host["w1"], host["b1"],
+                                         host["w2"], host["b2"], w.k, layer.C, lg, dy_h, g_aux,
+                                         g_z, tok, ents)
+    rep = {"dx_rows": rel_fro(as_f64(grads["dx"][torch.from_numpy(tok).cuda()]), rows)}
+    gpu = {1: as_f64(grads["dw1"]), 2: as_f64(grads["dw2"]), 3: as_f64(grads["db1"]),
+           4: as_f64(grads["db2"])}
+    for kind, key in ((1, "dw1"), (2, "dw2"), (3, "db1"), (4, "db2")):
+        sel = [i for i, e in enumerate(ents) if e[0] == kind]
+        got = [gpu[kind][ents[i][1], ents[i][2], ents[i][3]] if kind <= 2 else
+               gpu[kind][ents[i][1], ents[i][2]] for i in sel]
+        rep[key] = rel_fro(got, vals[sel])
+
+    # router: the logit gradient for every token from the forward's own
+    # expert outputs (dw = dy . out row), then dbg and sampled dWg columns
+    r = oracle.route(lg, w.k, layer.C)
+    out = layer.out.reshape(-1, w.d)
+    slot, idx = r["slot"], r["idx"]
+    dwk = np.zeros((w.S, w.k))
+    for s0 in range(0, w.S, 1024):
+        sl = slice(s0, min(w.S, s0 + 1024))
+        for rr in range(w.k):
+            keep = slot[sl, rr] >= 0
+            u = idx[sl, rr].astype(np.int64) * layer.C + slot[sl, rr]
+            u_t = torch.from_numpy(np.where(keep, u, 0)).cuda()
+            o = as_f64(out[u_t])
+            dwk[sl, rr] = np.where(keep, np.einsum("ij,ij->i", o, dy_h_f64(dy_h[sl])), 0.0)
+    dl = oracle.router_backward(lg, idx, r["w"], dwk, counts, g_aux, g_z)
+    rep["dbg"] = rel_fro(as_f64(grads["dbg"]), dl.sum(0))
+    cols = np.sort(rng.choice(w.d, 128, replace=False))
+    x64 = dy_h_f64(host["x"][:, cols])
+    rep["dwg_cols"] = rel_fro(as_f64(grads["dwg"])[:, cols], dl.T @ x64)
+    _print(name + "_bwd", rep)
+    for key, err in rep.items():
+        assert err <= TOL, (key, rep)
+    del layer, inputs, grads
+    torch.cuda.empty_cache()
+
+
+def dy_h_f64(a):
+    """bf16 bit patterns (uint16) as float64."""
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -189,3 +189,27 @@ def test_no_loss_weight_no_router_gradient_from_losses():
     want = 2.0 / S * torch.logsumexp(l64, 1)[:, None] * torch.softmax(l64, 1)
     assert np.allclose(g["dl"], want.numpy(), rtol=1e-13, atol=0)
     assert np.allclose(g["dbg"], want.numpy().sum(0), rtol=1e-12, atol=1e-15)
+
+
+def test_entries_match_full_backward():
+    """The one-by-one entries (full-size checks) equal the full backward's,
+    and the router function equals its logit gradient."""
+    S, d, h, E, k = 30, 6, 10, 5, 2
+    x, wg, bg, w1, b1, w2, b2, dy = make(S, d, h, E, 13)
+    C = oracle.capacity(S, E, k, 0.8)
+    lg = oracle.logits(x, wg, bg)
+    g = oracle.layer_backward(x, wg, w1, b1, w2, b2, k, C, lg, dy, 0.6, 0.4)
+    rng = np.random.default_rng(1)
+    tok = rng.choice(S, 7, replace=False)
+    ents = [(1, int(rng.integers(E)), int(rng.integers(h)), int(rng.integers(d))) for _ in range(9)]
+    ents += [(2, int(rng.integers(E)), int(rng.integers(d)), int(rng.integers(h))) for _ in range(9)]
+    ents += [(3, int(rng.integers(E)), int(rng.integers(h)), 0) for _ in range(5)]
+    ents += [(4, int(rng.integers(E)), int(rng.integers(d)), 0) for _ in range(5)]
+    rows, vals = oracle.backward_entries(x, wg, w1, b1, w2, b2, k, C, lg, dy, 0.6, 0.4, tok, ents)
+    assert np.allclose(rows, g["dx"][tok], rtol=1e-12, atol=1e-13)
+    full = {1: g["dw1"], 2: g["dw2"], 3: g["db1"], 4: g["db2"]}
+    want = [full[kd][e, a, b] if kd <= 2 else full[kd][e, a] for kd, e, a, b in ents]
+    assert np.allclose(vals, want, rtol=1e-12, atol=1e-13)
+    r = oracle.route(lg, k, C)
+    dl = oracle.router_backward(lg, r["idx"], r["w"], g["dw"], r["counts"], 0.6, 0.4)
+    assert np.allclose(dl, g["dl"], rtol=1e-13, atol=1e-15)
