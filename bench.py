@@ -56,16 +56,17 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_sha() -> str:
+def source_sha(name: str) -> str:
     import hashlib
-    path = os.path.join(ROOT, "sparse_moe_layer_wg_amd", "csrc", "gemm.hip")
+    path = os.path.join(ROOT, "sparse_moe_layer_wg_amd", "csrc", name)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None
-    when there is none or the GEMM source has changed since it was taken."""
+    when there is none or the kernel's source file has changed since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -75,7 +76,7 @@ def measured_traffic(workload: str, kernel: str):
         return None
     for ent in entries:
         if ent.get("workload") == workload and ent.get("kernel") == kernel:
-            if ent.get("gemm_source_sha256") != gemm_source_sha():
+            if ent.get("source_sha256") != source_sha(ent.get("source", "gemm.hip")):
                 return None
             return float(ent["fetch_bytes"]) + float(ent["write_bytes"])
     return None
@@ -149,6 +150,8 @@ def main():
                      dropless=w.dropless)
     if a.backward:
         out = bench_training(a, w, inputs, cfg)
+        if a.copy_calibration_mb > 0:
+            out["copy_calibration_bytes"] = calibration_copy(a.copy_calibration_mb)
         if not a.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(w, inputs, a.cpu_seconds, backward=True)
         print(json.dumps(out), flush=True)
@@ -274,17 +277,23 @@ def main():
         "wall_s": wall,
     }
     if a.copy_calibration_mb > 0:
-        n = a.copy_calibration_mb << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = n
+        out["copy_calibration_bytes"] = calibration_copy(a.copy_calibration_mb)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, a.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def calibration_copy(mib: int) -> int:
+    """One plain device copy of `mib` MiB: the reference kernel of known size
+    for the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 def probe_C(cfg):

@@ -47,18 +47,44 @@ constexpr int STAGE = (BM + BN) * RS;
 constexpr int EPS = WNT * 2 + 8;             // epilogue staging row (bytes)
 static_assert(NTH / 64 * WM * EPS <= 2 * STAGE, "epilogue staging fits LDS");
 
-// 8 K-rows x 4 bf16 columns -> 4 columns x 8 K values (one 16-byte LDS row
-// chunk each).
-__device__ __forceinline__ void transpose8x4(const uint2 (&v)[8], u32x4_t (&o)[4]) {
+// One column of 8 K-rows x 4 bf16 columns as 8 K values (a 16-byte LDS row
+// chunk): column col of v[r] is half (col & 1) of word (col >> 1).
+__device__ __forceinline__ u32x4_t column8(const uint2 (&v)[8], bool hi_word, uint32_t sel) {
+    u32x4_t o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint2 a = v[2 * q], b = v[2 * q + 1];
-        o[0][q] = (a.x & 0xffffu) | (b.x << 16);
-        o[1][q] = (a.x >> 16) | (b.x & 0xffff0000u);
-        o[2][q] = (a.y & 0xffffu) | (b.y << 16);
-        o[3][q] = (a.y >> 16) | (b.y & 0xffff0000u);
+        const uint32_t a = hi_word ? v[2 * q].y : v[2 * q].x;
+        const uint32_t b = hi_word ? v[2 * q + 1].y : v[2 * q + 1].x;
+        o[q] = __builtin_amdgcn_perm(b, a, sel);  // low half: K-row 2q, high: 2q+1
     }
+    return o;
 }
+
+// K-major operand store: lane l holds columns 4l..4l+3 of 8 K-rows and writes
+// each column as a 16-byte chunk of LDS row 4l + col.  Rows 4 apart are 576
+// bytes apart, a multiple of the bank width, so writing column c in every
+// lane at once would put 16 lanes on the same banks.  Store c instead writes
+// column (c + l/4) % 4: the 64 lanes then spread evenly over the banks (four
+// per 16-byte bank group, the minimum for a 1 KiB store).
+struct KMajorStore {
+    int off[4];        // LDS byte offset of store c (row and K chunk)
+    uint32_t sel[4];   // byte selector of the column's half
+    bool hi[4];        // column in the upper word
+    __device__ KMajorStore(int lane, int wave, int rs) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int col = (c + (lane >> 2)) & 3;
+            off[c] = (4 * lane + col) * rs + wave * 16;
+            sel[c] = (col & 1) ? 0x07060302u : 0x05040100u;
+            hi[c] = (col >> 1) != 0;
+        }
+    }
+    __device__ __forceinline__ void store(char* base, const uint2 (&v)[8]) const {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<u32x4_t*>(base + off[c]) = column8(v, hi[c], sel[c]);
+    }
+};
 
 template <bool WGRAD, bool MASK>
 __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
@@ -80,7 +106,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
     // K-contiguous loader (dgrad A): row tid/8 + 64*i, 16-byte chunk tid%8
     const int r_off = (tid >> 3) * RS + (tid & 7) * 16;
     // K-major loader: K-rows 8*wave .. 8*wave+7, columns 4*lane .. 4*lane+3
-    const int t_off = (4 * lane) * RS + wave * 16;
+    const KMajorStore kst(lane, wave, RS);
 
     if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
     for (;;) {
@@ -148,20 +174,14 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
         };
         auto sstore = [&](int buf) {
             char* st = smem + buf * STAGE;
-            u32x4_t o[4];
             if constexpr (WGRAD) {
-                transpose8x4(va, o);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(st + t_off + c * RS) = o[c];
+                kst.store(st, va);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<u32x4_t*>(st + r_off + i * 64 * RS) = ra[i];
             }
-            transpose8x4(vb, o);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                *reinterpret_cast<u32x4_t*>(st + BOFF + t_off + c * RS) = o[c];
+            kst.store(st + BOFF, vb);
         };
 
         // ---------------------------------------------------------- k-loop
