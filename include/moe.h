@@ -238,8 +238,8 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
  * on `stream` between the steps (NULL entries skipped). */
 #define MOE_NUM_BWD_EVENTS 9 /* [0] start, [1] after occupancy / m-tile lists /
     inverse map / dispatched rows, [2] after the hidden-activation recompute, [3] after the combine
-    and router backward and db2, [4] after dW2, [5] after dU, [6] after dW1,
-    [7] after the expert-side input gradient, [8] after db1, dx, dWg, dbg */
+    and router backward, [4] after dW2 and db2, [5] after dU, [6] after dW1
+    and db1, [7] after the expert-side input gradient, [8] after dx, dWg, dbg */
 moe_status moe_backward_workspace_bytes(const moe_config *cfg, size_t *bytes);
 moe_status moe_layer_backward(const moe_config *cfg, const void *x, const float *w_gate,
                               const void *w1, const void *b1, const void *w2,

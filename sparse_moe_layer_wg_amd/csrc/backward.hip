@@ -115,47 +115,6 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     }
 }
 
-// out[e, n] = sum of v over expert e's rows; block = (expert, 512 columns),
-// 4 waves split the rows, partial sums combined in a fixed order.
-__global__ __launch_bounds__(256) void segment_colsum_kernel(const bf16_t* __restrict__ v,
-                                                             const int32_t* __restrict__ occ,
-                                                             const int32_t* __restrict__ row0,
-                                                             int C, int N,
-                                                             bf16_t* __restrict__ out) {
-    __shared__ float part[4][512];
-    const int e = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int n = blockIdx.x * 512 + lane * 8;
-    const int M = occ[e];
-    const int64_t base = row0 ? (int64_t)row0[e] : (int64_t)e * C;
-    float acc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-    if (n < N) {
-        for (int m = wave; m < M; m += 4) {
-            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(v + (base + m) * N + n);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                acc[2 * c] += __uint_as_float(x[c] << 16);
-                acc[2 * c + 1] += __uint_as_float(x[c] & 0xffff0000u);
-            }
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) part[wave][lane * 8 + c] = acc[c];
-    __syncthreads();
-    const int i = threadIdx.x * 2;  // 256 threads x 2 columns
-    if (blockIdx.x * 512 + i < N) {
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            s0 += part[w][i];
-            s1 += part[w][i + 1];
-        }
-        *reinterpret_cast<uint32_t*>(out + (int64_t)e * N + blockIdx.x * 512 + i) =
-            pack_bf16x2(s0, s1);
-    }
-}
-
 // fp32 GEMM for the router side, 64x64 tiles, 4x4 results per thread, k-steps
 // of 16 staged in LDS as [k][row].
 //   DX:  C[s, i] = sum_j dl[s, j] wg[j, i]  (+ the token's dX rows, bf16 out)
@@ -318,15 +277,6 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
     if (S == 0) return hipSuccess;
     router_bwd_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
         logits, topk_idx, topk_w, dw, counts, g_aux, g_z, dl, S, E, k);
-    return hipGetLastError();
-}
-
-hipError_t launch_segment_colsum(const void* v, const int32_t* occ, const int32_t* row0, int E,
-                                 int C, int N, void* out, hipStream_t st) {
-    if (E == 0 || N == 0) return hipSuccess;
-    dim3 grid((unsigned)ceil_div(N, 512), (unsigned)E);
-    segment_colsum_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(v), occ, row0, C, N,
-                                                static_cast<bf16_t*>(out));
     return hipGetLastError();
 }
 

@@ -86,9 +86,46 @@ struct KMajorStore {
     }
 };
 
+// One output tile: expert, origin, rows (M), k-tiles and the expert's
+// first row; ca/cb: this lane's first column of the K-major pieces (clamped
+// into range; clamped columns are never stored).
+struct BwdTile {
+    int e, m0, n0, M, KT, Keff, ca, cb;
+    size_t row_e;
+};
+
+template <bool WGRAD>
+__device__ __forceinline__ BwdTile decode_tile(const BwdGemmParams& p, int t, int MT, int NT,
+                                               int lane) {
+    BwdTile u;
+    if constexpr (WGRAD) {
+        u.e = t / (MT * NT);
+        const int r = t - u.e * MT * NT;
+        u.m0 = (r / NT) * BM;
+        u.n0 = (r % NT) * BN;
+        u.M = p.M;
+        u.Keff = __builtin_amdgcn_readfirstlane(p.occ[u.e]);
+        u.KT = (u.Keff + BK - 1) / BK;
+    } else {
+        const int q = t / NT;
+        u.e = __builtin_amdgcn_readfirstlane(p.mt_expert[q]);
+        const int mt0 = __builtin_amdgcn_readfirstlane(p.mt_start[u.e]);
+        u.m0 = (q - mt0) * BM;
+        u.n0 = (t - q * NT) * BN;
+        u.M = __builtin_amdgcn_readfirstlane(p.occ[u.e]);
+        u.Keff = p.K;
+        u.KT = p.K / BK;
+    }
+    u.row_e = p.row0 ? (size_t)__builtin_amdgcn_readfirstlane(p.row0[u.e]) : (size_t)u.e * p.C;
+    u.ca = WGRAD ? min(u.m0 + 4 * lane, u.M - 4) : 0;
+    u.cb = min(u.n0 + 4 * lane, p.N - 4);
+    return u;
+}
+
 template <bool WGRAD, bool MASK>
 __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ float s_bias[WGRAD ? NTH / 64 : 1][WGRAD ? BM : 1];
     __shared__ int s_next;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / 4, wn = wave % 4;
@@ -107,81 +144,80 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
     const int r_off = (tid >> 3) * RS + (tid & 7) * 16;
     // K-major loader: K-rows 8*wave .. 8*wave+7, columns 4*lane .. 4*lane+3
     const KMajorStore kst(lane, wave, RS);
+    const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
+    const bf16_t* __restrict__ B = static_cast<const bf16_t*>(p.B);
 
-    if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
-    for (;;) {
-        __syncthreads();
-        const int t = __builtin_amdgcn_readfirstlane(s_next);
-        if (t >= t_end) break;
-        int e, m0, n0, M, KT, Keff;
+    u32x4_t ra[4];       // dgrad A: 4 K-contiguous 16-byte chunks
+    uint2 va[8], vb[8];  // K-major operands: 8 K-rows x 4 columns
+    auto gload = [&](const BwdTile& u, int kt) {
+        const int kb = kt * BK;
         if constexpr (WGRAD) {
-            e = t / (MT * NT);
-            const int r = t - e * MT * NT;
-            m0 = (r / NT) * BM;
-            n0 = (r % NT) * BN;
-            M = p.M;
-            Keff = __builtin_amdgcn_readfirstlane(p.occ[e]);
-            KT = (Keff + BK - 1) / BK;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int k = kb + 8 * wave + r;
+                va[r] = make_uint2(0u, 0u);
+                vb[r] = make_uint2(0u, 0u);
+                if (k < u.Keff) {
+                    const size_t ar = u.row_e + k;
+                    const size_t br = p.b_rows ? (size_t)p.b_rows[ar] : ar;
+                    va[r] = *reinterpret_cast<const uint2*>(A + ar * u.M + u.ca);
+                    vb[r] = *reinterpret_cast<const uint2*>(B + br * N + u.cb);
+                }
+            }
         } else {
-            const int q = t / NT;
-            e = __builtin_amdgcn_readfirstlane(p.mt_expert[q]);
-            const int mt0 = __builtin_amdgcn_readfirstlane(p.mt_start[e]);
-            m0 = (q - mt0) * BM;
-            n0 = (t - q * NT) * BN;
-            M = __builtin_amdgcn_readfirstlane(p.occ[e]);
-            Keff = p.K;
-            KT = p.K / BK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rg = min(u.m0 + (tid >> 3) + 64 * i, u.M - 1);
+                ra[i] = *reinterpret_cast<const u32x4_t*>(A + (u.row_e + rg) * p.K + kb +
+                                                          (tid & 7) * 8);
+            }
+            const bf16_t* W = B + (size_t)u.e * p.K * N;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                vb[r] = *reinterpret_cast<const uint2*>(W + (size_t)(kb + 8 * wave + r) * N + u.cb);
         }
-        const size_t row_e = p.row0 ? (size_t)__builtin_amdgcn_readfirstlane(p.row0[e])
-                                    : (size_t)e * p.C;
-        const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
-        const bf16_t* __restrict__ B = static_cast<const bf16_t*>(p.B);
+    };
+    auto sstore = [&](int buf) {
+        char* st = smem + buf * STAGE;
+        if constexpr (WGRAD) {
+            kst.store(st, va);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4_t*>(st + r_off + i * 64 * RS) = ra[i];
+        }
+        kst.store(st + BOFF, vb);
+    };
 
-        // ---------------------------------------------------------- loads
-        u32x4_t ra[4];       // dgrad A: 4 K-contiguous 16-byte chunks
-        uint2 va[8], vb[8];  // K-major operands: 8 K-rows x 4 columns
-        // column offsets of this lane's K-major pieces (clamped into range;
-        // clamped columns are never stored)
-        const int ca = WGRAD ? min(m0 + 4 * lane, M - 4) : 0;
-        const int cb = min(n0 + 4 * lane, N - 4);
-        auto gload = [&](int kt) {
-            const int kb = kt * BK;
-            if constexpr (WGRAD) {
+    // Tiles of this XCD's chunk come from an atomic counter.  The tile after
+    // the current one is claimed when the current one starts, so that the
+    // loads of its first k-tile can be issued before the current epilogue
+    // (a weight-gradient tile has only occ/64 k-tiles: its first load and its
+    // epilogue would otherwise both sit exposed).
+    if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
+    __syncthreads();
+    int t = __builtin_amdgcn_readfirstlane(s_next);
+    BwdTile cur{};
+    if (t < t_end) {
+        cur = decode_tile<WGRAD>(p, t, MT, NT, lane);
+        if (cur.KT > 0) gload(cur, 0);
+    }
+    while (t < t_end) {
+        __syncthreads();   // the previous epilogue's LDS reads are done
+        if (tid == 0) s_next = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
+        // bias gradient (weight gradients, first n-tile): column sums of A
+        const bool bias = WGRAD && p.bias_grad && cur.n0 == 0;
+        float csum[4] = {0.f, 0.f, 0.f, 0.f};
+        auto add_bias = [&]() {
+            if (bias) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    const int k = kb + 8 * wave + r;
-                    va[r] = make_uint2(0u, 0u);
-                    vb[r] = make_uint2(0u, 0u);
-                    if (k < Keff) {
-                        const size_t ar = row_e + k;
-                        const size_t br = p.b_rows ? (size_t)p.b_rows[ar] : ar;
-                        va[r] = *reinterpret_cast<const uint2*>(A + ar * M + ca);
-                        vb[r] = *reinterpret_cast<const uint2*>(B + br * N + cb);
-                    }
+                    csum[0] += __uint_as_float(va[r].x << 16);
+                    csum[1] += __uint_as_float(va[r].x & 0xffff0000u);
+                    csum[2] += __uint_as_float(va[r].y << 16);
+                    csum[3] += __uint_as_float(va[r].y & 0xffff0000u);
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rg = min(m0 + (tid >> 3) + 64 * i, M - 1);
-                    ra[i] = *reinterpret_cast<const u32x4_t*>(A + (row_e + rg) * p.K + kb +
-                                                              (tid & 7) * 8);
-                }
-                const bf16_t* W = B + (size_t)e * p.K * N;
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    vb[r] = *reinterpret_cast<const uint2*>(W + (size_t)(kb + 8 * wave + r) * N + cb);
             }
-        };
-        auto sstore = [&](int buf) {
-            char* st = smem + buf * STAGE;
-            if constexpr (WGRAD) {
-                kst.store(st, va);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<u32x4_t*>(st + r_off + i * 64 * RS) = ra[i];
-            }
-            kst.store(st + BOFF, vb);
         };
 
         // ---------------------------------------------------------- k-loop
@@ -192,14 +228,14 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-        if (KT > 0) {
-            gload(0);
+        if (cur.KT > 0) {
+            add_bias();
             sstore(0);
-            __syncthreads();
         }
-        for (int kt = 0; kt < KT; ++kt) {
-            const bool more = kt + 1 < KT;
-            if (more) gload(kt + 1);
+        __syncthreads();   // stage 0 filled; s_next visible to every wave
+        for (int kt = 0; kt < cur.KT; ++kt) {
+            const bool more = kt + 1 < cur.KT;
+            if (more) gload(cur, kt + 1);
             const char* st = smem + (kt & 1) * STAGE;
 #pragma unroll
             for (int ks = 0; ks < BK / 16; ++ks) {
@@ -217,16 +253,30 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                         acc[i][j] =
                             __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
             }
-            if (more) sstore((kt + 1) & 1);
+            if (more) {
+                add_bias();
+                sstore((kt + 1) & 1);
+            }
             __syncthreads();
         }
 
-        int nx = 0;
-        if (tid == 0) nx = xcd * per + atomicAdd(&p.tile_ctr[xcd], 1);
+        // next tile: decode it and start loading its first k-tile
+        const int tn = __builtin_amdgcn_readfirstlane(s_next);
+        BwdTile nxt{};
+        if (tn < t_end) {
+            nxt = decode_tile<WGRAD>(p, tn, MT, NT, lane);
+            if (nxt.KT > 0) gload(nxt, 0);
+        }
+
         // ---------------------------------------------------------- epilogue
         // Accumulator block (n x m): lane l holds row m = l%32, register r
         // column n = 8*(r/4) + 4*(l/32) + r%4.  Rounded to bf16, staged per
         // wave in LDS, stored as 16-byte row chunks.
+        if (bias) {
+            // column sums: each wave covered its 8 of every 64 K-rows
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s_bias[wave][4 * lane + c] = csum[c];
+        }
         char* ep = smem + wave * (WM * EPS);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -240,21 +290,20 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                         make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]),
                                    pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
                 }
-        if (tid == 0) s_next = nx;
         __builtin_amdgcn_wave_barrier();
         constexpr int CPR = WNT * 2 / 16;   // 16-byte chunks per staged row
         constexpr int NIT = WM * CPR / 64;  // chunks per lane
-        const int nw = n0 + wn * WNT;
+        const int nw = cur.n0 + wn * WNT;
         bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) +
-                                    (WGRAD ? (size_t)e * p.M * N : row_e * N);
-        const bf16_t* __restrict__ mk = MASK ? static_cast<const bf16_t*>(p.mask) + row_e * N
+                                    (WGRAD ? (size_t)cur.e * p.M * N : cur.row_e * N);
+        const bf16_t* __restrict__ mk = MASK ? static_cast<const bf16_t*>(p.mask) + cur.row_e * N
                                              : nullptr;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
-            const int m = m0 + wm * WM + row, n = nw + ch * 8;
+            const int m = cur.m0 + wm * WM + row, n = nw + ch * 8;
             u32x4_t ov = *reinterpret_cast<const u32x4_t*>(ep + row * EPS + ch * 16);
-            if (m < M && n < N) {
+            if (m < cur.M && n < N) {
                 if constexpr (MASK) {
                     // dReLU: keep the gradient where the forward's hidden
                     // value is positive (bf16 > 0: sign clear, not zero)
@@ -271,6 +320,18 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                 *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = ov;
             }
         }
+        if (bias) {
+            __syncthreads();
+            if (tid < BM && cur.m0 + tid < cur.M) {
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < NTH / 64; ++w) v += s_bias[w][tid];
+                static_cast<bf16_t*>(p.bias_grad)[(size_t)cur.e * cur.M + cur.m0 + tid] =
+                    f32_to_bf16(v);
+            }
+        }
+        t = tn;
+        cur = nxt;
     }  // tile loop
 }
 

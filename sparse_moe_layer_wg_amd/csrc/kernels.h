@@ -145,6 +145,8 @@ struct BwdGemmParams {
     const int32_t* mt_expert;  // ... and the expert of each m-tile
     const int32_t* row0;       // NULL (row e*C) or [E]
     const int32_t* b_rows;     // wgrad: NULL or [rows] token row of each row
+    void* bias_grad;           // wgrad: NULL, or [E, M] column sums of A over
+                               // the expert's rows (the bias gradient)
     int32_t* tile_ctr;         // 8 counters, zero at launch
     int E, C, M, N, K;
     size_t rows;               // rows of the expert buffers (E*C or S*k)
@@ -167,10 +169,6 @@ hipError_t launch_combine_bwd(const void* dy, const void* out, const int32_t* to
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                              const float* dw, const int32_t* counts, float g_aux, float g_z,
                              float* dl, int S, int E, int k, hipStream_t st);
-// out[e, n] = sum over rows r of expert e of v[r, n] (bf16 in, fp32 sums,
-// bf16 out).
-hipError_t launch_segment_colsum(const void* v, const int32_t* occ, const int32_t* row0, int E,
-                                 int C, int N, void* out, hipStream_t st);
 // Router-side fp32 GEMMs:
 //   dx[s, i] = bf16(sum_j dl[s, j] wg[j, i] + sum over kept r of dX[u(s,r), i])
 //   dwg[j, i] = sum_s dl[s, j] x[s, i];  dbg[j] = sum_s dl[s, j]

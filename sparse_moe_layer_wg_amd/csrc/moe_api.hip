@@ -565,7 +565,6 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
                                limit, stream));
     MOE_TRY(launch_router_bwd(logits, topk_idx, topk_w, dwk, counts, g_aux, g_z, dl, p.S, p.E, p.k,
                               stream));
-    if (db2) MOE_TRY(launch_segment_colsum(G, occ, row0, p.E, p.C, p.d, db2, stream));
     record(ev, 3, stream);
 
     BwdGemmParams b{};
@@ -574,10 +573,12 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.E = p.E;
     b.C = p.C;
     b.rows = p.rows;
-    // dW2 = dO^T H (reads H before dgrad 2 overwrites it)
+    // dW2 = dO^T H (reads H before dgrad 2 overwrites it); db2 = column
+    // sums of dO in the same pass
     b.A = G;
     b.B = H;
     b.b_rows = nullptr;
+    b.bias_grad = db2;
     b.Cout = dw2;
     b.M = p.d;
     b.N = p.h;
@@ -590,16 +591,18 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.A = G;
     b.B = w2;
     b.mask = H;
+    b.bias_grad = nullptr;
     b.Cout = H;
     b.N = p.h;
     b.K = p.d;
     b.tile_ctr = ctr + 16;
     MOE_TRY(launch_bwd_gemm(b, false, true, stream));
     record(ev, 5, stream);
-    // dW1 = dU^T X
+    // dW1 = dU^T X; db1 = column sums of dU
     b.A = H;
     b.B = X;
     b.b_rows = nullptr;
+    b.bias_grad = db1;
     b.mask = nullptr;
     b.Cout = dw1;
     b.M = p.h;
@@ -611,6 +614,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.A = H;
     b.B = w1;
     b.b_rows = nullptr;
+    b.bias_grad = nullptr;
     b.Cout = G;
     b.N = p.d;
     b.K = p.h;
@@ -618,9 +622,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     MOE_TRY(launch_bwd_gemm(b, false, false, stream));
     record(ev, 7, stream);
 
-    // db1 (dU stays in H's buffer); dx = dispatch backward + dl Wg;
-    // dWg = dl^T x; dbg = colsum dl
-    if (db1) MOE_TRY(launch_segment_colsum(H, occ, row0, p.E, p.C, p.h, db1, stream));
+    // dx = dispatch backward + dl Wg; dWg = dl^T x; dbg = colsum dl
     MOE_TRY(launch_router_dx(dl, w_gate, G, topk_idx, slot, dx, p.S, p.d, p.E, p.k, stride, limit,
                              stream));
     MOE_TRY(launch_router_dw(dl, x, dw_gate, db_gate, p.S, p.d, p.E, at<void>(ws, cv.rpart),
