@@ -34,6 +34,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -92,6 +94,8 @@ struct KMajorStore {
 struct BwdTile {
     int e, m0, n0, M, KT, Keff, ca, cb;
     size_t row_e;
+    uint32_t aoff[4];  // dgrad: byte offsets of this thread's A chunks from
+                       // the expert's first row (rows clamped to the filled ones)
 };
 
 template <bool WGRAD>
@@ -119,6 +123,14 @@ __device__ __forceinline__ BwdTile decode_tile(const BwdGemmParams& p, int t, in
     u.row_e = p.row0 ? (size_t)__builtin_amdgcn_readfirstlane(p.row0[u.e]) : (size_t)u.e * p.C;
     u.ca = WGRAD ? min(u.m0 + 4 * lane, u.M - 4) : 0;
     u.cb = min(u.n0 + 4 * lane, p.N - 4);
+    if constexpr (!WGRAD) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rg = min(u.m0 + (tid >> 3) + 64 * i, u.M - 1);
+            u.aoff[i] = (uint32_t)rg * (uint32_t)p.K * 2u + (uint32_t)(tid & 7) * 16u;
+        }
+    }
     return u;
 }
 
@@ -127,7 +139,8 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
     __shared__ float s_bias[WGRAD ? NTH / 64 : 1][WGRAD ? BM : 1];
     __shared__ int s_next;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / 4, wn = wave % 4;
     const int frow = lane & 31, fhalf = lane >> 5;
     const int N = p.N;
@@ -144,14 +157,18 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
     const int r_off = (tid >> 3) * RS + (tid & 7) * 16;
     // K-major loader: K-rows 8*wave .. 8*wave+7, columns 4*lane .. 4*lane+3
     const KMajorStore kst(lane, wave, RS);
-    const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
-    const bf16_t* __restrict__ B = static_cast<const bf16_t*>(p.B);
-
     u32x4_t ra[4];       // dgrad A: 4 K-contiguous 16-byte chunks
     uint2 va[8], vb[8];  // K-major operands: 8 K-rows x 4 columns
+    // Loads address a wave-uniform row base (scalar registers) plus a 32-bit
+    // per-lane byte offset, so that each K-row costs no vector registers.
+    const char* __restrict__ Ac = reinterpret_cast<const char*>(p.A);
+    const char* __restrict__ Bc = reinterpret_cast<const char*>(p.B);
     auto gload = [&](const BwdTile& u, int kt) {
         const int kb = kt * BK;
         if constexpr (WGRAD) {
+            // rows past the occupancy load as zero
+            const bf16_t* __restrict__ Ab = reinterpret_cast<const bf16_t*>(Ac);
+            const bf16_t* __restrict__ Bb = reinterpret_cast<const bf16_t*>(Bc);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int k = kb + 8 * wave + r;
@@ -160,21 +177,20 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                 if (k < u.Keff) {
                     const size_t ar = u.row_e + k;
                     const size_t br = p.b_rows ? (size_t)p.b_rows[ar] : ar;
-                    va[r] = *reinterpret_cast<const uint2*>(A + ar * u.M + u.ca);
-                    vb[r] = *reinterpret_cast<const uint2*>(B + br * N + u.cb);
+                    va[r] = *reinterpret_cast<const uint2*>(Ab + ar * u.M + u.ca);
+                    vb[r] = *reinterpret_cast<const uint2*>(Bb + br * N + u.cb);
                 }
             }
         } else {
+            const char* Ak = Ac + (u.row_e * p.K + kb) * 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rg = min(u.m0 + (tid >> 3) + 64 * i, u.M - 1);
-                ra[i] = *reinterpret_cast<const u32x4_t*>(A + (u.row_e + rg) * p.K + kb +
-                                                          (tid & 7) * 8);
-            }
-            const bf16_t* W = B + (size_t)u.e * p.K * N;
+            for (int i = 0; i < 4; ++i)
+                ra[i] = *reinterpret_cast<const u32x4_t*>(Ak + u.aoff[i]);
+            const char* Wk = Bc + ((size_t)u.e * p.K + kb + 8 * wave) * N * 2;
+            const uint32_t ob = (uint32_t)u.cb * 2u;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                vb[r] = *reinterpret_cast<const uint2*>(W + (size_t)(kb + 8 * wave + r) * N + u.cb);
+                vb[r] = *reinterpret_cast<const uint2*>(Wk + (size_t)r * N * 2 + ob);
         }
     };
     auto sstore = [&](int buf) {
@@ -233,31 +249,101 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
             sstore(0);
         }
         __syncthreads();   // stage 0 filled; s_next visible to every wave
-        for (int kt = 0; kt < cur.KT; ++kt) {
-            const bool more = kt + 1 < cur.KT;
-            if (more) gload(cur, kt + 1);
+
+        // One k-tile from LDS buffer kt&1, as in the forward kernel: with
+        // REFILL, k-tile kt+1 is loaded into registers during the first
+        // 16-wide step and transposed into the other buffer during the last;
+        // the fragments of step ks+1 are read while the MFMAs of step ks run.
+        // Instruction groups keep memory and VALU work spread over the MFMAs
+        // (a wave issues in order).
+        bf16x8_t fa[2][TM], fb[2][TN];
+        auto load_frags = [&](const char* st, int ks, int slot) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(st + fa_off + i * 32 * RS + ks * 32);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(st + fb_off + j * 32 * RS + ks * 32);
+        };
+        auto ktile = [&](auto refill_tag, int kt) {
+            constexpr bool REFILL = decltype(refill_tag)::value;
+            constexpr int KS = BK / 16;
+            constexpr int NL = WGRAD ? 16 : 12;    // global loads per thread
+            constexpr int NW = WGRAD ? 8 : 8;      // LDS stores per thread
+            constexpr int NF = TM + TN;            // fragment reads per step
+            constexpr int NM = TM * TN;            // MFMAs per step
             const char* st = smem + (kt & 1) * STAGE;
+            load_frags(st, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                bf16x8_t fa[TM], fb[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    fa[i] = *reinterpret_cast<const bf16x8_t*>(st + fa_off + i * 32 * RS + ks * 32);
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    fb[j] = *reinterpret_cast<const bf16x8_t*>(st + fb_off + j * 32 * RS + ks * 32);
+            for (int ks = 0; ks < KS; ++ks) {
+                if constexpr (REFILL) {
+                    if (ks == 0) gload(cur, kt + 1);
+                    if (ks == KS - 1) {
+                        add_bias();
+                        sstore((kt + 1) & 1);
+                    }
+                }
+                if (ks + 1 < KS) load_frags(st, ks + 1, (ks + 1) & 1);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] =
-                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-            }
-            if (more) {
-                add_bias();
-                sstore((kt + 1) & 1);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+                if (REFILL && ks == 0) {
+#pragma unroll
+                    for (int g = 0; g < NM; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x020, NL / NM, 0);  // VMEM read
+                        if (g < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                    }
+                } else if (REFILL && ks == KS - 1) {
+#pragma unroll
+                    for (int g = 0; g < NM; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);      // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x200, NW / NM, 0); // LDS write
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                    }
+                } else if (ks + 1 < KS) {
+#pragma unroll
+                    for (int g = 0; g < NF; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, NM / NF, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
+        };
+        if constexpr (WGRAD) {
+            // A weight-gradient tile runs only occ/64 k-tiles; there the plain
+            // loop (loads first, transposes and stores after the MFMAs) measured
+            // faster than the interleaved one.
+            for (int kt = 0; kt < cur.KT; ++kt) {
+                const bool more = kt + 1 < cur.KT;
+                if (more) gload(cur, kt + 1);
+                const char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+                for (int ks = 0; ks < BK / 16; ++ks) {
+                    load_frags(st, ks, 0);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+                }
+                if (more) {
+                    add_bias();
+                    sstore((kt + 1) & 1);
+                }
+                __syncthreads();
+            }
+        } else {
+            int kt = 0;
+            for (; kt + 1 < cur.KT; ++kt) ktile(std::true_type{}, kt);
+            if (kt < cur.KT) ktile(std::false_type{}, kt);
         }
 
         // next tile: decode it and start loading its first k-tile
