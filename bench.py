@@ -47,6 +47,8 @@ def parse():
                     help="no capacity limit: compact [S*k,d] expert segments, no drops")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: forward + moe_layer_backward")
+    ap.add_argument("--ep-share", default=None, choices=list(mw.EP_SHARES),
+                    help="time the expert FFN at one GPU's expert-parallel share instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -142,6 +144,9 @@ def main():
               f"(the layer has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.ep_share:
+        print(json.dumps(bench_ep_share(a, mw.EP_SHARES[a.ep_share])), flush=True)
+        return
     w = mw.get(a.workload)
     if a.dropless:
         w = w.with_(dropless=True, name=w.name + "_dropless")
@@ -298,6 +303,96 @@ def calibration_copy(mib: int) -> int:
 
 def probe_C(cfg):
     return moe.capacity(cfg)
+
+
+def bench_ep_share(a, sh) -> dict:
+    """One step = moe_expert_ffn over the rows one GPU of an expert-parallel
+    layer receives (compact expert segments, as the dispatch all-to-all would
+    deliver them): both expert GEMMs over E_local experts."""
+    counts = mw.ep_share_counts(sh)
+    rows = int(counts.sum())
+    inp = mw.generate_ep_share(sh, rows, "cuda")
+    cfg = moe.config(rows, sh.d, sh.h, sh.E_local, 1, dtype="bf16", dropless=True)
+    out = torch.empty((rows, sh.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    cnt = torch.from_numpy(counts[None, :].astype(np.int32)).cuda()
+
+    def step():
+        moe.expert_ffn(cfg, inp["xd"], cnt, inp["w1"], None, inp["w2"], None, out, ws)
+
+    for _ in range(a.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(a.steps):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / a.steps
+    ffn_us = float(np.mean([b.elapsed_time(e) * 1000.0 for b, e in evs]))
+    flops = 2 * 2.0 * rows * sh.d * sh.h
+    by = 2 * sh.E_local * sh.d * sh.h * 2 + rows * (2 * sh.d + 2 * sh.h) * 2
+    t = ffn_us * 1e-6
+    if by / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_PEAK_TFLOPS["bf16"] * 1e12):
+        roof = {"bound": "hbm", "achieved": by / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "expert_gemm1+expert_gemm2 (one moe_expert_ffn call)"
+    roof["algorithmic_flops"] = flops
+    roof["algorithmic_bytes"] = by
+    roof["avg_launch_us"] = ffn_us
+    out_d = {
+        "metric": "expert-FFN rows/s on one GPU's expert-parallel share",
+        "value": rows / (ms / 1000.0),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": sh.name, "sources": sh.sources, "tokens_per_source": sh.S,
+                   "E_total": sh.E_total, "k": sh.k, "E_local": sh.E_local, "d_model": sh.d,
+                   "d_ff": sh.h, "rows": rows, "seed": sh.seed},
+        "roofline": roof,
+        "wall_s": wall,
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        w1h, w2h = mw.to_numpy(inp["w1"]), mw.to_numpy(inp["w2"])
+        seg = np.concatenate([[0], np.cumsum(counts)[:-1]])
+
+        def run(m):   # the first m rows of every local expert
+            idx = (seg[:, None] + np.arange(m)[None, :]).reshape(-1)
+            xs = mw.to_numpy(inp["xd"][torch.from_numpy(idx).cuda()]).reshape(sh.E_local, m, sh.d)
+            t_0 = time.perf_counter()
+            oracle.expert_ffn(xs, np.full(sh.E_local, m, np.int32), w1h, None, w2h, None)
+            return time.perf_counter() - t_0
+        m0 = 2
+        t_m0 = run(m0)
+        m = int(min(counts.min(), max(m0, m0 * a.cpu_seconds / max(t_m0, 1e-3))))
+        tc = run(m) if m != m0 else t_m0
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        out_d["cpu_baseline"] = {"value": sh.E_local * m / tc, "unit": "rows/s",
+                                 "cores": threads, "kind": "oracle",
+                                 "sample": f"the first {m} rows of each of the {sh.E_local} local "
+                                           f"experts through the fp64 oracle FFN, {tc:.1f} s"}
+    return out_d
 
 
 BWD_STAGES = ["setup", "recompute_h", "combine_router_bwd", "wgrad2", "dgrad2", "wgrad1",

@@ -117,6 +117,60 @@ def generate(w: Workload, device="cpu") -> dict:
     return dict(x=x, wg=wg, bg=bg, w1=w1, b1=b1, w2=w2, b2=b2)
 
 
+@dataclasses.dataclass(frozen=True)
+class EPShare:
+    """One GPU's share of an expert-parallel layer: `sources` GPUs of S tokens
+    each route k of E_total experts; this GPU holds experts 0..E_local-1 and
+    receives every row routed to them."""
+    name: str
+    sources: int
+    S: int
+    E_total: int
+    k: int
+    E_local: int
+    d: int
+    h: int
+    seed: int
+
+
+# DeepSeek-R1-shaped layout: 256 routed experts over 8 GPUs, 32 per GPU
+EP_SHARES = {
+    s.name: s
+    for s in [EPShare("deepseek_ep8_share", sources=8, S=8192, E_total=256, k=8, E_local=32,
+                      d=7168, h=2048, seed=5)]
+}
+
+
+def ep_share_counts(sh: EPShare):
+    """Rows each local expert receives (int64 [E_local]).  Every token of every
+    source picks k distinct experts uniformly at random (the balanced,
+    uniform-router case); no capacity limit."""
+    import numpy as np
+    rng = np.random.default_rng(sh.seed)
+    counts = np.zeros(sh.E_local, np.int64)
+    for _ in range(sh.sources):
+        u = rng.random((sh.S, sh.E_total), dtype=np.float32)
+        top = np.argpartition(u, -sh.k, axis=1)[:, -sh.k:]
+        counts += np.bincount(top.ravel(), minlength=sh.E_total)[:sh.E_local]
+    return counts
+
+
+def generate_ep_share(sh: EPShare, rows: int, device="cpu") -> dict:
+    """Received rows xd [rows, d] ~ N(0,1) and the local experts' weights
+    W1 [E_local,h,d] ~ N(0,1/d), W2 [E_local,d,h] ~ N(0,1/h), all bf16."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(sh.seed)
+    bf = torch.bfloat16
+    xd = torch.randn((rows, sh.d), generator=g, device=dev).to(bf)
+    w1 = torch.empty((sh.E_local, sh.h, sh.d), device=dev, dtype=bf)
+    w2 = torch.empty((sh.E_local, sh.d, sh.h), device=dev, dtype=bf)
+    for e in range(sh.E_local):
+        w1[e] = torch.randn((sh.h, sh.d), generator=g, device=dev).mul_(sh.d ** -0.5).to(bf)
+        w2[e] = torch.randn((sh.d, sh.h), generator=g, device=dev).mul_(sh.h ** -0.5).to(bf)
+    return dict(xd=xd, w1=w1, w2=w2)
+
+
 def to_numpy(t: torch.Tensor | None):
     """Host numpy view of a tensor; bf16 becomes its uint16 bit patterns."""
     if t is None:
