@@ -397,13 +397,15 @@ def bench_ep_share(a, sh) -> dict:
 
 BWD_STAGES = ["setup", "recompute_h", "combine_router_bwd", "wgrad2", "dgrad2", "wgrad1",
               "dgrad1", "router_dx_dw"]
-BWD_GEMMS = ("recompute_h", "wgrad2", "dgrad2", "wgrad1", "dgrad1")
+BWD_GEMMS = ("wgrad2", "dgrad2", "wgrad1", "dgrad1")   # H is saved: no recompute
 
 
 def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
-    """One step = moe_layer_forward (keeping the routing and expert outputs)
-    + moe_layer_backward of sum(dy*y) + 0.01*aux + 0.001*z."""
-    layer = MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False)
+    """One step = moe_layer_forward (keeping the routing, expert outputs and
+    hidden activations) + moe_layer_backward of sum(dy*y) + 0.01*aux +
+    0.001*z."""
+    # the forward keeps the expert hidden activations for the backward
+    layer = MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False, keep_hidden=True)
     x = inputs["x"]
     S, d, h, E = w.S, w.d, w.h, w.E
     dev, at = "cuda", w.torch_dtype
@@ -425,7 +427,7 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
                            layer.logits, layer.topk_idx, layer.topk_w, layer.slot, layer.counts,
                            layer.out, dy, gr["dx"], gr["dwg"], gr["dw1"], gr["dw2"], bws,
                            db_gate=gr["dbg"], db1=gr["db1"], db2=gr["db2"], g_aux=0.01,
-                           g_z=0.001, events=bwd_events)
+                           g_z=0.001, hidden=layer.hidden, events=bwd_events)
 
     def make_events():
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_BWD_EVENTS)]
@@ -495,7 +497,8 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "pass": "forward+backward", "S": S, "d_model": d,
+        "config": {"workload": w.name, "pass": "forward+backward", "hidden": "saved",
+                   "S": S, "d_model": d,
                    "d_ff": h, "E": E, "k": w.k,
                    "capacity_factor": None if w.dropless else w.capacity_factor,
                    "C": None if w.dropless else layer.C, "dropless": w.dropless,
@@ -503,7 +506,8 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
         "roofline": roof,
         "backward_ms": bwd_ms,
         "backward_stage_us": stage_us,
-        "backward_gemm_mfma_frac": 5 * flops / gemm_s / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),
+        "backward_gemm_mfma_frac": len(BWD_GEMMS) * flops / gemm_s /
+        (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),
         "routing": {"kept": kept, "nonempty_experts": nonempty},
         "wall_s": wall,
     }

@@ -188,8 +188,10 @@ moe_status moe_combine(const moe_config *cfg, const void *out, const int32_t *to
  * losses, enqueued back to back with no host synchronisation.
  * Required: x, w_gate, w1, w2, y, ws.  Optional (NULL = not wanted, kept in
  * ws): gate_bias, b1, b2, logits, topk_idx, topk_w, slot, counts, losses,
- * xd, out.  When xd and out are both NULL one workspace buffer serves as
- * both.  With bf16 activations, xd NULL and S*d*2 < 2^32 bytes, no dispatch
+ * xd, out, hidden.  When xd and out are both NULL one workspace buffer serves
+ * as both.  hidden [E,C,h] ([S*k,h] with MOE_CFG_DROPLESS), act dtype:
+ * receives the expert hidden activations ReLU(xd W1^T + b1) of the filled
+ * rows, which moe_layer_backward can then reuse instead of recomputing.  With bf16 activations, xd NULL and S*d*2 < 2^32 bytes, no dispatch
  * buffer is written at all: the first expert GEMM reads each slot's row
  * straight from x through an inverse slot map (same results bit for bit;
  * the dispatch stage then takes no time).  stage_events: NULL, or an array
@@ -201,8 +203,8 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
                              const void *w2, const void *b2, void *y, float *logits,
                              int32_t *topk_idx, float *topk_w, int32_t *slot,
                              int32_t *counts, float *losses, void *xd, void *out,
-                             void *ws, size_t ws_bytes, hipEvent_t *stage_events,
-                             hipStream_t stream);
+                             void *hidden, void *ws, size_t ws_bytes,
+                             hipEvent_t *stage_events, hipStream_t stream);
 
 /* ---------------------------------------------------------------- backward
  * The pages' setting is training: the layer is trained with its auxiliary
@@ -225,13 +227,15 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
  * MOE_ERR_UNSUPPORTED), in capacity and dropless modes.
  * In:  x, w_gate, w1, b1 (NULL = 0), w2 as given to the forward; the
  *      forward's outputs logits, topk_idx, topk_w, slot, counts and out
- *      (the expert outputs, [E,C,d] or [S*k,d]); dy [S,d] act; the loss
- *      weights g_aux and g_z (finite).
+ *      (the expert outputs, [E,C,d] or [S*k,d]); hidden: NULL (the hidden
+ *      activations are recomputed, one more expert GEMM) or the forward's
+ *      `hidden` output (read only); dy [S,d] act; the loss weights g_aux and
+ *      g_z (finite).
  * Out: dx [S,d] act, dw_gate [E,d] fp32, db_gate [E] fp32 (NULL = not
  *      wanted), dw1 [E,h,d] act, db1 [E,h] act (NULL = not wanted),
  *      dw2 [E,d,h] act, db2 [E,d] act (NULL = not wanted).
- * Precision: fp32 accumulation everywhere; the hidden activations are
- * recomputed (bf16, as in the forward), dO, du and the expert-side input
+ * Precision: fp32 accumulation everywhere; the hidden activations are the
+ * forward's (bf16, saved or recomputed bit-identically), dO, du and the expert-side input
  * gradient are rounded to bf16 once; the router side is fp32.
  * ws: at least moe_backward_workspace_bytes() bytes, 256-byte aligned.
  * stage_events: NULL, or MOE_NUM_BWD_EVENTS caller-created events recorded
@@ -245,8 +249,8 @@ moe_status moe_layer_backward(const moe_config *cfg, const void *x, const float 
                               const void *w1, const void *b1, const void *w2,
                               const float *logits, const int32_t *topk_idx,
                               const float *topk_w, const int32_t *slot,
-                              const int32_t *counts, const void *out, const void *dy,
-                              float g_aux, float g_z, void *dx, float *dw_gate,
+                              const int32_t *counts, const void *out, const void *hidden,
+                              const void *dy, float g_aux, float g_z, void *dx, float *dw_gate,
                               float *db_gate, void *dw1, void *db1, void *dw2, void *db2,
                               void *ws, size_t ws_bytes, hipEvent_t *stage_events,
                               hipStream_t stream);

@@ -90,10 +90,10 @@ def library():
     lib.moe_dispatch.argtypes = [cfgp, vp, vp, vp, vp, vp]
     lib.moe_expert_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
-    lib.moe_layer_forward.argtypes = [cfgp] + [vp] * 17 + [ctypes.c_size_t, vp, vp]
+    lib.moe_layer_forward.argtypes = [cfgp] + [vp] * 18 + [ctypes.c_size_t, vp, vp]
     lib.moe_backward_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     f32 = ctypes.c_float
-    lib.moe_layer_backward.argtypes = [cfgp] + [vp] * 12 + [f32, f32] + [vp] * 8 + \
+    lib.moe_layer_backward.argtypes = [cfgp] + [vp] * 13 + [f32, f32] + [vp] * 8 + \
         [ctypes.c_size_t, vp, vp]
     for f in ("moe_workspace_bytes", "moe_gate", "moe_dispatch", "moe_expert_ffn",
               "moe_combine", "moe_layer_forward", "moe_backward_workspace_bytes",
@@ -231,7 +231,7 @@ def combine(cfg, out, topk_idx, slot, topk_w, y, stream=None):
 
 def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
                   topk_idx=None, topk_w=None, slot=None, counts=None, losses=None, xd=None,
-                  out=None, events=None, stream=None):
+                  out=None, hidden=None, events=None, stream=None):
     """Whole forward pass (``moe_layer_forward``).  ``events``: None or a list
     of MOE_NUM_STAGE_EVENTS entries, each None (boundary not recorded) or a
     torch.cuda.Event already created."""
@@ -254,6 +254,7 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
         _arg(losses, "losses", torch.float32, 2, required=False),
         _arg(xd, "xd", at, R * d, required=False),
         _arg(out, "out", at, R * d, required=False),
+        _arg(hidden, "hidden", at, R * h, required=False),
         wsp, wsb, ev, _stream(stream))
     _check(st, "moe_layer_forward")
 
@@ -267,7 +268,7 @@ def backward_workspace_bytes(cfg: MoeConfig) -> int:
 
 def layer_backward(cfg, x, w_gate, w1, b1, w2, logits, topk_idx, topk_w, slot, counts, out, dy,
                    dx, dw_gate, dw1, dw2, ws, db_gate=None, db1=None, db2=None, g_aux=0.0,
-                   g_z=0.0, events=None, stream=None):
+                   g_z=0.0, hidden=None, events=None, stream=None):
     """Gradients of sum(dy*y) + g_aux*aux + g_z*z (``moe_layer_backward``).
     ``events``: None or MOE_NUM_BWD_EVENTS entries (None or created events)."""
     R = dispatch_rows(cfg)
@@ -281,7 +282,8 @@ def layer_backward(cfg, x, w_gate, w1, b1, w2, logits, topk_idx, topk_w, slot, c
         _arg(topk_idx, "topk_idx", torch.int32, S * k),
         _arg(topk_w, "topk_w", torch.float32, S * k), _arg(slot, "slot", torch.int32, S * k),
         _arg(counts, "counts", torch.int32, k * E), _arg(out, "out", at, R * d),
-        _arg(dy, "dy", at, S * d), float(g_aux), float(g_z), _arg(dx, "dx", at, S * d),
+        _arg(hidden, "hidden", at, R * h, required=False), _arg(dy, "dy", at, S * d),
+        float(g_aux), float(g_z), _arg(dx, "dx", at, S * d),
         _arg(dw_gate, "dw_gate", torch.float32, E * d),
         _arg(db_gate, "db_gate", torch.float32, E, required=False),
         _arg(dw1, "dw1", at, E * h * d), _arg(db1, "db1", at, E * h, required=False),

@@ -360,14 +360,16 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
                              const float* gate_bias, const void* w1, const void* b1,
                              const void* w2, const void* b2, void* y, float* logits,
                              int32_t* topk_idx, float* topk_w, int32_t* slot, int32_t* counts,
-                             float* losses, void* xd, void* out, void* ws, size_t ws_bytes,
+                             float* losses, void* xd, void* out, void* hidden, void* ws,
+                             size_t ws_bytes,
                              hipEvent_t* stage_events, hipStream_t stream) {
     Plan p;
     moe_status s = make_plan(cfg, &p);
     if (s != MOE_OK) return s;
     if (!w_gate || !w1 || !w2 || !ws) return MOE_ERR_INVALID_ARG;
     if (p.S > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
-    for (const void* q : {x, w1, b1, w2, b2, (const void*)y, (const void*)xd, (const void*)out})
+    for (const void* q : {x, w1, b1, w2, b2, (const void*)y, (const void*)xd, (const void*)out,
+                          (const void*)hidden})
         if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
     if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
     const Carve cv = carve(p);
@@ -402,7 +404,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     record(ev, 5, stream);
     s = run_ffn(p, fuse ? x : XD, inv, w1, b1, w2, b2, OUT, at<int32_t>(ws, cv.occ),
                 at<int32_t>(ws, cv.mt_start), at<int32_t>(ws, cv.seg), at<int32_t>(ws, cv.ctr),
-                at<void>(ws, cv.H), ev, stream);
+                hidden ? hidden : at<void>(ws, cv.H), ev, stream);
     if (s != MOE_OK) return s;
     MOE_TRY(launch_combine(OUT, idx, sl, w, y, p.S, p.d, p.k, p.E, row_stride(p), row_limit(p),
                            p.bf16, stream));
@@ -479,7 +481,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
                               const void* w1, const void* b1, const void* w2,
                               const float* logits, const int32_t* topk_idx, const float* topk_w,
                               const int32_t* slot, const int32_t* counts, const void* out,
-                              const void* dy, float g_aux, float g_z, void* dx, float* dw_gate,
+                              const void* hidden, const void* dy, float g_aux, float g_z,
+                              void* dx, float* dw_gate,
                               float* db_gate, void* dw1, void* db1, void* dw2, void* db2,
                               void* ws, size_t ws_bytes, hipEvent_t* stage_events,
                               hipStream_t stream) {
@@ -492,7 +495,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
         return MOE_ERR_INVALID_ARG;
     if (!counts) return MOE_ERR_INVALID_ARG;
     if (!isfinite(g_aux) || !isfinite(g_z)) return MOE_ERR_INVALID_ARG;
-    for (const void* q : {x, w1, b1, w2, out, dy, (const void*)dx, (const void*)dw1,
+    for (const void* q : {x, w1, b1, w2, out, hidden, dy, (const void*)dx, (const void*)dw1,
                           (const void*)db1, (const void*)dw2, (const void*)db2})
         if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
     if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
@@ -540,24 +543,29 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     MOE_TRY(launch_dispatch(x, topk_idx, slot, X, p.S, p.d, p.k, p.E, stride, limit, 2, stream));
     record(ev, 1, stream);
 
-    // H = ReLU(x W1^T + b1) again (rows gathered from x), as in the forward
-    GemmParams g{};
-    g.occ = occ;
-    g.mt_start = mt_fwd;
-    g.mt_expert = mt_fwd + p.E + 1;
-    g.tile_ctr = ctr;
-    g.a_rows = inv;
-    g.row0 = row0;
-    g.E = p.E;
-    g.C = p.C;
-    g.A = x;
-    g.B = w1;
-    g.bias = b1;
-    g.Cout = H;
-    g.N = p.h;
-    g.K = p.d;
-    g.relu = true;
-    MOE_TRY(launch_expert_gemm(g, true, bm, stream));
+    // H = ReLU(x W1^T + b1): the forward's, or computed again (rows gathered
+    // from x) exactly as the forward does
+    const void* Hs = hidden;
+    if (!hidden) {
+        GemmParams g{};
+        g.occ = occ;
+        g.mt_start = mt_fwd;
+        g.mt_expert = mt_fwd + p.E + 1;
+        g.tile_ctr = ctr;
+        g.a_rows = inv;
+        g.row0 = row0;
+        g.E = p.E;
+        g.C = p.C;
+        g.A = x;
+        g.B = w1;
+        g.bias = b1;
+        g.Cout = H;
+        g.N = p.h;
+        g.K = p.d;
+        g.relu = true;
+        MOE_TRY(launch_expert_gemm(g, true, bm, stream));
+        Hs = H;
+    }
     record(ev, 2, stream);
 
     // combine and router backward
@@ -573,10 +581,10 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.E = p.E;
     b.C = p.C;
     b.rows = p.rows;
-    // dW2 = dO^T H (reads H before dgrad 2 overwrites it); db2 = column
+    // dW2 = dO^T H (reads H before dgrad 2 may overwrite it); db2 = column
     // sums of dO in the same pass
     b.A = G;
-    b.B = H;
+    b.B = Hs;
     b.b_rows = nullptr;
     b.bias_grad = db2;
     b.Cout = dw2;
@@ -585,12 +593,13 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     b.tile_ctr = ctr + 8;
     MOE_TRY(launch_bwd_gemm(b, true, false, stream));
     record(ev, 4, stream);
-    // dU = (dO W2) * [H > 0], in place over H
+    // dU = (dO W2) * [H > 0], into H's workspace buffer (in place when H
+    // was recomputed there)
     b.mt_start = mt_bwd;
     b.mt_expert = mt_bwd + p.E + 1;
     b.A = G;
     b.B = w2;
-    b.mask = H;
+    b.mask = Hs;
     b.bias_grad = nullptr;
     b.Cout = H;
     b.N = p.h;

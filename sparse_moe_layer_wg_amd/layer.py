@@ -13,7 +13,8 @@ from . import _lib
 
 class MoELayer:
     def __init__(self, cfg: _lib.MoeConfig, w_gate, gate_bias, w1, b1, w2, b2,
-                 keep: bool = True, device="cuda", dispatch_buffer: bool = True):
+                 keep: bool = True, device="cuda", dispatch_buffer: bool = True,
+                 keep_hidden: bool = False):
         self.cfg = cfg
         self.C = _lib.capacity(cfg)
         # rows of the dispatch buffer / expert output: [E,C] padded, or S*k
@@ -40,22 +41,26 @@ class MoELayer:
             self.xd = torch.empty((*rshape, d), dtype=at, device=dev) if dispatch_buffer \
                 else None
             self.out = torch.empty((*rshape, d), dtype=at, device=dev)
+            # the expert hidden activations, kept for the backward pass
+            self.hidden = torch.empty((*rshape, cfg.d_ff), dtype=at, device=dev) \
+                if keep_hidden else None
         else:
+            self.hidden = None
             self.logits = self.topk_idx = self.topk_w = self.slot = None
             self.counts = self.losses = self.xd = self.out = None
             self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
 
     @classmethod
-    def from_inputs(cls, cfg, inputs: dict, keep=True, dispatch_buffer=True):
+    def from_inputs(cls, cfg, inputs: dict, keep=True, dispatch_buffer=True, keep_hidden=False):
         return cls(cfg, inputs["wg"], inputs["bg"], inputs["w1"], inputs["b1"], inputs["w2"],
                    inputs["b2"], keep=keep, device=inputs["x"].device,
-                   dispatch_buffer=dispatch_buffer)
+                   dispatch_buffer=dispatch_buffer, keep_hidden=keep_hidden)
 
     def forward(self, x, y=None, events=None, stream=None):
         y = self.y if y is None else y
         _lib.layer_forward(self.cfg, x, self.w_gate, self.gate_bias, self.w1, self.b1, self.w2,
                            self.b2, y, self.ws, logits=self.logits, topk_idx=self.topk_idx,
                            topk_w=self.topk_w, slot=self.slot, counts=self.counts,
-                           losses=self.losses, xd=self.xd, out=self.out, events=events,
-                           stream=stream)
+                           losses=self.losses, xd=self.xd, out=self.out, hidden=self.hidden,
+                           events=events, stream=stream)
         return y

@@ -120,13 +120,13 @@ def test_workspace_size_and_errors_before_launch():
     vp = lambda: fake
     # required pointer missing -> INVALID_ARG
     st = lib.moe_layer_forward(ctypes.byref(cfg), None, vp(), None, vp(), None, vp(), None, vp(),
-                               None, None, None, None, None, None, None, None, vp(), n.value,
-                               None, None)
+                               None, None, None, None, None, None, None, None, None, vp(),
+                               n.value, None, None)
     assert st == 1
     # workspace too small -> WORKSPACE
     st = lib.moe_layer_forward(ctypes.byref(cfg), vp(), vp(), None, vp(), None, vp(), None, vp(),
-                               None, None, None, None, None, None, None, None, vp(), n.value - 1,
-                               None, None)
+                               None, None, None, None, None, None, None, None, None, vp(),
+                               n.value - 1, None, None)
     assert st == 3
     # misaligned activation pointer -> INVALID_ARG
     st = lib.moe_dispatch(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 2), vp(), vp(), vp(),
@@ -165,13 +165,14 @@ def test_backward_validation_on_host():
     f = ctypes.c_float
 
     def call(ws_bytes=need, g_aux=0.0, drop=None):
-        args = [fake] * 12
+        args = [fake] * 13
+        args[11] = None                                  # hidden: optional
         if drop is not None:
             args[drop] = None
         return lib.moe_layer_backward(ctypes.byref(cfg), *args, f(g_aux), f(0.0), fake, fake,
                                       None, fake, None, fake, None, fake, ws_bytes, None, None)
     assert call(ws_bytes=need - 1) == 3                 # workspace too small
-    assert call(drop=11) == 1                           # dy missing
+    assert call(drop=12) == 1                           # dy missing
     assert call(drop=10) == 1                           # forward expert outputs missing
     assert call(g_aux=float("nan")) == 1                # loss weight not finite
     assert moe.backward_workspace_bytes(moe.config(2000, 128, 256, 8, 2, dropless=True)) > 0

@@ -34,7 +34,7 @@ def _with_biases(w, inputs, seed):
     return inputs
 
 
-def run_backward(w, inputs, layer, dy, g_aux, g_z, want_biases=True):
+def run_backward(w, inputs, layer, dy, g_aux, g_z, want_biases=True, hidden=None):
     cfg = layer.cfg
     E, d, h = w.E, w.d, w.h
     dev = "cuda"
@@ -53,7 +53,7 @@ def run_backward(w, inputs, layer, dy, g_aux, g_z, want_biases=True):
                        layer.logits, layer.topk_idx, layer.topk_w, layer.slot, layer.counts,
                        layer.out, dy, grads["dx"], grads["dwg"], grads["dw1"], grads["dw2"], ws,
                        db_gate=grads["dbg"], db1=grads["db1"], db2=grads["db2"], g_aux=g_aux,
-                       g_z=g_z)
+                       g_z=g_z, hidden=hidden)
     torch.cuda.synchronize()
     return grads
 
@@ -98,6 +98,37 @@ def test_backward_full_parity(w):
     dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
     grads = run_backward(w, inputs, layer, dy, g_aux=0.7, g_z=0.3)
     check_backward(w, inputs, layer, grads, dy, 0.7, 0.3)
+
+
+def test_backward_saved_hidden_matches_recompute():
+    """A forward that keeps its hidden activations, and a backward that reuses
+    them, give the same forward outputs and the same gradients, bit for bit,
+    as the recomputing backward; the saved buffer is left unchanged."""
+    from sparse_moe_layer_wg_amd.layer import MoELayer
+    for w in (BWD[0], BWD[3]):
+        inputs = _with_biases(w, mw.generate(w, "cuda"), w.seed + 100)
+        inputs, plain = run_layer(w, inputs, dispatch_buffer=False)
+        cfg = plain.cfg
+        kept = MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False,
+                                    keep_hidden=True)
+        kept.forward(inputs["x"])
+        torch.cuda.synchronize()
+        assert torch.equal(kept.y, plain.y)
+        # expert outputs of the filled rows (padded rows are never written)
+        if w.dropless:
+            assert torch.equal(kept.out, plain.out)
+        else:
+            occ = np.minimum(plain.counts.cpu().numpy().sum(0), plain.C)
+            filled = torch.from_numpy(np.arange(plain.C)[None, :] < occ[:, None]).cuda()
+            assert torch.equal(kept.out[filled], plain.out[filled])
+        saved = kept.hidden.clone()
+        g = torch.Generator(device="cuda").manual_seed(w.seed + 300)
+        dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        a = run_backward(w, inputs, plain, dy, 0.4, 0.2)
+        b = run_backward(w, inputs, kept, dy, 0.4, 0.2, hidden=kept.hidden)
+        for key in a:
+            assert torch.equal(a[key], b[key]), (w.name, key)
+        assert torch.equal(kept.hidden, saved)
 
 
 def test_backward_zero_upstream_gives_exact_zeros():
