@@ -275,3 +275,40 @@ def test_zero_router_closed_form(E, k):
     aux, z = layer.losses.cpu().numpy()
     assert abs(aux - 1.0) <= 1e-5 and abs(z - np.log(E) ** 2) <= 1e-5 * np.log(E) ** 2
     _print(f"zero_router_E{E}", check_layer(w, inputs, layer, full=True))
+
+
+# --------------------------------------------------------------------- graph capture
+def test_layer_forward_replays_in_a_hip_graph():
+    """moe_layer_forward enqueues kernels only (no allocation, copy, memset or
+    host synchronisation), so it can be captured in a HIP graph.  The graph is
+    replayed several times, with eager work and synchronisations between the
+    replays and new token values each time, and every replay equals an eager
+    run on the same inputs bit for bit."""
+    from sparse_moe_layer_wg_amd.layer import MoELayer
+    w = MID[0]
+    inputs = mw.generate(w, "cuda")
+    eager = MoELayer.from_inputs(moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor,
+                                            dtype=w.dtype), inputs, keep=True,
+                                 dispatch_buffer=False)
+    graphed = MoELayer.from_inputs(eager.cfg, inputs, keep=True, dispatch_buffer=False)
+    x_static = inputs["x"].clone()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graphed.forward(x_static)          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed.forward(x_static)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for rep in range(4):
+        x_new = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        x_static.copy_(x_new)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager.forward(x_new)
+        torch.cuda.synchronize()
+        for name in ("y", "topk_idx", "slot", "counts", "losses", "logits"):
+            assert torch.equal(getattr(graphed, name), getattr(eager, name)), (rep, name)
