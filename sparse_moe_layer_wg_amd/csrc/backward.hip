@@ -115,110 +115,69 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     }
 }
 
-// fp32 GEMM for the router side, 64x64 tiles, 4x4 results per thread, k-steps
-// of 16 staged in LDS as [k][row].
-//   DX:  C[s, i] = sum_j dl[s, j] wg[j, i]  (+ the token's dX rows, bf16 out)
-//   DW:  C[j, i] = sum_s dl[s, j] x[s, i]   (fp32 out), the tokens split into
-//        gridDim.z chunks of kchunk: chunk z writes its partial sums to
-//        Cout + z*E*d, and the blocks of column tile 0 also the partial
-//        column sums of dl to pdbg + z*E (summed in a fixed order later).
+// dWg on the router side in fp32: C[j, i] = sum_s dl[s, j] x[s, i], 64x64
+// tiles, 4x4 results per thread (contiguous, read from LDS as float4), k-steps
+// of 16 tokens staged as [k][row].  The tokens are split into gridDim.z chunks
+// of kchunk: chunk z writes its partial sums to part + z*E*d, and the blocks
+// of column tile 0 also the partial column sums of dl to pdbg + z*E (both
+// summed in a fixed order by router_dw_reduce_kernel).
 constexpr int RT = 64, RK = 16;
-template <bool DX>
-__global__ __launch_bounds__(256) void router_gemm_kernel(
-    const float* __restrict__ dl, const void* __restrict__ Bsrc, const bf16_t* __restrict__ dX,
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot,
-    void* __restrict__ Cout, float* __restrict__ pdbg, int S, int d, int E, int k, int stride,
-    int limit, int kchunk) {
-    __shared__ float As[RK][RT + 4];
-    __shared__ float Bs[RK][RT + 4];
+__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
+                                                        const bf16_t* __restrict__ x,
+                                                        float* __restrict__ part,
+                                                        float* __restrict__ pdbg, int S, int d,
+                                                        int E, int kchunk) {
+    __shared__ __attribute__((aligned(16))) float As[RK][RT];
+    __shared__ __attribute__((aligned(16))) float Bs[RK][RT];
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
     const int m0 = blockIdx.y * RT, n0 = blockIdx.x * RT;
-    const int M = DX ? S : E;
-    const int kbeg = DX ? 0 : blockIdx.z * kchunk;
-    const int K = DX ? E : min(S, kbeg + kchunk);
+    const int kbeg = blockIdx.z * kchunk;
+    const int K = min(S, kbeg + kchunk);
     float acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    float csum = 0.f;  // DW, column tile 0: sum of dl[., m0 + tid] over the chunk
+    float csum = 0.f;  // column tile 0: sum of dl[., m0 + tid] over the chunk
+    const int kk = tid / 16, cc = (tid % 16) * 4;  // this thread's loads
     for (int k0 = kbeg; k0 < K; k0 += RK) {
-        // A(m, kk): DX: dl[m, kk] (m = token); DW: dl[kk, m] (kk = token)
-        // B(n, kk): DX: wg[kk, n];             DW: x[kk, n] (bf16)
-        // thread loads 4 A and 4 B elements: (kk = tid / 16, col = (tid % 16) * 4 + c)
         __syncthreads();
+        const bool krow = k0 + kk < K;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            float av = 0.f, bv = 0.f;
-            if (DX) {
-                // A is K-contiguous: kk varies fastest across threads
-                const int mm = tid / 4 + 0, kk = (tid % 4) * 4 + c;
-                if (m0 + mm < M && k0 + kk < K) av = dl[(int64_t)(m0 + mm) * E + k0 + kk];
-                As[kk][mm] = av;
-            } else {
-                const int kk = tid / 16, mm = (tid % 16) * 4 + c;
-                if (m0 + mm < M && k0 + kk < K) av = dl[(int64_t)(k0 + kk) * E + m0 + mm];
-                As[kk][mm] = av;
-            }
-            const int kk = tid / 16, nn = (tid % 16) * 4 + c;
-            if (n0 + nn < d && k0 + kk < K) {
-                if (DX)
-                    bv = static_cast<const float*>(Bsrc)[(int64_t)(k0 + kk) * d + n0 + nn];
-                else
-                    bv = bf16_to_f32(static_cast<const bf16_t*>(Bsrc)[(int64_t)(k0 + kk) * d + n0 + nn]);
-            }
-            Bs[kk][nn] = bv;
+            As[kk][cc + c] = (krow && m0 + cc + c < E) ? dl[(int64_t)(k0 + kk) * E + m0 + cc + c]
+                                                       : 0.f;
+            Bs[kk][cc + c] =
+                (krow && n0 + cc + c < d) ? bf16_to_f32(x[(int64_t)(k0 + kk) * d + n0 + cc + c])
+                                          : 0.f;
         }
         __syncthreads();
-        if (!DX && blockIdx.x == 0 && tid < RT) {
+        if (blockIdx.x == 0 && tid < RT) {
 #pragma unroll
-            for (int kk = 0; kk < RK; ++kk) csum += As[kk][tid];
+            for (int q = 0; q < RK; ++q) csum += As[q][tid];
         }
 #pragma unroll
-        for (int kk = 0; kk < RK; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+        for (int q = 0; q < RK; ++q) {
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&As[q][ty * 4]);
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&Bs[q][tx * 4]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
         }
     }
+    float* out = part + (int64_t)blockIdx.z * E * d;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int m = m0 + ty + 16 * i;
-        if (m >= M) continue;
-        if (DX) {
-            // the token's expert-side input gradient rows, in rank order
-            int64_t u[kMaxK];
+        const int m = m0 + ty * 4 + i;
+        if (m >= E) continue;
 #pragma unroll
-            for (int r = 0; r < kMaxK; ++r)
-                u[r] = r < k ? assignment_row(topk_idx, slot, (int64_t)m * k + r, E, stride, limit)
-                             : -1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = n0 + tx + 16 * j;
-                if (n >= d) continue;
-                float v = acc[i][j];
-#pragma unroll
-                for (int r = 0; r < kMaxK; ++r)
-                    if (u[r] >= 0) v += bf16_to_f32(dX[u[r] * d + n]);
-                static_cast<bf16_t*>(Cout)[(int64_t)m * d + n] = f32_to_bf16(v);
-            }
-        } else {
-            float* part = static_cast<float*>(Cout) + (int64_t)blockIdx.z * E * d;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = n0 + tx + 16 * j;
-                if (n < d) part[(int64_t)m * d + n] = acc[i][j];
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n < d) out[(int64_t)m * d + n] = acc[i][j];
         }
     }
-    if (!DX && blockIdx.x == 0 && tid < RT && m0 + tid < E)
-        pdbg[(int64_t)blockIdx.z * E + m0 + tid] = csum;
+    if (blockIdx.x == 0 && tid < RT && m0 + tid < E) pdbg[(int64_t)blockIdx.z * E + m0 + tid] = csum;
 }
 
 // dwg = sum over chunks of the partial products, dbg likewise (chunk order).
@@ -247,6 +206,82 @@ __global__ void zero_bytes_kernel(uint32_t* __restrict__ p, size_t n) {
         p[i] = 0u;
     if ((n & 2) && blockIdx.x == 0 && threadIdx.x == 0)
         reinterpret_cast<uint16_t*>(p)[2 * words] = 0u;
+}
+
+// Router part of dx on the bf16 MFMAs: dl [S,E] and Wg [E,d] are fp32; with
+// v = hi + lo (hi = bf16(v), lo = bf16(v - hi)) for both, dl Wg is taken as
+// dl_hi W_hi + dl_hi W_lo + dl_lo W_hi (the dropped lo*lo term is 2^-16 of the
+// product, far below the bf16 rounding of dx).  The three products become one
+// GEMM over K = 3E' (E' = E rounded up to 64, zero padded):
+//   A [S, 3E'] = [dl_hi | dl_hi | dl_lo],  B [3E', d] = [W_hi ; W_lo ; W_hi].
+// count1 receives S (the one "expert" of that GEMM).
+__global__ void router_dx_split_kernel(const float* __restrict__ dl, const float* __restrict__ wg,
+                                       int S, int E, int Ep, int d, bf16_t* __restrict__ a,
+                                       bf16_t* __restrict__ b, int32_t* __restrict__ count1) {
+    const int64_t na = (int64_t)S * Ep, nb = (int64_t)Ep * d;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na + nb;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < na) {
+            const int64_t s = i / Ep;
+            const int j = (int)(i - s * Ep);
+            const float v = j < E ? dl[s * E + j] : 0.f;
+            const bf16_t hi = f32_to_bf16(v);
+            const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+            bf16_t* row = a + s * 3 * Ep;
+            row[j] = hi;
+            row[Ep + j] = hi;
+            row[2 * Ep + j] = lo;
+        } else {
+            const int64_t q = i - na;
+            const int j = (int)(q / d), c = (int)(q - (int64_t)j * d);
+            const float v = j < E ? wg[(int64_t)j * d + c] : 0.f;
+            const bf16_t hi = f32_to_bf16(v);
+            const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+            b[(int64_t)j * d + c] = hi;
+            b[((int64_t)Ep + j) * d + c] = lo;
+            b[((int64_t)2 * Ep + j) * d + c] = hi;
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) count1[0] = S;
+}
+
+// dx[s] = bf16(dxr[s] + sum over kept r of dX[u(s,r)]): one wave per token,
+// fp32 sums in rank order.
+__global__ __launch_bounds__(256) void dx_assemble_kernel(
+    const u32x4_t* __restrict__ dxr, const u32x4_t* __restrict__ dX,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot,
+    u32x4_t* __restrict__ dx, int S, int nvec, int k, int E, int stride, int limit) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
+    if (s >= S) return;
+    int64_t u[kMaxK];
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r)
+        u[r] = r < k ? assignment_row(topk_idx, slot, (int64_t)s * k + r, E, stride, limit) : -1;
+    for (int i = lane; i < nvec; i += kWave) {
+        float acc[8];
+        const u32x4_t v0 = dxr[(int64_t)s * nvec + i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = __uint_as_float(v0[q] << 16);
+            acc[2 * q + 1] = __uint_as_float(v0[q] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxK; ++r) {
+            if (u[r] >= 0) {
+                const u32x4_t v = dX[u[r] * nvec + i];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += __uint_as_float(v[q] << 16);
+                    acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+                }
+            }
+        }
+        u32x4_t o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        dx[(int64_t)s * nvec + i] = o;
+    }
 }
 
 }  // namespace
@@ -280,14 +315,62 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
     return hipGetLastError();
 }
 
+size_t router_dx_workspace(int S, int d, int E) {
+    const size_t Ep = (size_t)(E + 63) / 64 * 64;
+    size_t o = 0;
+    auto take = [&](size_t n) { o += (n + 255) & ~(size_t)255; };
+    take((size_t)S * 3 * Ep * 2);                        // A
+    take(3 * Ep * (size_t)d * 2);                        // B
+    take((size_t)S * d * 2);                             // dxr
+    take((2 + 1 + 2 + mtile_table_len(1, S, (size_t)S)) * 4);  // count, occ, m-tiles
+    take(8 * 4);                                         // tile counters
+    return o;
+}
+
 hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
                             const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
-                            int E, int k, int stride, int limit, hipStream_t st) {
+                            int E, int k, int stride, int limit, void* work, hipStream_t st) {
     if (S == 0) return hipSuccess;
-    dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(S, RT));
-    router_gemm_kernel<true><<<grid, 256, 0, st>>>(dl, wg, static_cast<const bf16_t*>(dX),
-                                                   topk_idx, slot, dx, nullptr, S, d, E, k,
-                                                   stride, limit, 0);
+    const int Ep = (E + 63) / 64 * 64;
+    char* o = static_cast<char*>(work);
+    auto take = [&](size_t n) {
+        char* at = o;
+        o += (n + 255) & ~(size_t)255;
+        return at;
+    };
+    bf16_t* A = reinterpret_cast<bf16_t*>(take((size_t)S * 3 * Ep * 2));
+    bf16_t* B = reinterpret_cast<bf16_t*>(take((size_t)3 * Ep * d * 2));
+    void* dxr = take((size_t)S * d * 2);
+    int32_t* tab = reinterpret_cast<int32_t*>(take((2 + 1 + 2 + mtile_table_len(1, S, (size_t)S)) * 4));
+    int32_t* ctr = reinterpret_cast<int32_t*>(take(8 * 4));
+    int32_t* count1 = tab;   // [1]
+    int32_t* occ1 = tab + 1; // [1]
+    int32_t* mt1 = tab + 2;  // [2] prefix, then the m-tile experts
+    const int64_t n = (int64_t)S * Ep + (int64_t)Ep * d;
+    const unsigned g = (unsigned)(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192);
+    router_dx_split_kernel<<<g, 256, 0, st>>>(dl, wg, S, E, Ep, d, A, B, count1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = launch_occupancy(count1, 1, 1, S, 256, 0, occ1, mt1, nullptr, S, ctr, 8, st);
+    if (err != hipSuccess) return err;
+    BwdGemmParams b{};
+    b.A = A;
+    b.B = B;
+    b.Cout = dxr;
+    b.occ = occ1;
+    b.mt_start = mt1;
+    b.mt_expert = mt1 + 2;
+    b.tile_ctr = ctr;
+    b.E = 1;
+    b.C = S;
+    b.N = d;
+    b.K = 3 * Ep;
+    b.rows = (size_t)S;
+    err = launch_bwd_gemm(b, false, false, st);
+    if (err != hipSuccess) return err;
+    dx_assemble_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
+        static_cast<const u32x4_t*>(dxr), static_cast<const u32x4_t*>(dX), topk_idx, slot,
+        static_cast<u32x4_t*>(dx), S, d / 8, k, E, stride, limit);
     return hipGetLastError();
 }
 
@@ -312,8 +395,8 @@ hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* d
     float* pw = static_cast<float*>(part);
     float* pb = pw + (size_t)nsplit * E * d;
     dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(E, RT), (unsigned)nsplit);
-    router_gemm_kernel<false><<<grid, 256, 0, st>>>(dl, x, nullptr, nullptr, nullptr, pw, pb, S,
-                                                    d, E, 1, 0, 0, kchunk);
+    router_dw_kernel<<<grid, 256, 0, st>>>(dl, static_cast<const bf16_t*>(x), pw, pb, S, d, E,
+                                           kchunk);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const int64_t n = (int64_t)E * d;
     router_dw_reduce_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(pw, pb, nsplit, E, d,

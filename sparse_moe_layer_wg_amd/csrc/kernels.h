@@ -169,12 +169,17 @@ hipError_t launch_combine_bwd(const void* dy, const void* out, const int32_t* to
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                              const float* dw, const int32_t* counts, float g_aux, float g_z,
                              float* dl, int S, int E, int k, hipStream_t st);
-// Router-side fp32 GEMMs:
+// Router side of the input gradient:
 //   dx[s, i] = bf16(sum_j dl[s, j] wg[j, i] + sum over kept r of dX[u(s,r), i])
-//   dwg[j, i] = sum_s dl[s, j] x[s, i];  dbg[j] = sum_s dl[s, j]
+// the first sum on the bf16 MFMAs with a two-term split of dl and wg (relative
+// error about 2^-16, below dx's bf16 rounding); `work` holds
+// router_dx_workspace bytes.
+size_t router_dx_workspace(int S, int d, int E);
 hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
                             const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
-                            int E, int k, int stride, int limit, hipStream_t st);
+                            int E, int k, int stride, int limit, void* work, hipStream_t st);
+// Router weight gradient in fp32:
+//   dwg[j, i] = sum_s dl[s, j] x[s, i];  dbg[j] = sum_s dl[s, j]
 // (dwg over token chunks: `part` holds router_dw_workspace bytes of partials)
 size_t router_dw_workspace(int S, int d, int E);
 hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,

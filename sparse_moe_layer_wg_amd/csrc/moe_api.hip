@@ -423,10 +423,11 @@ constexpr int kBwdCounters = 40;
 // Backward workspace, every region 256-byte aligned:
 //   occ [E], forward m-tile list (E+1 + table), backward m-tile list
 //   (E+1 + table), seg [E], tile counters, inv [R], dw [S,k] fp32,
-//   dl [S,E] fp32, router-gradient partials, H then dU [R,h], dO then dX
+//   dl [S,E] fp32, router weight-gradient partials, the router dx GEMM's
+//   operands and tables, H then dU [R,h], dO then dX
 //   [R,d], the dispatched rows of x [R,d]   (R = rows)
 struct BwdCarve {
-    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, rpart, H, G, X, end;
+    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, rpart, rdx, H, G, X, end;
 };
 
 BwdCarve bwd_carve(const Plan& p) {
@@ -447,6 +448,7 @@ BwdCarve bwd_carve(const Plan& p) {
     c.dw = take((size_t)p.S * p.k * 4);
     c.dl = take((size_t)p.S * p.E * 4);
     c.rpart = take(router_dw_workspace(p.S, p.d, p.E));
+    c.rdx = take(router_dx_workspace(p.S, p.d, p.E));
     c.H = take(p.rows * p.h * 2);
     c.G = take(p.rows * p.d * 2);
     c.X = take(p.rows * p.d * 2);
@@ -633,7 +635,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
 
     // dx = dispatch backward + dl Wg; dWg = dl^T x; dbg = colsum dl
     MOE_TRY(launch_router_dx(dl, w_gate, G, topk_idx, slot, dx, p.S, p.d, p.E, p.k, stride, limit,
-                             stream));
+                             at<void>(ws, cv.rdx), stream));
     MOE_TRY(launch_router_dw(dl, x, dw_gate, db_gate, p.S, p.d, p.E, at<void>(ws, cv.rpart),
                              stream));
     record(ev, 8, stream);
