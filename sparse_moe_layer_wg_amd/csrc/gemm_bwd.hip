@@ -167,18 +167,19 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
         const int kb = kt * BK;
         if constexpr (WGRAD) {
             // rows past the occupancy load as zero
-            const bf16_t* __restrict__ Ab = reinterpret_cast<const bf16_t*>(Ac);
-            const bf16_t* __restrict__ Bb = reinterpret_cast<const bf16_t*>(Bc);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int k = kb + 8 * wave + r;
                 va[r] = make_uint2(0u, 0u);
                 vb[r] = make_uint2(0u, 0u);
-                if (k < u.Keff) {
+                if (k < u.Keff) {   // wave-uniform
                     const size_t ar = u.row_e + k;
-                    const size_t br = p.b_rows ? (size_t)p.b_rows[ar] : ar;
-                    va[r] = *reinterpret_cast<const uint2*>(Ab + ar * u.M + u.ca);
-                    vb[r] = *reinterpret_cast<const uint2*>(Bb + br * N + u.cb);
+                    const size_t br =
+                        p.b_rows ? (size_t)__builtin_amdgcn_readfirstlane(p.b_rows[ar]) : ar;
+                    va[r] = *reinterpret_cast<const uint2*>(Ac + ar * u.M * 2 +
+                                                            (uint32_t)u.ca * 2u);
+                    vb[r] = *reinterpret_cast<const uint2*>(Bc + br * N * 2 +
+                                                            (uint32_t)u.cb * 2u);
                 }
             }
         } else {
