@@ -145,7 +145,10 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if a.ep_share:
-        print(json.dumps(bench_ep_share(a, mw.EP_SHARES[a.ep_share])), flush=True)
+        out = bench_ep_share(a, mw.EP_SHARES[a.ep_share])
+        if a.copy_calibration_mb > 0:
+            out["copy_calibration_bytes"] = calibration_copy(a.copy_calibration_mb)
+        print(json.dumps(out), flush=True)
         return
     w = mw.get(a.workload)
     if a.dropless:
@@ -348,7 +351,8 @@ def bench_ep_share(a, sh) -> dict:
         roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_PEAK_TFLOPS["bf16"],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    t1, t2 = (measured_traffic(sh.name, k) for k in ("expert_gemm1", "expert_gemm2"))
+    roof["traffic"] = t1 + t2 if t1 is not None and t2 is not None else None
     roof["kernel"] = "expert_gemm1+expert_gemm2 (one moe_expert_ffn call)"
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = by
