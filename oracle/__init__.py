@@ -58,14 +58,15 @@ def _load():
     lib.oracle_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_token_output.argtypes = [i32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     f64 = ctypes.c_double
-    lib.oracle_layer_backward.argtypes = [i32] * 6 + [vp, i32, vp, vp, vp, vp, vp, vp, vp, f64, f64] \
+    lib.oracle_layer_backward.argtypes = [i32] * 7 + [vp, i32, vp, vp, vp, vp, vp, vp, vp, f64, f64] \
         + [vp] * 9
+    lib.oracle_reroute.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_router_backward.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, f64, f64, vp]
-    lib.oracle_backward_entries.argtypes = [i32] * 6 + [vp, i32, vp, vp, vp, vp, vp, vp, vp] \
+    lib.oracle_backward_entries.argtypes = [i32] * 7 + [vp, i32, vp, vp, vp, vp, vp, vp, vp] \
         + [f64, f64, i32, vp, vp, i32, vp, vp, vp, vp, vp]
     for name in ("oracle_logits", "oracle_route", "oracle_dispatch", "oracle_expert_ffn",
                  "oracle_combine", "oracle_token_output", "oracle_layer_backward",
-                 "oracle_router_backward", "oracle_backward_entries"):
+                 "oracle_router_backward", "oracle_backward_entries", "oracle_reroute"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -117,8 +118,12 @@ def logits(x: np.ndarray, wg: np.ndarray, bg: np.ndarray | None = None) -> np.nd
     return out
 
 
-def route(lg: np.ndarray, k: int, C: int) -> dict:
-    """Softmax, top-k, renormalised weights, capacity slots, counts, losses."""
+def route(lg: np.ndarray, k: int, C: int, reroute: bool = False) -> dict:
+    """Softmax, top-k, renormalised weights, capacity slots, counts, losses.
+    ``serve`` is the expert serving each assignment: ``idx``, except that
+    with ``reroute`` dropped assignments move to alternative experts
+    (oracle_reroute); ``counts`` then gains a row k with the offers each
+    expert accepted."""
     lg = np.ascontiguousarray(lg, dtype=np.float32)
     S, E = lg.shape
     assert 1 <= k <= E and C >= 1
@@ -131,13 +136,24 @@ def route(lg: np.ndarray, k: int, C: int) -> dict:
     losses = np.empty((2,), np.float64)
     _load().oracle_route(S, E, k, C, _ptr(lg), _ptr(idx), _ptr(w), _ptr(slot), _ptr(counts),
                          _ptr(lse), _ptr(psum), _ptr(losses))
-    return dict(idx=idx, w=w, slot=slot, counts=counts, lse=lse, psum=psum,
+    serve = idx
+    if reroute:
+        serve = np.empty_like(idx)
+        acc = np.empty(E, np.int32)
+        _load().oracle_reroute(S, E, k, C, _ptr(lg), _ptr(idx), _ptr(serve), _ptr(slot), _ptr(acc))
+        counts = np.vstack([counts, acc[None, :]])
+    return dict(idx=idx, serve=serve, w=w, slot=slot, counts=counts, lse=lse, psum=psum,
                 aux=float(losses[0]), z=float(losses[1]))
 
 
-def occupancy(counts: np.ndarray, C: int) -> np.ndarray:
-    """Filled slots per expert: min(total assignments, C)."""
-    return np.minimum(counts.sum(axis=0), C).astype(np.int32)
+def occupancy(counts: np.ndarray, C: int, k: int | None = None) -> np.ndarray:
+    """Filled slots per expert: min(assignments, C), plus the accepted
+    re-routed offers (row k of counts) when counts has k + 1 rows."""
+    k = counts.shape[0] if k is None else k
+    occ = np.minimum(counts[:k].sum(axis=0), C)
+    if counts.shape[0] > k:
+        occ = occ + counts[k]
+    return occ.astype(np.int32)
 
 
 def dispatch(x: np.ndarray, idx: np.ndarray, slot: np.ndarray, E: int, C: int) -> np.ndarray:
@@ -243,25 +259,26 @@ def layer_dropless(x, wg, bg, w1, b1, w2, b2, k: int, lg: np.ndarray | None = No
     return res
 
 
-def layer(x, wg, bg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray | None = None) -> dict:
+def layer(x, wg, bg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray | None = None,
+          reroute: bool = False) -> dict:
     """Whole forward pass.  With ``lg`` given, routing starts from those fp32
     logits instead of computing them (used to compare against a device that
     produced the logits itself)."""
     if lg is None:
         lg = logits(x, wg, bg)
-    r = route(lg, k, C)
+    r = route(lg, k, C, reroute)
     E = lg.shape[1]
     S = lg.shape[0]
-    xd = dispatch(x, r["idx"], r["slot"], E, C)
-    occ = occupancy(r["counts"], C)
+    xd = dispatch(x, r["serve"], r["slot"], E, C)
+    occ = occupancy(r["counts"], C, k)
     out = expert_ffn(xd, occ, w1, b1, w2, b2)
-    y = combine(out, r["idx"], r["slot"], r["w"], S)
+    y = combine(out, r["serve"], r["slot"], r["w"], S)
     r.update(logits=lg, xd=xd, occ=occ, out=out, y=y)
     return r
 
 
 def layer_backward(x, wg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray, dy: np.ndarray,
-                   g_aux: float = 0.0, g_z: float = 0.0) -> dict:
+                   g_aux: float = 0.0, g_z: float = 0.0, reroute: bool = False) -> dict:
     """fp64 gradients of L = sum(dy * y) + g_aux * aux + g_z * z with the
     routing that the fp32 logits ``lg`` select (capacity C; C = S for
     dropless routing, which no expert can exceed).  Returns dx [S,d],
@@ -280,7 +297,7 @@ def layer_backward(x, wg, w1, b1, w2, b2, k: int, C: int, lg: np.ndarray, dy: np
                dw1=np.empty((E, h, d)), db1=np.empty((E, h)), dw2=np.empty((E, d, h)),
                db2=np.empty((E, d)), dl=np.empty((S, E)), dw=np.empty((S, k)))
     _load().oracle_layer_backward(
-        S, d, h, E, k, C, _ptr(x), dt, _ptr(wg), _ptr(lg), _ptr(w1), _ptr(b1), _ptr(w2),
+        S, d, h, E, k, C, int(reroute), _ptr(x), dt, _ptr(wg), _ptr(lg), _ptr(w1), _ptr(b1), _ptr(w2),
         _ptr(b2), _ptr(dy), float(g_aux), float(g_z),
         *[_ptr(out[n]) for n in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2", "dl", "dw")])
     return out
@@ -305,7 +322,7 @@ def router_backward(lg: np.ndarray, idx, w, dw, counts, g_aux: float, g_z: float
 
 
 def backward_entries(x, wg, w1, b1, w2, b2, k: int, C: int, lg, dy, g_aux, g_z, tokens,
-                     entries) -> tuple[np.ndarray, np.ndarray]:
+                     entries, reroute: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """dx rows of ``tokens`` and weight-gradient ``entries`` [(kind, e, a, b)]
     (kind 1 dW1[e,a,b], 2 dW2[e,a,b], 3 db1[e,a], 4 db2[e,a]) computed one by
     one, for full-size checks."""
@@ -322,7 +339,7 @@ def backward_entries(x, wg, w1, b1, w2, b2, k: int, C: int, lg, dy, g_aux, g_z, 
     dx_rows = np.empty((tokens.size, d))
     vals = np.empty(len(ent))
     _load().oracle_backward_entries(
-        S, d, h, E, k, C, _ptr(x), dt, _ptr(wg), _ptr(lg), _ptr(w1), _ptr(b1), _ptr(w2),
+        S, d, h, E, k, C, int(reroute), _ptr(x), dt, _ptr(wg), _ptr(lg), _ptr(w1), _ptr(b1), _ptr(w2),
         _ptr(b2), _ptr(dy), float(g_aux), float(g_z), tokens.size, _ptr(tokens), _ptr(dx_rows),
         len(ent), _ptr(kind), _ptr(ee), _ptr(ea), _ptr(eb), _ptr(vals))
     return dx_rows, vals

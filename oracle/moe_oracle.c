@@ -193,6 +193,86 @@ void oracle_route(int S, int E, int k, int C, const float *logits,
     free(p);
 }
 
+/* Overflow re-routing, a reading of [blog] "Expert Capacity" (tokens over an
+ * expert's capacity are dropped "or routed to alternative experts"; the pages
+ * give no rule).  After the capacity pass (oracle_route), the j-th dropped
+ * assignment of token s (dropped ranks in rank order, j = 0, 1, ...) is
+ * offered to the token's (k+j)-th ranked expert: all E experts ordered by
+ * (logit descending, index ascending), ranks counted from 0, so the offer
+ * goes to the best expert outside the token's top-k, then the next, and so
+ * on.  Offers are taken virtual rank by virtual rank (j = 0 for every token,
+ * then j = 1, ...), tokens in order; an offer is accepted while its expert
+ * holds fewer than C rows (rows kept by the capacity pass plus offers
+ * accepted before it), and is otherwise dropped for good.  No offer exists
+ * when k + j >= E.  The assignment keeps its weight w[s,r].
+ * In:  idx [S,k] (the top-k), slot [S,k] from the capacity pass.
+ * Out: serve [S,k] (the expert serving (s,r): idx unless re-routed),
+ *      slot updated in place, accepted [E] (offers each expert took). */
+void oracle_reroute(int S, int E, int k, int C, const float *logits, const int32_t *idx,
+                    int32_t *serve, int32_t *slot, int32_t *accepted)
+{
+    int32_t *cnt = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (size_t q = 0; q < (size_t)S * k; ++q) {
+        serve[q] = idx[q];
+        if (slot[q] >= 0)
+            cnt[idx[q]] += 1;                  /* rows kept by the capacity pass */
+    }
+    memset(accepted, 0, sizeof(int32_t) * (size_t)E);
+    /* offers[s*k + j]: rank r of the token's j-th dropped assignment, or -1 */
+    int32_t *offer_r = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *offer_e = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *taken = (int32_t *)malloc(sizeof(int32_t) * (size_t)(2 * k + 1));
+    for (int s = 0; s < S; ++s) {
+        const float *l = logits + (size_t)s * E;
+        int nt = 0;
+        for (int r = 0; r < k; ++r)
+            taken[nt++] = idx[(size_t)s * k + r];
+        int j = 0;
+        for (int r = 0; r < k; ++r) {
+            offer_r[(size_t)s * k + r] = -1;
+            offer_e[(size_t)s * k + r] = -1;
+        }
+        for (int r = 0; r < k; ++r) {
+            if (slot[(size_t)s * k + r] >= 0)
+                continue;
+            /* the next expert in the token's ranking after those taken */
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                int used = 0;
+                for (int t = 0; t < nt; ++t)
+                    if (taken[t] == e)
+                        used = 1;
+                if (used)
+                    continue;
+                if (best < 0 || l[e] > l[best])
+                    best = e;
+            }
+            offer_r[(size_t)s * k + j] = r;
+            offer_e[(size_t)s * k + j] = best;   /* -1 when k + j >= E */
+            if (best >= 0)
+                taken[nt++] = best;
+            ++j;
+        }
+    }
+    for (int j = 0; j < k; ++j) {
+        for (int s = 0; s < S; ++s) {
+            int r = offer_r[(size_t)s * k + j], e = offer_e[(size_t)s * k + j];
+            if (r < 0 || e < 0)
+                continue;
+            if (cnt[e] < C) {
+                serve[(size_t)s * k + r] = e;
+                slot[(size_t)s * k + r] = cnt[e];
+                cnt[e] += 1;
+                accepted[e] += 1;
+            }
+        }
+    }
+    free(cnt);
+    free(offer_r);
+    free(offer_e);
+    free(taken);
+}
+
 /* Dispatch, the local stand-in for the first all-to-all ([atlas] "In plain
  * words"): xd[e,c,:] = x[s,:] for every kept assignment (s,r) with
  * e = idx[s,r], c = slot[s,r].  Slots nobody was assigned stay zero.  The
@@ -399,7 +479,7 @@ void oracle_router_backward(int S, int E, int k, const float *logits, const int3
     }
 }
 
-void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
+void oracle_layer_backward(int S, int d, int h, int E, int k, int C, int reroute,
                            const void *x, int dtype, const float *wg, const float *logits,
                            const void *w1, const void *b1, const void *w2, const void *b2,
                            const void *dy, double g_aux, double g_z,
@@ -414,6 +494,14 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
     double *psum = (double *)malloc(sizeof(double) * (size_t)E);
     double losses[2];
     oracle_route(S, E, k, C, logits, idx, w, slot, counts, lse, psum, losses);
+    /* the expert that serves each assignment (re-routing moves some); the
+     * router's selected-softmax term keeps the top-k idx */
+    int32_t *serve = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *acc_e = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (reroute)
+        oracle_reroute(S, E, k, C, logits, idx, serve, slot, acc_e);
+    else
+        memcpy(serve, idx, sizeof(int32_t) * (size_t)S * k);
 
     /* per-assignment hidden activations a and pre-activation gradients du */
     size_t nas = (size_t)S * k;
@@ -433,7 +521,7 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
                 dw[q] = 0.0;
                 if (slot[q] < 0)
                     continue;
-                int e = idx[q];
+                int e = serve[q];
                 double *a = a_all + q * h;
                 double *du = du_all + q * h;
                 for (int j = 0; j < h; ++j) {
@@ -492,7 +580,7 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
         for (int s = 0; s < S; ++s) {
             for (int r = 0; r < k; ++r) {
                 size_t q = (size_t)s * k + r;
-                if (slot[q] < 0 || idx[q] != e)
+                if (slot[q] < 0 || serve[q] != e)
                     continue;
                 const double *a = a_all + q * h;
                 const double *du = du_all + q * h;
@@ -544,6 +632,8 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
     free(psum);
     free(a_all);
     free(du_all);
+    free(serve);
+    free(acc_e);
 }
 
 /* Backward entries computed one by one, for full-size checks (same chain
@@ -554,7 +644,7 @@ void oracle_layer_backward(int S, int d, int h, int E, int k, int C,
  *   weight-gradient entries: kind 1 = dW1[e,a,b] (a < h, b < d), 2 = dW2[e,a,b]
  *   (a < d, b < h), 3 = db1[e,a], 4 = db2[e,a], each a sum over the kept
  *   assignments of expert e. */
-void oracle_backward_entries(int S, int d, int h, int E, int k, int C,
+void oracle_backward_entries(int S, int d, int h, int E, int k, int C, int reroute,
                              const void *x, int dtype, const float *wg, const float *logits,
                              const void *w1, const void *b1, const void *w2, const void *b2,
                              const void *dy, double g_aux, double g_z,
@@ -570,6 +660,12 @@ void oracle_backward_entries(int S, int d, int h, int E, int k, int C,
     double *psum = (double *)malloc(sizeof(double) * (size_t)E);
     double losses[2];
     oracle_route(S, E, k, C, logits, idx, w, slot, counts, lse, psum, losses);
+    int32_t *serve = (int32_t *)malloc(sizeof(int32_t) * ((size_t)S * k + 1));
+    int32_t *acc_e = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (reroute)
+        oracle_reroute(S, E, k, C, logits, idx, serve, slot, acc_e);
+    else
+        memcpy(serve, idx, sizeof(int32_t) * (size_t)S * k);
 
     /* dx rows */
     #pragma omp parallel
@@ -590,7 +686,7 @@ void oracle_backward_entries(int S, int d, int h, int E, int k, int C,
                 dwr[r] = 0.0;
                 if (slot[q] < 0)
                     continue;
-                int e = idx[q];
+                int e = serve[q];
                 for (int j = 0; j < h; ++j) {
                     double acc = 0.0;
                     for (int i = 0; i < d; ++i)
@@ -662,7 +758,7 @@ void oracle_backward_entries(int S, int d, int h, int E, int k, int C,
         for (int s = 0; s < S; ++s) {
             for (int r = 0; r < k; ++r) {
                 size_t q = (size_t)s * k + r;
-                if (slot[q] < 0 || idx[q] != e)
+                if (slot[q] < 0 || serve[q] != e)
                     continue;
                 if (kind[t] == 2 || kind[t] == 4) {
                     double dO = w[q] * act_at(dy, dtype, (size_t)s * d + ka);
@@ -703,4 +799,6 @@ void oracle_backward_entries(int S, int d, int h, int E, int k, int C,
     free(w);
     free(lse);
     free(psum);
+    free(serve);
+    free(acc_e);
 }
