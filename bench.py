@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="balanced_bf16", choices=mw.ORDER)
     ap.add_argument("--dropless", action="store_true",
                     help="no capacity limit: compact [S*k,d] expert segments, no drops")
+    ap.add_argument("--reroute", action="store_true",
+                    help="offer dropped assignments to the tokens' next-ranked experts")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: forward + moe_layer_backward")
     ap.add_argument("--ep-share", default=None, choices=list(mw.EP_SHARES),
@@ -101,6 +103,13 @@ def algorithmic_work(w: mw.Workload, occ: np.ndarray, kept: int) -> dict:
     }
 
 
+def filled_rows(counts: np.ndarray, C: int, k: int) -> np.ndarray:
+    """Rows each expert holds: min(assignments, C), plus the accepted
+    re-routed assignments when counts carries that extra row."""
+    occ = np.minimum(counts[:k].sum(0), C)
+    return occ + counts[k] if counts.shape[0] > k else occ
+
+
 def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float, backward=False) -> dict:
     import oracle
     host = {n: mw.to_numpy(t) for n, t in inputs.items()}
@@ -112,15 +121,16 @@ def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float, backward=False) 
         if backward:
             lg = oracle.logits(host["x"][:n], host["wg"], host["bg"])
             oracle.layer(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
-                         host["w2"], host["b2"], w.k, max(C, 1), lg=lg)
+                         host["w2"], host["b2"], w.k, max(C, 1), lg=lg, reroute=w.reroute)
             oracle.layer_backward(host["x"][:n], host["wg"], host["w1"], host["b1"], host["w2"],
-                                  host["b2"], w.k, max(C, 1), lg, dy[:n], 0.01, 0.001)
+                                  host["b2"], w.k, max(C, 1), lg, dy[:n], 0.01, 0.001,
+                                  reroute=w.reroute)
         elif w.dropless:
             oracle.layer_dropless(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
                                   host["w2"], host["b2"], w.k)
         else:
             oracle.layer(host["x"][:n], host["wg"], host["bg"], host["w1"], host["b1"],
-                         host["w2"], host["b2"], w.k, C)
+                         host["w2"], host["b2"], w.k, C, reroute=w.reroute)
         return time.perf_counter() - t0
 
     n0 = min(w.S, 256)
@@ -132,7 +142,8 @@ def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float, backward=False) 
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {w.S} tokens of the same workload (same E, d, h, k, "
                       + ("dropless routing" if w.dropless else
-                         "capacity_factor; C scaled with the sample")
+                         "capacity_factor; C scaled with the sample"
+                         + (", overflow re-routing" if w.reroute else ""))
                       + "), full fp64 oracle layer from logits to y"
                       + (" plus its backward" if backward else "") + f", {t:.1f} s"}
 
@@ -151,11 +162,16 @@ def main():
         print(json.dumps(out), flush=True)
         return
     w = mw.get(a.workload)
+    if a.dropless and a.reroute:
+        print("--dropless drops nothing: --reroute does not apply", file=sys.stderr)
+        sys.exit(2)
     if a.dropless:
         w = w.with_(dropless=True, name=w.name + "_dropless")
+    if a.reroute:
+        w = w.with_(reroute=True, name=w.name + "_reroute")
     inputs = mw.generate(w, "cuda")
     cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype,
-                     dropless=w.dropless)
+                     dropless=w.dropless, reroute=w.reroute)
     if a.backward:
         out = bench_training(a, w, inputs, cfg)
         if a.copy_calibration_mb > 0:
@@ -218,7 +234,7 @@ def main():
     probe.forward(x)
     torch.cuda.synchronize()
     counts = probe.counts.cpu().numpy()
-    occ = np.minimum(counts.sum(0), probe.C)
+    occ = filled_rows(counts, probe.C, w.k)
     kept = int(occ.sum())
     aux, z = (float(v) for v in probe.losses.cpu().numpy())
     drops = int((probe.slot < 0).sum().item())
@@ -272,7 +288,7 @@ def main():
         "config": {"workload": w.name, "S": w.S, "d_model": w.d, "d_ff": w.h, "E": w.E,
                    "k": w.k, "capacity_factor": None if w.dropless else w.capacity_factor,
                    "C": None if w.dropless else probe_C(cfg), "dropless": w.dropless,
-                   "seed": w.seed},
+                   "reroute": w.reroute, "seed": w.seed},
         "roofline": roof,
         "ffn_mfma_frac": ffn_flops / ffn_s / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),
         "gemm_us": gemm_us,
@@ -281,6 +297,7 @@ def main():
                          f"(each recorded event adds queue time between two kernels)",
         "stage_rates": stage_frac,
         "routing": {"kept": kept, "dropped": drops, "nonempty_experts": int((occ > 0).sum()),
+                    "rerouted": int(counts[w.k].sum()) if w.reroute else 0,
                     "aux": aux, "z": z},
         "wall_s": wall,
     }
@@ -458,7 +475,7 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
     bwd_ms = float(np.mean([ev[0].elapsed_time(ev[-1]) for ev in evs]))
 
     counts = layer.counts.cpu().numpy()
-    occ = np.minimum(counts.sum(0), layer.C)
+    occ = filled_rows(counts, layer.C, w.k)
     kept = int(occ.sum())
     nonempty = int((occ > 0).sum())
     es = 2
@@ -506,7 +523,7 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
                    "d_ff": h, "E": E, "k": w.k,
                    "capacity_factor": None if w.dropless else w.capacity_factor,
                    "C": None if w.dropless else layer.C, "dropless": w.dropless,
-                   "seed": w.seed},
+                   "reroute": w.reroute, "seed": w.seed},
         "roofline": roof,
         "backward_ms": bwd_ms,
         "backward_stage_us": stage_us,

@@ -45,7 +45,8 @@
  *     fp32;  W1 [E,h,d];  b1 [E,h];  W2 [E,d,h];  b2 [E,d];  xd, out [E,C,d]
  *     ([S*k,d] with MOE_CFG_DROPLESS);
  *     logits [S,E] fp32;  topk_idx, slot [S,k] int32;  topk_w [S,k] fp32;
- *     counts [k,E] int32 (assignments of rank r to expert e before capacity);
+ *     counts [k,E] int32 (assignments of rank r to expert e before capacity;
+ *     one more row with MOE_CFG_REROUTE);
  *     losses [2] fp32 = {aux, z}.
  *   Dtypes.  x, W1, b1, W2, b2, xd, out and y share act_dtype (fp32 or
  *     bf16, with fp32 accumulation).  Wg, bg, logits, topk_w and losses are
@@ -116,6 +117,24 @@ typedef struct moe_config {
  * removes. */
 #define MOE_CFG_DROPLESS 1u
 
+/* moe_config.flags: overflow re-routing (not with MOE_CFG_DROPLESS).  The
+ * pages allow overflowing tokens to be "routed to alternative experts"
+ * ("GShard: Scaling Giant Neural Networks with Conditional Computation"
+ * (blog), paragraph "Expert Capacity") and give no rule; this library's rule:
+ * after the capacity pass, the j-th dropped assignment of token s (dropped
+ * ranks in rank order) is offered to the token's (k+j)-th ranked expert (all
+ * E experts ordered by logit descending, index ascending; none when
+ * k + j >= E).  Offers take capacity after every real assignment, virtual
+ * rank by virtual rank (j = 0 for all tokens, then j = 1, ...), tokens in
+ * order; an offer is accepted while its expert holds fewer than C rows and is
+ * otherwise dropped for good.  An accepted assignment keeps its weight
+ * topk_w[s,r]; topk_idx[s,r] then names the expert that serves it and
+ * slot[s,r] its row there.  counts gains a row: counts [k+1,E], row k = the
+ * offers each expert accepted (rows 0..k-1 and the losses are unchanged).
+ * The backward differentiates the weights through the top-k logits, which it
+ * ranks again from `logits`. */
+#define MOE_CFG_REROUTE 2u
+
 /* moe_gate flag: read `logits` as an input instead of computing them from x,
  * Wg and bg (x, w_gate and gate_bias may then be NULL). */
 #define MOE_GATE_LOGITS_IN 1u
@@ -148,7 +167,7 @@ const char *moe_status_string(int32_t status);
  * Out: logits [S,E] fp32 (input with MOE_GATE_LOGITS_IN; may be NULL
  *      otherwise, then kept in ws), topk_idx [S,k], topk_w [S,k],
  *      slot [S,k] (-1 = dropped; with MOE_CFG_DROPLESS the global row in
- *      xd/out), counts [k,E], losses [2].
+ *      xd/out), counts [k,E] ([k+1,E] with MOE_CFG_REROUTE), losses [2].
  * Logits within a small margin of a top-k decision are re-evaluated in fp64
  * and rounded once to fp32, and the stored logits hold those values. */
 moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,

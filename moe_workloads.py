@@ -41,6 +41,7 @@ class Workload:
     gate_bias: str | None = None    # None or "zipf1.2"
     ffn_bias: str | None = None     # None or "zeros"
     dropless: bool = False          # no capacity limit, compact expert segments
+    reroute: bool = False           # dropped assignments offered to next-ranked experts
 
     @property
     def torch_dtype(self):

@@ -8,6 +8,7 @@ loudly when ``libmoe.so`` has not been built: there is no fallback.
 from ._lib import (  # noqa: F401
     MOE_BF16,
     MOE_CFG_DROPLESS,
+    MOE_CFG_REROUTE,
     MOE_F32,
     MOE_GATE_LOGITS_IN,
     MOE_NUM_BWD_EVENTS,

@@ -18,6 +18,7 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_GATE_LOGITS_IN = 1
 MOE_CFG_DROPLESS = 1
+MOE_CFG_REROUTE = 2
 MOE_NUM_STAGE_EVENTS = 9
 MOE_NUM_BWD_EVENTS = 9
 
@@ -52,15 +53,26 @@ class MoeConfig(ctypes.Structure):
     def dropless(self) -> bool:
         return bool(self.flags & MOE_CFG_DROPLESS)
 
+    @property
+    def reroute(self) -> bool:
+        return bool(self.flags & MOE_CFG_REROUTE)
+
+    @property
+    def count_rows(self) -> int:
+        """Rows of counts: k, or k + 1 with re-routing."""
+        return self.k + (1 if self.reroute else 0)
+
 
 def config(S, d_model, d_ff, E, k, capacity_factor=1.0, capacity=0, dtype="bf16",
-           dropless=False) -> MoeConfig:
+           dropless=False, reroute=False) -> MoeConfig:
     """Layer shape.  ``dropless``: no capacity limit; xd/out are compact
-    [S*k, d] expert segments and ``slot`` holds global rows."""
+    [S*k, d] expert segments and ``slot`` holds global rows.  ``reroute``:
+    dropped assignments are offered to the tokens' next-ranked experts."""
     dt = {"bf16": MOE_BF16, "f32": MOE_F32, torch.bfloat16: MOE_BF16,
           torch.float32: MOE_F32}[dtype]
     return MoeConfig(int(S), int(d_model), int(d_ff), int(E), int(k), int(capacity),
-                     float(capacity_factor), dt, MOE_CFG_DROPLESS if dropless else 0)
+                     float(capacity_factor), dt,
+                     (MOE_CFG_DROPLESS if dropless else 0) | (MOE_CFG_REROUTE if reroute else 0))
 
 
 _lib = None
@@ -183,7 +195,7 @@ def gate(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, loss
         _arg(topk_idx, "topk_idx", torch.int32, S * k),
         _arg(topk_w, "topk_w", torch.float32, S * k),
         _arg(slot, "slot", torch.int32, S * k),
-        _arg(counts, "counts", torch.int32, k * E),
+        _arg(counts, "counts", torch.int32, cfg.count_rows * E),
         _arg(losses, "losses", torch.float32, 2),
         MOE_GATE_LOGITS_IN if logits_in else 0, wsp, wsb, _stream(stream))
     _check(st, "moe_gate")
@@ -209,7 +221,7 @@ def expert_ffn(cfg, xd, counts, w1, b1, w2, b2, out, ws, stream=None):
     wsp, wsb = _ws(ws)
     st = library().moe_expert_ffn(
         ctypes.byref(cfg), _arg(xd, "xd", at, R * d),
-        _arg(counts, "counts", torch.int32, cfg.k * E),
+        _arg(counts, "counts", torch.int32, cfg.count_rows * E),
         _arg(w1, "w1", at, E * h * d), _arg(b1, "b1", at, E * h, required=False),
         _arg(w2, "w2", at, E * d * h), _arg(b2, "b2", at, E * d, required=False),
         _arg(out, "out", at, R * d), wsp, wsb, _stream(stream))
@@ -250,7 +262,7 @@ def layer_forward(cfg, x, w_gate, gate_bias, w1, b1, w2, b2, y, ws, logits=None,
         _arg(topk_idx, "topk_idx", torch.int32, S * k, required=False),
         _arg(topk_w, "topk_w", torch.float32, S * k, required=False),
         _arg(slot, "slot", torch.int32, S * k, required=False),
-        _arg(counts, "counts", torch.int32, k * E, required=False),
+        _arg(counts, "counts", torch.int32, cfg.count_rows * E, required=False),
         _arg(losses, "losses", torch.float32, 2, required=False),
         _arg(xd, "xd", at, R * d, required=False),
         _arg(out, "out", at, R * d, required=False),
@@ -281,7 +293,7 @@ def layer_backward(cfg, x, w_gate, w1, b1, w2, logits, topk_idx, topk_w, slot, c
         _arg(w2, "w2", at, E * d * h), _arg(logits, "logits", torch.float32, S * E),
         _arg(topk_idx, "topk_idx", torch.int32, S * k),
         _arg(topk_w, "topk_w", torch.float32, S * k), _arg(slot, "slot", torch.int32, S * k),
-        _arg(counts, "counts", torch.int32, k * E), _arg(out, "out", at, R * d),
+        _arg(counts, "counts", torch.int32, cfg.count_rows * E), _arg(out, "out", at, R * d),
         _arg(hidden, "hidden", at, R * h, required=False), _arg(dy, "dy", at, S * d),
         float(g_aux), float(g_z), _arg(dx, "dx", at, S * d),
         _arg(dw_gate, "dw_gate", torch.float32, E * d),

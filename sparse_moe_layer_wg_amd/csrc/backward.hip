@@ -80,11 +80,32 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, const float* __restrict__ dw,
     const int32_t* __restrict__ counts, float g_aux, float g_z, float* __restrict__ dl, int S,
-    int E, int k) {
+    int E, int k, bool topk_from_logits) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
     if (s >= S) return;
     const float* l = logits + (int64_t)s * E;
+    // the top-k the weights belong to: topk_idx, or (re-routing moved some
+    // assignments there) the top-k again from the logits, ranked by (logit
+    // descending, index ascending) as the router ranks them
+    int sel[kMaxK];
+    for (int r = 0; r < k; ++r) {
+        if (!topk_from_logits) {
+            sel[r] = topk_idx[(int64_t)s * k + r];
+            continue;
+        }
+        uint64_t best = 0;
+        for (int j = lane; j < E; j += kWave) {
+            bool used = false;
+            for (int q = 0; q < r; ++q) used |= sel[q] == j;
+            if (used) continue;
+            const uint64_t key = (static_cast<uint64_t>(float_order_key(l[j])) << 32) |
+                                 (0xffffffffu - static_cast<uint32_t>(j));
+            best = key > best ? key : best;
+        }
+        best = wave_max_u64(best);
+        sel[r] = (int)(0xffffffffu - __builtin_amdgcn_readfirstlane((uint32_t)best));
+    }
     float m = -INFINITY;
     for (int j = lane; j < E; j += kWave) m = fmaxf(m, l[j]);
 #pragma unroll
@@ -109,7 +130,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     float wdw = 0.f;
     for (int r = 0; r < k; ++r) wdw += topk_w[(int64_t)s * k + r] * dw[(int64_t)s * k + r];
     for (int r = 0; r < k; ++r) {
-        const int j = topk_idx[(int64_t)s * k + r];
+        const int j = sel[r];
         if ((j & (kWave - 1)) == lane)
             g[j] += topk_w[(int64_t)s * k + r] * (dw[(int64_t)s * k + r] - wdw);
     }
@@ -308,10 +329,11 @@ hipError_t launch_combine_bwd(const void* dy, const void* out, const int32_t* to
 
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                              const float* dw, const int32_t* counts, float g_aux, float g_z,
-                             float* dl, int S, int E, int k, hipStream_t st) {
+                             float* dl, int S, int E, int k, bool topk_from_logits,
+                             hipStream_t st) {
     if (S == 0) return hipSuccess;
     router_bwd_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
-        logits, topk_idx, topk_w, dw, counts, g_aux, g_z, dl, S, E, k);
+        logits, topk_idx, topk_w, dw, counts, g_aux, g_z, dl, S, E, k, topk_from_logits);
     return hipGetLastError();
 }
 

@@ -59,9 +59,23 @@ hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* his
 // exclusive prefix of occ over experts (compact rows), every segment cut to
 // end by row `rows` (the compact buffers' length).  m-tiles are bm rows high
 // and an expert's last one may take `extra` more rows (expert_mtiles).
+// With reroute, counts has a row k of accepted re-routed assignments, added
+// to the occupancy.
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int extra,
                             int32_t* occ, int32_t* mt_start, int32_t* seg, int rows,
-                            int32_t* ctr, int n_ctr, hipStream_t st);
+                            int32_t* ctr, int n_ctr, hipStream_t st, bool reroute = false);
+// Overflow re-routing after the capacity pass (padded rows only): offers of
+// dropped assignments to the tokens' next-ranked experts, taken in slot order
+// within the remaining capacity.  Moves accepted assignments in topk_idx /
+// slot (and inv when non-null), writes counts row k (accepted per expert),
+// raises occ, rebuilds the m-tile prefix (height bm) and zeroes n_ctr tile
+// counters.  Scratch: offer_e, offer_r [S,k], hist [E][k*nb], offers
+// [(k+1), E] int32.
+hipError_t launch_reroute(const float* logits, int32_t* topk_idx, int32_t* slot, int32_t* inv,
+                          int32_t* counts, int32_t* occ, int32_t* mt_start, int32_t* ctr,
+                          int n_ctr, int S, int E, int k, int nb, int C, int bm,
+                          int32_t* offer_e, int32_t* offer_r, int32_t* hist, int32_t* offers,
+                          hipStream_t st);
 // Zero losses and counts (empty input).
 hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st);
 
@@ -165,10 +179,12 @@ hipError_t launch_combine_bwd(const void* dy, const void* out, const int32_t* to
                               hipStream_t st);
 // Router backward: gradient of the logits dl [S,E] (fp32) from the top-k
 // weight gradient dw, the aux loss (weight g_aux, first-choice counts) and
-// the z-loss (weight g_z).
+// the z-loss (weight g_z).  topk_from_logits: the weights' top-k is ranked
+// again from the logits (topk_idx holds serving experts after re-routing).
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                              const float* dw, const int32_t* counts, float g_aux, float g_z,
-                             float* dl, int S, int E, int k, hipStream_t st);
+                             float* dl, int S, int E, int k, bool topk_from_logits,
+                             hipStream_t st);
 // Router side of the input gradient:
 //   dx[s, i] = bf16(sum_j dl[s, j] wg[j, i] + sum over kept r of dX[u(s,r), i])
 // the first sum on the bf16 MFMAs with a two-term split of dl and wg (relative

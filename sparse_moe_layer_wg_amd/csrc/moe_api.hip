@@ -15,6 +15,8 @@ struct Plan {
     int S, d, h, E, k, C, nb;
     bool bf16;
     bool dropless;  // compact expert segments, no drops (C = S bounds every expert)
+    bool reroute;   // dropped assignments offered to alternative experts
+    int crows;      // rows of counts: k, or k + 1 with re-routing
     size_t rows;    // rows of the dispatch buffer / expert output: E*C or S*k
     size_t es;      // bytes per activation element
 };
@@ -31,8 +33,10 @@ int row_limit(const Plan& p) { return p.dropless ? (int)p.rows : p.C; }
 // definition, UNSUPPORTED for valid shapes the kernels do not handle.
 moe_status make_plan(const moe_config* c, Plan* pl) {
     if (!c) return MOE_ERR_INVALID_ARG;
-    if (c->flags & ~MOE_CFG_DROPLESS) return MOE_ERR_INVALID_ARG;
+    if (c->flags & ~(MOE_CFG_DROPLESS | MOE_CFG_REROUTE)) return MOE_ERR_INVALID_ARG;
     const bool dropless = (c->flags & MOE_CFG_DROPLESS) != 0;
+    const bool reroute = (c->flags & MOE_CFG_REROUTE) != 0;
+    if (dropless && reroute) return MOE_ERR_INVALID_ARG;   // dropless drops nothing
     if (c->S < 0 || c->d_model < 1 || c->d_ff < 1 || c->E < 1 || c->k < 1 || c->k > c->E)
         return MOE_ERR_INVALID_ARG;
     if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -69,6 +73,8 @@ moe_status make_plan(const moe_config* c, Plan* pl) {
     pl->nb = (int)ceil_div(c->S, kTokBlock);
     pl->bf16 = bf16;
     pl->dropless = dropless;
+    pl->reroute = reroute;
+    pl->crows = c->k + (reroute ? 1 : 0);
     pl->rows = (size_t)rows;
     pl->es = bf16 ? 2 : 4;
     return MOE_OK;
@@ -87,7 +93,7 @@ constexpr int kTileCounters = 16;
 // with R = rows: E*C padded, S*k compact (dropless).
 struct Carve {
     size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, seg, ctr,
-        inv, wsplit;
+        inv, wsplit, offer_e, offer_r, rhist, roffers;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -105,7 +111,7 @@ Carve carve(const Plan& p) {
     c.idx = take((size_t)p.S * p.k * 4);
     c.w = take((size_t)p.S * p.k * 4);
     c.slot = take((size_t)p.S * p.k * 4);
-    c.counts = take((size_t)p.k * p.E * 4);
+    c.counts = take((size_t)p.crows * p.E * 4);
     c.losses = take(2 * 4);
     c.hist = take((size_t)p.E * p.k * p.nb * 4);
     c.ppart = take((size_t)p.nb * p.E * 4);
@@ -117,6 +123,12 @@ Carve carve(const Plan& p) {
     c.ctr = take(kTileCounters * 4);
     c.inv = take(p.rows * 4);
     c.wsplit = gate_uses_split(p.bf16, p.d) ? take((size_t)3 * p.E * p.d * 2) : o;
+    if (p.reroute) {
+        c.offer_e = take((size_t)p.S * p.k * 4);
+        c.offer_r = take((size_t)p.S * p.k * 4);
+        c.rhist = take((size_t)p.E * p.k * p.nb * 4);
+        c.roffers = take(((size_t)p.k + 1) * p.E * 4);
+    }
     c.route_end = o;
     c.H = take(p.rows * p.h * p.es);
     c.ffn_end = o;
@@ -186,6 +198,12 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
                                       gemm_block_m(p.bf16, p.S, p.E, p.k), losses, mt,
                                       at<int32_t>(ws, cv.seg), at<int32_t>(ws, cv.ctr),
                                       kTileCounters, st));
+    if (p.reroute)
+        MOE_TRY(launch_reroute(logits, topk_idx, slot, inv, counts, occ, mt,
+                               at<int32_t>(ws, cv.ctr), kTileCounters, p.S, p.E, p.k, p.nb, p.C,
+                               gemm_block_m(p.bf16, p.S, p.E, p.k), at<int32_t>(ws, cv.offer_e),
+                               at<int32_t>(ws, cv.offer_r), at<int32_t>(ws, cv.rhist),
+                               at<int32_t>(ws, cv.roffers), st));
     record(ev, 4, st);
     return MOE_OK;
 }
@@ -294,7 +312,7 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const float* w_gate,
     if (p.S > 0 && (logits_in ? !logits : (!x || !w_gate))) return MOE_ERR_INVALID_ARG;
     if (!logits_in && !aligned(x, 16)) return MOE_ERR_INVALID_ARG;
     if (p.S == 0) {
-        MOE_TRY(launch_zero_outputs(counts, p.k * p.E, losses, stream));
+        MOE_TRY(launch_zero_outputs(counts, p.crows * p.E, losses, stream));
         return MOE_OK;
     }
     if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
@@ -338,7 +356,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* xd, const int32_t* 
     const int bm = gemm_block_m(p.bf16, p.S, p.E, p.k);
     MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, bm, strip_rows(bm), occ, mt,
                              p.dropless ? seg : nullptr, (int)p.rows, ctr, kTileCounters,
-                             stream));
+                             stream, p.reroute));
     return run_ffn(p, xd, nullptr, w1, b1, w2, b2, out, occ, mt, seg, ctr, at<void>(ws, cv.H),
                    nullptr, stream);
 }
@@ -377,7 +395,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     hipEvent_t* ev = stage_events;
     record(ev, 0, stream);
     if (p.S == 0) {
-        MOE_TRY(launch_zero_outputs(counts, counts ? p.k * p.E : 0, losses, stream));
+        MOE_TRY(launch_zero_outputs(counts, counts ? p.crows * p.E : 0, losses, stream));
         for (int i = 1; i < MOE_NUM_STAGE_EVENTS; ++i) record(ev, i, stream);
         return MOE_OK;
     }
@@ -534,9 +552,11 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     // and the inverse slot map (row -> token)
     const int bm = gemm_block_m(true, p.S, p.E, p.k);
     MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, bm, strip_rows(bm), occ, mt_fwd,
-                             p.dropless ? seg : nullptr, (int)p.rows, ctr, kBwdCounters, stream));
+                             p.dropless ? seg : nullptr, (int)p.rows, ctr, kBwdCounters, stream,
+                             p.reroute));
     MOE_TRY(launch_occupancy(counts, p.E, p.k, p.C, 256, 0, occ, mt_bwd,
-                             p.dropless ? seg : nullptr, (int)p.rows, nullptr, 0, stream));
+                             p.dropless ? seg : nullptr, (int)p.rows, nullptr, 0, stream,
+                             p.reroute));
     MOE_TRY(launch_inverse_rows(topk_idx, slot, p.S, p.k, p.E, stride, limit, inv, stream));
     // the expert rows of x, written once: dW1's K-major operand reads them
     // as plain rows (a gather there would put a dependent index load in
@@ -574,7 +594,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     MOE_TRY(launch_combine_bwd(dy, out, topk_idx, slot, topk_w, G, dwk, p.S, p.d, p.k, p.E, stride,
                                limit, stream));
     MOE_TRY(launch_router_bwd(logits, topk_idx, topk_w, dwk, counts, g_aux, g_z, dl, p.S, p.E, p.k,
-                              stream));
+                              p.reroute, stream));
     record(ev, 3, stream);
 
     BwdGemmParams b{};

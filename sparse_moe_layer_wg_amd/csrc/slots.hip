@@ -82,15 +82,17 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hi
     __shared__ int s_rank_start[kMaxK + 1];
     __shared__ double s_red[256];
     const int e = blockIdx.x, tid = threadIdx.x;
-    double pa = 0.0;
-    for (int b = tid; b < nb; b += 256) pa += (double)ppart[(size_t)b * E + e];
-    s_red[tid] = pa;
-    __syncthreads();
-    for (int off = 128; off >= 1; off >>= 1) {
-        if (tid < off) s_red[tid] += s_red[tid + off];
+    if (ppart) {   // (absent for the re-routing offers)
+        double pa = 0.0;
+        for (int b = tid; b < nb; b += 256) pa += (double)ppart[(size_t)b * E + e];
+        s_red[tid] = pa;
         __syncthreads();
+        for (int off = 128; off >= 1; off >>= 1) {
+            if (tid < off) s_red[tid] += s_red[tid + off];
+            __syncthreads();
+        }
+        if (tid == 0) psum[e] = s_red[0];
     }
-    if (tid == 0) psum[e] = s_red[0];
     const int T = k * nb;
     int32_t* row = hist + (size_t)e * T;
     int carry = 0;
@@ -207,14 +209,21 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ occ,
                                                         int32_t* __restrict__ mt_start,
                                                         int32_t* __restrict__ seg, int rows,
-                                                        int32_t* __restrict__ ctr, int n_ctr) {
+                                                        int32_t* __restrict__ ctr, int n_ctr,
+                                                        bool reroute) {
     __shared__ int s_wave[4];
     const int tid = threadIdx.x;
     for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
     for (int e = tid; e < E; e += 256) {
         long long n = 0;
         for (int r = 0; r < k; ++r) n += counts[(size_t)r * E + e];
-        occ[e] = n < 0 ? 0 : n < C ? (int)n : C;
+        int o = n < 0 ? 0 : n < C ? (int)n : C;
+        if (reroute) {
+            // row k: re-routed assignments the expert accepted (within C)
+            const int a = counts[(size_t)k * E + e];
+            o += a < 0 ? 0 : a < C - o ? a : C - o;
+        }
+        occ[e] = o;
     }
     __syncthreads();  // each thread reads other threads' occ below
     if (seg) {
@@ -236,6 +245,135 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
         }
         __syncthreads();
     }
+    tile_prefix(occ, E, bm, extra, s_wave, mt_start, nullptr);
+}
+
+// ------------------------------------------------------------ re-routing
+// Overflow re-routing (the capacity paragraph of the GShard blog allows
+// overflowing tokens to go to alternative experts; the rule here is a
+// reading): the j-th dropped assignment of a token (dropped ranks in rank
+// order) is offered to the token's (k+j)-th ranked expert, by (logit
+// descending, index ascending).  Offers form virtual ranks j = 0..k-1 after
+// the k real ones and take capacity in the same order as real assignments
+// (virtual rank by virtual rank, tokens in order), so the tile histogram,
+// scan and in-tile ballot ranks of the capacity pass serve again.
+
+// Largest order key among experts not yet taken (wave-uniform); marks it.
+template <int EQ>
+__device__ __forceinline__ int next_ranked(const float (&v)[EQ], int E, int lane,
+                                           uint32_t& taken) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+        const int j = lane + kWave * q;
+        if (j < E && !((taken >> q) & 1u)) {
+            const uint64_t key = (static_cast<uint64_t>(float_order_key(v[q])) << 32) |
+                                 (0xffffffffu - static_cast<uint32_t>(j));
+            best = key > best ? key : best;
+        }
+    }
+    best = wave_max_u64(best);
+    const int j = (int)(0xffffffffu - __builtin_amdgcn_readfirstlane((uint32_t)best));
+    if ((j & (kWave - 1)) == lane) taken |= 1u << (j / kWave);
+    return j;
+}
+
+// One wave per token: the token's offers (expert, original rank) for virtual
+// ranks j < its dropped count, -1 elsewhere, and the offer histogram
+// hist[e][j*nb + b] (zero on entry).
+template <int EQ>
+__global__ __launch_bounds__(256) void reroute_offers_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ slot, int S, int E, int k, int nb, int32_t* __restrict__ offer_e,
+    int32_t* __restrict__ offer_r, int32_t* __restrict__ hist) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+    if (s >= S) return;
+    float v[EQ];
+#pragma unroll
+    for (int q = 0; q < EQ; ++q) {
+        const int j = lane + kWave * q;
+        v[q] = j < E ? logits[(size_t)s * E + j] : 0.f;
+    }
+    uint32_t taken = 0;   // the top-k are not alternatives
+    for (int r = 0; r < k; ++r) {
+        const int e = topk_idx[(size_t)s * k + r];
+        if ((e & (kWave - 1)) == lane) taken |= 1u << (e / kWave);
+    }
+    const int T = k * nb, b = s / kTokBlock;
+    int j = 0;
+    for (int r = 0; r < k; ++r) {
+        if (slot[(size_t)s * k + r] >= 0) continue;   // wave-uniform
+        const int e = k + j < E ? next_ranked<EQ>(v, E, lane, taken) : -1;
+        if (lane == 0) {
+            offer_e[(size_t)s * k + j] = e;
+            offer_r[(size_t)s * k + j] = r;
+            if (e >= 0) atomicAdd(&hist[(size_t)e * T + (size_t)j * nb + b], 1);
+        }
+        ++j;
+    }
+    if (lane == 0)
+        for (; j < k; ++j) {
+            offer_e[(size_t)s * k + j] = -1;
+            offer_r[(size_t)s * k + j] = -1;
+        }
+}
+
+// One block per token block, wave w takes virtual ranks w, w+4, ...: an offer
+// at position pos among its expert's offers (scanned tile base + stable
+// in-tile rank) is accepted when pos < C - occ[e]; the assignment then moves
+// to expert e, row occ[e] + pos (occ from the capacity pass).
+__global__ __launch_bounds__(256) void reroute_positions_kernel(
+    const int32_t* __restrict__ offer_e, const int32_t* __restrict__ offer_r,
+    const int32_t* __restrict__ hist_base, const int32_t* __restrict__ occ, int S, int E, int k,
+    int nb, int C, int nbits, int32_t* __restrict__ topk_idx, int32_t* __restrict__ slot,
+    int32_t* __restrict__ inv) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x, s = b * kTokBlock + lane;
+    const int T = k * nb;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int j = wave; j < k; j += 4) {
+        const int e = s < S ? offer_e[(size_t)s * k + j] : -1;
+        const bool has = e >= 0;
+        uint64_t same = __ballot(has);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool one = (e >> bit) & 1;
+            const uint64_t ones = __ballot(one);
+            same &= one ? ones : ~ones;
+        }
+        const int before = __popcll(same & lt_mask);
+        if (has) {
+            const int pos = hist_base[(size_t)e * T + (size_t)j * nb + b] + before;
+            const int o = occ[e];
+            if (pos < C - o) {
+                const int r = offer_r[(size_t)s * k + j];
+                topk_idx[(size_t)s * k + r] = e;
+                slot[(size_t)s * k + r] = o + pos;
+                if (inv) inv[(size_t)e * C + o + pos] = s;
+            }
+        }
+    }
+}
+
+// counts[k, e] = accepted offers = min(offers, C - occ[e]); occ[e] grows by
+// them; then the m-tile prefix again and the GEMM tile counters zeroed.
+__global__ __launch_bounds__(256) void reroute_occupancy_kernel(
+    const int32_t* __restrict__ offers, int E, int k, int C, int bm, int extra,
+    int32_t* __restrict__ counts,
+    int32_t* __restrict__ occ, int32_t* __restrict__ mt_start, int32_t* __restrict__ ctr,
+    int n_ctr) {
+    __shared__ int s_wave[4];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
+    for (int e = tid; e < E; e += 256) {
+        int n = 0;
+        for (int j = 0; j < k; ++j) n += offers[(size_t)j * E + e];
+        const int room = C - occ[e];
+        const int a = n < room ? n : room;
+        counts[(size_t)k * E + e] = a;
+        occ[e] += a;
+    }
+    __syncthreads();
     tile_prefix(occ, E, bm, extra, s_wave, mt_start, nullptr);
 }
 
@@ -287,15 +425,51 @@ hipError_t launch_positions_finalize(const int32_t* topk_idx, const int32_t* his
 
 hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, int extra,
                             int32_t* occ, int32_t* mt_start, int32_t* seg, int rows,
-                            int32_t* ctr, int n_ctr, hipStream_t st) {
+                            int32_t* ctr, int n_ctr, hipStream_t st, bool reroute) {
     occupancy_kernel<<<1, 256, 0, st>>>(counts, E, k, C, bm, extra, occ, mt_start, seg, rows,
-                                        ctr, n_ctr);
+                                        ctr, n_ctr, reroute);
     return hipGetLastError();
 }
 
 hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st) {
     const int n = n_counts > 2 ? n_counts : 2;
     zero_outputs_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(counts, n_counts, losses);
+    return hipGetLastError();
+}
+
+hipError_t launch_reroute(const float* logits, int32_t* topk_idx, int32_t* slot, int32_t* inv,
+                          int32_t* counts, int32_t* occ, int32_t* mt_start, int32_t* ctr,
+                          int n_ctr, int S, int E, int k, int nb, int C, int bm,
+                          int32_t* offer_e, int32_t* offer_r, int32_t* hist, int32_t* offers,
+                          hipStream_t st) {
+    if (S == 0) return hipSuccess;
+    const size_t hn = (size_t)E * k * nb;
+    zero_outputs_kernel<<<(unsigned)ceil_div((int64_t)hn, 256), 256, 0, st>>>(hist, (int)hn,
+                                                                              nullptr);
+    const unsigned g = (unsigned)ceil_div(S, 4);
+    const int eq = (E + kWave - 1) / kWave;
+    if (eq <= 1) reroute_offers_kernel<1><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    else if (eq <= 2) reroute_offers_kernel<2><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    else if (eq <= 4) reroute_offers_kernel<4><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    else if (eq <= 8) reroute_offers_kernel<8><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    else if (eq <= 16) reroute_offers_kernel<16><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    else reroute_offers_kernel<32><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // scan the offer tiles per expert (offers per virtual rank into `offers`;
+    // the occupancy slot_scan writes is not needed here)
+    slot_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, offers, offers + (size_t)k * E,
+                                        nullptr, nullptr);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    reroute_positions_kernel<<<nb, 256, 0, st>>>(offer_e, offer_r, hist, occ, S, E, k, nb, C,
+                                                 nbits, topk_idx, slot, inv);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    reroute_occupancy_kernel<<<1, 256, 0, st>>>(offers, E, k, C, bm, strip_rows(bm), counts, occ,
+                                                mt_start, ctr, n_ctr);
     return hipGetLastError();
 }
 

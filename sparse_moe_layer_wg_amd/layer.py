@@ -34,7 +34,7 @@ class MoELayer:
             self.topk_idx = torch.empty((S, k), dtype=torch.int32, device=dev)
             self.topk_w = torch.empty((S, k), dtype=torch.float32, device=dev)
             self.slot = torch.empty((S, k), dtype=torch.int32, device=dev)
-            self.counts = torch.empty((k, E), dtype=torch.int32, device=dev)
+            self.counts = torch.empty((cfg.count_rows, E), dtype=torch.int32, device=dev)
             self.losses = torch.empty((2,), dtype=torch.float32, device=dev)
             # Without a dispatch buffer the first expert GEMM gathers token
             # rows straight from x (bf16); with one, x is first permuted into it.

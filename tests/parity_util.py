@@ -38,7 +38,7 @@ def as_f64(t) -> np.ndarray:
 
 def cfg_of(w: mw.Workload):
     return moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype,
-                      dropless=w.dropless)
+                      dropless=w.dropless, reroute=w.reroute)
 
 
 def run_layer(w: mw.Workload, inputs=None, dispatch_buffer=True):
@@ -57,7 +57,9 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
     """Compare one finished layer run with the oracle.  ``full`` runs the
     oracle over every slot; otherwise rows are sampled.  A dropless layer is
     routed with a capacity of S (never reached) and its slots are the compact
-    rows of the oracle's (expert, rank, token) order."""
+    rows of the oracle's (expert, rank, token) order.  With re-routing the
+    layer's topk_idx names each assignment's serving expert (the oracle's
+    ``serve``) and counts has the extra row of accepted offers."""
     rep = {} if report is None else report
     S, E, k = w.S, w.E, w.k
     C = layer.C
@@ -66,10 +68,10 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
     tol = TOL[w.dtype]
 
     # routing from the GPU's own fp32 logits: integer outputs bit-exact
-    r = oracle.route(layer.logits.cpu().numpy(), k, C)
+    r = oracle.route(layer.logits.cpu().numpy(), k, C, w.reroute)
     idx = layer.topk_idx.cpu().numpy()
     slot = layer.slot.cpu().numpy()
-    assert np.array_equal(idx, r["idx"]), "top-k indices differ from the oracle"
+    assert np.array_equal(idx, r["serve"]), "top-k (serving) indices differ from the oracle"
     if w.dropless:
         assert (r["slot"] >= 0).all()
         assert np.array_equal(slot, oracle.compact_rows(r["idx"], E)), \
@@ -79,12 +81,14 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
     host = _check_routing_outputs(w, inputs, layer, r, rep)
     rep["drops"] = int((slot < 0).sum())
 
-    occ = oracle.occupancy(r["counts"], C)
+    if w.reroute:
+        rep["rerouted"] = int((r["serve"] != r["idx"]).sum())
+    occ = oracle.occupancy(r["counts"], C, k)
     xd_gpu = layer.xd
     out_gpu = layer.out
     y_gpu = as_f64(layer.y)
     if full:
-        xd_or = oracle.dispatch(host["x"], r["idx"], r["slot"], E, C)
+        xd_or = oracle.dispatch(host["x"], r["serve"], r["slot"], E, C)
         filled = np.arange(C)[None, :] < occ[:, None]
         if xd_gpu is not None:
             xd_h = mw.to_numpy(xd_gpu)
@@ -92,7 +96,7 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
         out_or = oracle.expert_ffn(xd_or, occ, host["w1"], host["b1"], host["w2"], host["b2"])
         rep["out_rel"] = rel_fro(as_f64(out_gpu)[filled], out_or[filled])
         assert rep["out_rel"] <= tol, rep
-        y_or = oracle.combine(out_or, r["idx"], r["slot"], r["w"], S)
+        y_or = oracle.combine(out_or, r["serve"], r["slot"], r["w"], S)
         rep["y_rel"] = rel_fro(y_gpu, y_or)
         assert rep["y_rel"] <= tol, rep
         dropped_all = (r["slot"] < 0).all(axis=1)
@@ -112,10 +116,10 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
         for rr in range(k):
             c = r["slot"][s, rr]
             if c >= 0:
-                row = mw.to_numpy(xd_gpu[r["idx"][s, rr], c])
+                row = mw.to_numpy(xd_gpu[r["serve"][s, rr], c])
                 assert np.array_equal(row, host["x"][s]), "dispatch row differs"
     y_or = oracle.token_output(tok, host["x"], host["w1"], host["b1"], host["w2"], host["b2"],
-                               r["idx"], r["slot"], r["w"])
+                               r["serve"], r["slot"], r["w"])
     rep["y_rel"] = rel_fro(y_gpu[tok], y_or)
     assert rep["y_rel"] <= tol, rep
     return rep
@@ -142,8 +146,8 @@ def _check_routing_outputs(w, inputs, layer, r, rep):
     tau = 32.0 * np.sqrt(w.d) * 2.0 ** -24
     rep["logit_err_over_tau"] = rep["logit_max_abs_err"] / tau
     assert rep["logit_err_over_tau"] < 0.25, rep
-    r_or = oracle.route(lg_or, w.k, layer.C)
-    agree = np.all(layer.topk_idx.cpu().numpy() == r_or["idx"], axis=1)
+    r_or = oracle.route(lg_or, w.k, layer.C, w.reroute)
+    agree = np.all(layer.topk_idx.cpu().numpy() == r_or["serve"], axis=1)
     rep["topk_agreement"] = float(agree.mean())
     rep["topk_mismatches"] = int((~agree).sum())
     assert rep["topk_agreement"] >= AGREEMENT, rep

@@ -85,9 +85,10 @@ def test_invalid_configs_rejected_on_host():
     c.act_dtype = 7
     bad.append(c)
     c = moe.config(10, 64, 64, 4, 2)
-    c.flags = 2                            # unknown config flag
+    c.flags = 4                            # unknown config flag
     bad.append(c)
     bad.append(moe.config(10, 64, 64, 4, 2, capacity=3, dropless=True))
+    bad.append(moe.config(10, 64, 64, 4, 2, dropless=True, reroute=True))
     for cfg in bad:
         assert lib.moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 1
         assert lib.moe_capacity(ctypes.byref(cfg)) == -1

@@ -62,7 +62,7 @@ def check_backward(w, inputs, layer, grads, dy, g_aux, g_z):
     host = {n: mw.to_numpy(t) for n, t in inputs.items()}
     ref = oracle.layer_backward(host["x"], host["wg"], host["w1"], host["b1"], host["w2"],
                                 host["b2"], w.k, layer.C, layer.logits.cpu().numpy(),
-                                mw.to_numpy(dy), g_aux, g_z)
+                                mw.to_numpy(dy), g_aux, g_z, reroute=w.reroute)
     rep = {}
     for key in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2"):
         if grads[key] is None:
@@ -177,15 +177,17 @@ def test_backward_empty_input():
         assert not torch.any(t != 0), key
 
 
-@pytest.mark.parametrize("name,ntok", [("balanced_bf16", 24), ("deepseek_bf16", 6)])
-def test_backward_full_size_sampled(name, ntok):
+@pytest.mark.parametrize("name,ntok,reroute", [("balanced_bf16", 24, False),
+                                               ("deepseek_bf16", 6, False),
+                                               ("skewed_bf16", 16, True)])
+def test_backward_full_size_sampled(name, ntok, reroute):
     """Full-size workloads in the training benchmark's configuration (fused
     gather in the forward, the benchmark's loss weights).  dx rows of sampled
     tokens and sampled entries of dW1, dW2, db1, db2 are computed one by one
     by the oracle; the router gradients dWg (sampled columns) and dbg come
     from the oracle's logit gradient for all tokens, given the forward's
-    expert outputs."""
-    w = mw.get(name)
+    expert outputs.  The skewed workload runs with overflow re-routing."""
+    w = mw.get(name).with_(reroute=reroute)
     print(f"\n[bwd full] {w}", flush=True)
     inputs, layer = run_layer(w, dispatch_buffer=False)
     g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
@@ -206,7 +208,7 @@ def test_backward_full_size_sampled(name, ntok):
                          int(rng.integers(nb))))
     rows, vals = oracle.backward_entries(host["x"], host["wg"], host["w1"], host["b1"],
                                          host["w2"], host["b2"], w.k, layer.C, lg, dy_h, g_aux,
-                                         g_z, tok, ents)
+                                         g_z, tok, ents, reroute=w.reroute)
     rep = {"dx_rows": rel_fro(as_f64(grads["dx"][torch.from_numpy(tok).cuda()]), rows)}
     gpu = {1: as_f64(grads["dw1"]), 2: as_f64(grads["dw2"]), 3: as_f64(grads["db1"]),
            4: as_f64(grads["db2"])}
@@ -218,9 +220,9 @@ def test_backward_full_size_sampled(name, ntok):
 
     # router: the logit gradient for every token from the forward's own
     # expert outputs (dw = dy . out row), then dbg and sampled dWg columns
-    r = oracle.route(lg, w.k, layer.C)
+    r = oracle.route(lg, w.k, layer.C, w.reroute)
     out = layer.out.reshape(-1, w.d)
-    slot, idx = r["slot"], r["idx"]
+    slot, idx = r["slot"], r["serve"]
     dwk = np.zeros((w.S, w.k))
     for s0 in range(0, w.S, 1024):
         sl = slice(s0, min(w.S, s0 + 1024))
@@ -230,7 +232,7 @@ def test_backward_full_size_sampled(name, ntok):
             u_t = torch.from_numpy(np.where(keep, u, 0)).cuda()
             o = as_f64(out[u_t])
             dwk[sl, rr] = np.where(keep, np.einsum("ij,ij->i", o, dy_h_f64(dy_h[sl])), 0.0)
-    dl = oracle.router_backward(lg, idx, r["w"], dwk, counts, g_aux, g_z)
+    dl = oracle.router_backward(lg, r["idx"], r["w"], dwk, counts[:w.k], g_aux, g_z)
     rep["dbg"] = rel_fro(as_f64(grads["dbg"]), dl.sum(0))
     cols = np.sort(rng.choice(w.d, 128, replace=False))
     x64 = dy_h_f64(host["x"][:, cols])
