@@ -69,13 +69,12 @@ hipError_t launch_occupancy(const int32_t* counts, int E, int k, int C, int bm, 
 // within the remaining capacity.  Moves accepted assignments in topk_idx /
 // slot (and inv when non-null), writes counts row k (accepted per expert),
 // raises occ, rebuilds the m-tile prefix (height bm) and zeroes n_ctr tile
-// counters.  Scratch: offer_e, offer_r [S,k], hist [E][k*nb], offers
-// [(k+1), E] int32.
+// counters.  Scratch: offer_e, offer_r [S,k], hist [E][k*nb] int32 (fully
+// written, no clearing needed).
 hipError_t launch_reroute(const float* logits, int32_t* topk_idx, int32_t* slot, int32_t* inv,
                           int32_t* counts, int32_t* occ, int32_t* mt_start, int32_t* ctr,
                           int n_ctr, int S, int E, int k, int nb, int C, int bm,
-                          int32_t* offer_e, int32_t* offer_r, int32_t* hist, int32_t* offers,
-                          hipStream_t st);
+                          int32_t* offer_e, int32_t* offer_r, int32_t* hist, hipStream_t st);
 // Zero losses and counts (empty input).
 hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hipStream_t st);
 

@@ -93,7 +93,7 @@ constexpr int kTileCounters = 16;
 // with R = rows: E*C padded, S*k compact (dropless).
 struct Carve {
     size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, seg, ctr,
-        inv, wsplit, offer_e, offer_r, rhist, roffers;
+        inv, wsplit, offer_e, offer_r, rhist;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -127,7 +127,6 @@ Carve carve(const Plan& p) {
         c.offer_e = take((size_t)p.S * p.k * 4);
         c.offer_r = take((size_t)p.S * p.k * 4);
         c.rhist = take((size_t)p.E * p.k * p.nb * 4);
-        c.roffers = take(((size_t)p.k + 1) * p.E * 4);
     }
     c.route_end = o;
     c.H = take(p.rows * p.h * p.es);
@@ -202,8 +201,7 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
         MOE_TRY(launch_reroute(logits, topk_idx, slot, inv, counts, occ, mt,
                                at<int32_t>(ws, cv.ctr), kTileCounters, p.S, p.E, p.k, p.nb, p.C,
                                gemm_block_m(p.bf16, p.S, p.E, p.k), at<int32_t>(ws, cv.offer_e),
-                               at<int32_t>(ws, cv.offer_r), at<int32_t>(ws, cv.rhist),
-                               at<int32_t>(ws, cv.roffers), st));
+                               at<int32_t>(ws, cv.offer_r), at<int32_t>(ws, cv.rhist), st));
     record(ev, 4, st);
     return MOE_OK;
 }

@@ -82,17 +82,15 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hi
     __shared__ int s_rank_start[kMaxK + 1];
     __shared__ double s_red[256];
     const int e = blockIdx.x, tid = threadIdx.x;
-    if (ppart) {   // (absent for the re-routing offers)
-        double pa = 0.0;
-        for (int b = tid; b < nb; b += 256) pa += (double)ppart[(size_t)b * E + e];
-        s_red[tid] = pa;
+    double pa = 0.0;
+    for (int b = tid; b < nb; b += 256) pa += (double)ppart[(size_t)b * E + e];
+    s_red[tid] = pa;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) s_red[tid] += s_red[tid + off];
         __syncthreads();
-        for (int off = 128; off >= 1; off >>= 1) {
-            if (tid < off) s_red[tid] += s_red[tid + off];
-            __syncthreads();
-        }
-        if (tid == 0) psum[e] = s_red[0];
     }
+    if (tid == 0) psum[e] = s_red[0];
     const int T = k * nb;
     int32_t* row = hist + (size_t)e * T;
     int carry = 0;
@@ -278,58 +276,123 @@ __device__ __forceinline__ int next_ranked(const float (&v)[EQ], int E, int lane
     return j;
 }
 
-// One wave per token: the token's offers (expert, original rank) for virtual
-// ranks j < its dropped count, -1 elsewhere, and the offer histogram
-// hist[e][j*nb + b] (zero on entry).
+// One block per 64-token routing tile, one wave per token at a time: the
+// token's offers (expert, original rank) for virtual ranks j < its dropped
+// count (-1 elsewhere), then the tile's offer histogram written whole into
+// hist[e][j*nb + b] (every entry, zeros included, so nothing is cleared
+// beforehand).  Dynamic LDS: k*E ints.
+constexpr int kOfferWaves = 16;
+
 template <int EQ>
-__global__ __launch_bounds__(256) void reroute_offers_kernel(
+__global__ __launch_bounds__(64 * kOfferWaves) void reroute_offers_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ slot, int S, int E, int k, int nb, int32_t* __restrict__ offer_e,
     int32_t* __restrict__ offer_r, int32_t* __restrict__ hist) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
-    if (s >= S) return;
-    float v[EQ];
+    extern __shared__ int s_h[];                  // [k][E] offers of this tile
+    __shared__ int s_off[kMaxK][kTokBlock];       // offered expert per (j, token)
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int b = blockIdx.x;
+    for (int i = tid; i < k * E; i += 64 * kOfferWaves) s_h[i] = 0;
+    for (int t = wave; t < kTokBlock; t += kOfferWaves) {
+        const int s = b * kTokBlock + t;           // wave-uniform
+        if (s >= S) {
+            if (lane < k) s_off[lane][t] = -1;
+            continue;
+        }
+        float v[EQ];
 #pragma unroll
-    for (int q = 0; q < EQ; ++q) {
-        const int j = lane + kWave * q;
-        v[q] = j < E ? logits[(size_t)s * E + j] : 0.f;
-    }
-    uint32_t taken = 0;   // the top-k are not alternatives
-    for (int r = 0; r < k; ++r) {
-        const int e = topk_idx[(size_t)s * k + r];
-        if ((e & (kWave - 1)) == lane) taken |= 1u << (e / kWave);
-    }
-    const int T = k * nb, b = s / kTokBlock;
-    int j = 0;
-    for (int r = 0; r < k; ++r) {
-        if (slot[(size_t)s * k + r] >= 0) continue;   // wave-uniform
-        const int e = k + j < E ? next_ranked<EQ>(v, E, lane, taken) : -1;
-        if (lane == 0) {
-            offer_e[(size_t)s * k + j] = e;
-            offer_r[(size_t)s * k + j] = r;
-            if (e >= 0) atomicAdd(&hist[(size_t)e * T + (size_t)j * nb + b], 1);
+        for (int q = 0; q < EQ; ++q) {
+            const int j = lane + kWave * q;
+            v[q] = j < E ? logits[(size_t)s * E + j] : 0.f;
         }
-        ++j;
-    }
-    if (lane == 0)
-        for (; j < k; ++j) {
-            offer_e[(size_t)s * k + j] = -1;
-            offer_r[(size_t)s * k + j] = -1;
+        uint32_t taken = 0;   // the top-k are not alternatives
+        for (int r = 0; r < k; ++r) {
+            const int e = topk_idx[(size_t)s * k + r];
+            if ((e & (kWave - 1)) == lane) taken |= 1u << (e / kWave);
         }
+        int j = 0;
+        for (int r = 0; r < k; ++r) {
+            if (slot[(size_t)s * k + r] >= 0) continue;   // wave-uniform
+            const int e = k + j < E ? next_ranked<EQ>(v, E, lane, taken) : -1;
+            if (lane == 0) {
+                offer_e[(size_t)s * k + j] = e;
+                offer_r[(size_t)s * k + j] = r;
+                s_off[j][t] = e;
+            }
+            ++j;
+        }
+        if (lane == 0)
+            for (; j < k; ++j) {
+                offer_e[(size_t)s * k + j] = -1;
+                offer_r[(size_t)s * k + j] = -1;
+                s_off[j][t] = -1;
+            }
+    }
+    __syncthreads();
+    if (tid < k * kTokBlock) {
+        const int e = s_off[tid / kTokBlock][tid % kTokBlock];
+        if (e >= 0) atomicAdd(&s_h[(tid / kTokBlock) * E + e], 1);
+    }
+    __syncthreads();
+    const size_t T = (size_t)k * nb;
+    for (int i = tid; i < k * E; i += 64 * kOfferWaves) {
+        const int j = i / E, e = i - j * E;
+        hist[(size_t)e * T + (size_t)j * nb + b] = s_h[i];
+    }
 }
 
-// One block per token block, wave w takes virtual ranks w, w+4, ...: an offer
-// at position pos among its expert's offers (scanned tile base + stable
-// in-tile rank) is accepted when pos < C - occ[e]; the assignment then moves
-// to expert e, row occ[e] + pos (occ from the capacity pass).
+// One block per expert: the expert's offers, in slot order (virtual rank,
+// then tile), get the rows after its o = occ[e] filled ones: hist becomes
+// o + exclusive position.  counts[k, e] = accepted = min(offers, C - o) and
+// occ[e] grows by it.
+__global__ __launch_bounds__(256) void reroute_scan_kernel(int32_t* __restrict__ hist, int E,
+                                                           int k, int nb, int C,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ occ) {
+    __shared__ int s_wave[4];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int T = k * nb;
+    int32_t* row = hist + (size_t)e * T;
+    const int o = occ[e];
+    int carry = 0;
+    for (int base = 0; base < T; base += 256) {
+        const int i = base + tid;
+        const int v = i < T ? row[i] : 0;
+        int total;
+        const int ex = block_exclusive_scan(v, s_wave, &total);
+        if (i < T) row[i] = o + carry + ex;
+        carry += total;
+    }
+    __syncthreads();   // every thread has read occ[e]
+    if (tid == 0) {
+        const int room = C - o;
+        const int a = carry < room ? carry : room;
+        counts[(size_t)k * E + e] = a;
+        occ[e] = o + a;
+    }
+}
+
+// Blocks 0..nb-1, one per routing tile, wave w taking virtual ranks w, w+4,
+// ...: an offer's row is its expert's scanned base plus its stable rank among
+// the tile's offers to that expert (ballots over the expert bits); it is
+// accepted when the row is below C, and the assignment moves there.  Block
+// nb rebuilds the m-tile prefix from the grown occupancies and zeroes the
+// n_ctr GEMM tile counters.
 __global__ __launch_bounds__(256) void reroute_positions_kernel(
     const int32_t* __restrict__ offer_e, const int32_t* __restrict__ offer_r,
-    const int32_t* __restrict__ hist_base, const int32_t* __restrict__ occ, int S, int E, int k,
-    int nb, int C, int nbits, int32_t* __restrict__ topk_idx, int32_t* __restrict__ slot,
-    int32_t* __restrict__ inv) {
+    const int32_t* __restrict__ hist_row, const int32_t* __restrict__ occ, int S, int E, int k,
+    int nb, int C, int nbits, int bm, int extra, int32_t* __restrict__ topk_idx,
+    int32_t* __restrict__ slot, int32_t* __restrict__ inv, int32_t* __restrict__ mt_start,
+    int32_t* __restrict__ ctr, int n_ctr) {
+    const int b = blockIdx.x;
+    if (b == nb) {
+        __shared__ int s_wave[4];
+        for (int i = threadIdx.x; i < n_ctr; i += 256) ctr[i] = 0;
+        tile_prefix(occ, E, bm, extra, s_wave, mt_start, nullptr);
+        return;
+    }
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x, s = b * kTokBlock + lane;
+    const int s = b * kTokBlock + lane;
     const int T = k * nb;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int j = wave; j < k; j += 4) {
@@ -343,38 +406,15 @@ __global__ __launch_bounds__(256) void reroute_positions_kernel(
         }
         const int before = __popcll(same & lt_mask);
         if (has) {
-            const int pos = hist_base[(size_t)e * T + (size_t)j * nb + b] + before;
-            const int o = occ[e];
-            if (pos < C - o) {
+            const int row = hist_row[(size_t)e * T + (size_t)j * nb + b] + before;
+            if (row < C) {
                 const int r = offer_r[(size_t)s * k + j];
                 topk_idx[(size_t)s * k + r] = e;
-                slot[(size_t)s * k + r] = o + pos;
-                if (inv) inv[(size_t)e * C + o + pos] = s;
+                slot[(size_t)s * k + r] = row;
+                if (inv) inv[(size_t)e * C + row] = s;
             }
         }
     }
-}
-
-// counts[k, e] = accepted offers = min(offers, C - occ[e]); occ[e] grows by
-// them; then the m-tile prefix again and the GEMM tile counters zeroed.
-__global__ __launch_bounds__(256) void reroute_occupancy_kernel(
-    const int32_t* __restrict__ offers, int E, int k, int C, int bm, int extra,
-    int32_t* __restrict__ counts,
-    int32_t* __restrict__ occ, int32_t* __restrict__ mt_start, int32_t* __restrict__ ctr,
-    int n_ctr) {
-    __shared__ int s_wave[4];
-    const int tid = threadIdx.x;
-    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
-    for (int e = tid; e < E; e += 256) {
-        int n = 0;
-        for (int j = 0; j < k; ++j) n += offers[(size_t)j * E + e];
-        const int room = C - occ[e];
-        const int a = n < room ? n : room;
-        counts[(size_t)k * E + e] = a;
-        occ[e] += a;
-    }
-    __syncthreads();
-    tile_prefix(occ, E, bm, extra, s_wave, mt_start, nullptr);
 }
 
 __global__ void zero_outputs_kernel(int32_t* counts, int n, float* losses) {
@@ -440,36 +480,32 @@ hipError_t launch_zero_outputs(int32_t* counts, int n_counts, float* losses, hip
 hipError_t launch_reroute(const float* logits, int32_t* topk_idx, int32_t* slot, int32_t* inv,
                           int32_t* counts, int32_t* occ, int32_t* mt_start, int32_t* ctr,
                           int n_ctr, int S, int E, int k, int nb, int C, int bm,
-                          int32_t* offer_e, int32_t* offer_r, int32_t* hist, int32_t* offers,
-                          hipStream_t st) {
+                          int32_t* offer_e, int32_t* offer_r, int32_t* hist, hipStream_t st) {
     if (S == 0) return hipSuccess;
-    const size_t hn = (size_t)E * k * nb;
-    zero_outputs_kernel<<<(unsigned)ceil_div((int64_t)hn, 256), 256, 0, st>>>(hist, (int)hn,
-                                                                              nullptr);
-    const unsigned g = (unsigned)ceil_div(S, 4);
+    const size_t lds = (size_t)k * E * sizeof(int);
     const int eq = (E + kWave - 1) / kWave;
-    if (eq <= 1) reroute_offers_kernel<1><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
-    else if (eq <= 2) reroute_offers_kernel<2><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
-    else if (eq <= 4) reroute_offers_kernel<4><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
-    else if (eq <= 8) reroute_offers_kernel<8><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
-    else if (eq <= 16) reroute_offers_kernel<16><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
-    else reroute_offers_kernel<32><<<g, 256, 0, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e, offer_r, hist);
+    auto offers = [&](auto kern) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        kern<<<nb, 64 * kOfferWaves, lds, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e,
+                                                offer_r, hist);
+    };
+    if (eq <= 1) offers(&reroute_offers_kernel<1>);
+    else if (eq <= 2) offers(&reroute_offers_kernel<2>);
+    else if (eq <= 4) offers(&reroute_offers_kernel<4>);
+    else if (eq <= 8) offers(&reroute_offers_kernel<8>);
+    else if (eq <= 16) offers(&reroute_offers_kernel<16>);
+    else offers(&reroute_offers_kernel<32>);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // scan the offer tiles per expert (offers per virtual rank into `offers`;
-    // the occupancy slot_scan writes is not needed here)
-    slot_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, offers, offers + (size_t)k * E,
-                                        nullptr, nullptr);
+    reroute_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, counts, occ);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    reroute_positions_kernel<<<nb, 256, 0, st>>>(offer_e, offer_r, hist, occ, S, E, k, nb, C,
-                                                 nbits, topk_idx, slot, inv);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    reroute_occupancy_kernel<<<1, 256, 0, st>>>(offers, E, k, C, bm, strip_rows(bm), counts, occ,
-                                                mt_start, ctr, n_ctr);
+    reroute_positions_kernel<<<nb + 1, 256, 0, st>>>(offer_e, offer_r, hist, occ, S, E, k, nb, C,
+                                                     nbits, bm, strip_rows(bm), topk_idx, slot,
+                                                     inv, mt_start, ctr, n_ctr);
     return hipGetLastError();
 }
 
