@@ -103,6 +103,18 @@ def algorithmic_work(w: mw.Workload, occ: np.ndarray, kept: int) -> dict:
     }
 
 
+ROTATE_BYTES = 512 * 2 ** 20
+
+
+def rotated(t: torch.Tensor, budget: int = ROTATE_BYTES) -> list:
+    """Identical copies of t at distinct addresses, enough that one pass over
+    them (at least 512 MiB) exceeds the 256 MB last-level cache: step i reads
+    copy i % len, so no step finds its inputs left in cache by the previous
+    one."""
+    n = max(1, min(16, -(-budget // max(1, t.numel() * t.element_size()))))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
 def filled_rows(counts: np.ndarray, C: int, k: int) -> np.ndarray:
     """Rows each expert holds: min(assignments, C), plus the accepted
     re-routed assignments when counts carries that extra row."""
@@ -182,6 +194,7 @@ def main():
         return
     layer = MoELayer.from_inputs(cfg, inputs, keep=False)
     x = inputs["x"]
+    xs = rotated(x)
     stream = torch.cuda.current_stream()
 
     def make_events(which):
@@ -192,8 +205,8 @@ def main():
                 e.record(stream)
         return evs
 
-    for _ in range(a.warmup):
-        layer.forward(x)
+    for i in range(a.warmup):
+        layer.forward(xs[i % len(xs)])
     # Inside the timed steps only the boundaries of the two expert GEMMs are
     # recorded (each recorded event costs a few microseconds between two
     # kernels); the full per-stage breakdown comes from separate steps below.
@@ -206,7 +219,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(a.steps):
-        layer.forward(x, events=step_events[i])
+        layer.forward(xs[i % len(xs)], events=step_events[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -222,7 +235,7 @@ def main():
     inst_events = [make_events(range(moe.MOE_NUM_STAGE_EVENTS)) for _ in range(n_inst)]
     torch.cuda.synchronize()
     for i in range(n_inst):
-        layer.forward(x, events=inst_events[i])
+        layer.forward(xs[i % len(xs)], events=inst_events[i])
     torch.cuda.synchronize()
     stage_us = {}
     for si, name in enumerate(STAGES):
@@ -300,6 +313,7 @@ def main():
                     "rerouted": int(counts[w.k].sum()) if w.reroute else 0,
                     "aux": aux, "z": z},
         "wall_s": wall,
+        "input_copies": len(xs),
     }
     if a.copy_calibration_mb > 0:
         out["copy_calibration_bytes"] = calibration_copy(a.copy_calibration_mb)
@@ -337,11 +351,13 @@ def bench_ep_share(a, sh) -> dict:
     ws = torch.empty(moe.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     cnt = torch.from_numpy(counts[None, :].astype(np.int32)).cuda()
 
-    def step():
-        moe.expert_ffn(cfg, inp["xd"], cnt, inp["w1"], None, inp["w2"], None, out, ws)
+    xs = rotated(inp["xd"])
 
-    for _ in range(a.warmup):
-        step()
+    def step(i):
+        moe.expert_ffn(cfg, xs[i % len(xs)], cnt, inp["w1"], None, inp["w2"], None, out, ws)
+
+    for i in range(a.warmup):
+        step(i)
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(a.steps)]
@@ -352,7 +368,7 @@ def bench_ep_share(a, sh) -> dict:
     t0.record(stream)
     for i in range(a.steps):
         evs[i][0].record(stream)
-        step()
+        step(i)
         evs[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -392,6 +408,7 @@ def bench_ep_share(a, sh) -> dict:
                    "d_ff": sh.h, "rows": rows, "seed": sh.seed},
         "roofline": roof,
         "wall_s": wall,
+        "input_copies": len(xs),
     }
     if not a.no_cpu_baseline:
         import oracle
@@ -442,7 +459,10 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
               db2=torch.empty((E, d), dtype=at, device=dev))
     stream = torch.cuda.current_stream()
 
-    def step(bwd_events=None):
+    xs, dys = rotated(x), rotated(dy)
+
+    def step(i, bwd_events=None):
+        x, dy = xs[i % len(xs)], dys[i % len(dys)]
         layer.forward(x)
         moe.layer_backward(cfg, x, inputs["wg"], inputs["w1"], inputs["b1"], inputs["w2"],
                            layer.logits, layer.topk_idx, layer.topk_w, layer.slot, layer.counts,
@@ -456,8 +476,8 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
             e.record(stream)
         return evs
 
-    for _ in range(a.warmup):
-        step()
+    for i in range(a.warmup):
+        step(i)
     evs = [make_events() for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -465,7 +485,7 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(a.steps):
-        step(evs[i])
+        step(i, evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -531,6 +551,7 @@ def bench_training(a, w: mw.Workload, inputs: dict, cfg) -> dict:
         (MFMA_PEAK_TFLOPS[w.dtype] * 1e12),
         "routing": {"kept": kept, "nonempty_experts": nonempty},
         "wall_s": wall,
+        "input_copies": len(xs),
     }
 
 
