@@ -59,6 +59,9 @@
  *     library never aborts and throws nothing across the ABI.
  *   Buffers.  Slots of xd/out past an expert's occupancy are left as they
  *     were (never read by later steps).  NaN/Inf inputs are not supported.
+ *   Alignment.  Activation-typed arrays (x, xd, out, y, W1, b1, W2, b2,
+ *     hidden, dy, dx and the expert weight gradients) and dw_gate start on
+ *     16-byte boundaries; a misaligned one is MOE_ERR_INVALID_ARG.
  *   Workspace.  `ws` is device scratch of at least moe_workspace_bytes()
  *     bytes, 256-byte aligned; its contents do not persist between calls.
  *     Calls that share a workspace must be ordered on one stream.
@@ -243,7 +246,10 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
  *   z:   dl[s,j] += g_z (2/S) lse_s p_sj;
  *   dWg = sum_s dl_s x_s^T;  dbg = sum_s dl_s;  dx_s += Wg^T dl_s.
  * Supported for bf16 activations with S*d*2 < 2^32 bytes (else
- * MOE_ERR_UNSUPPORTED), in capacity and dropless modes.
+ * MOE_ERR_UNSUPPORTED), in capacity, dropless and re-routing modes (with
+ * MOE_CFG_REROUTE, topk_idx names the serving experts: the expert side
+ * follows them, and the weights' logit gradient goes to the router's own
+ * top-k, ranked again from `logits`).
  * In:  x, w_gate, w1, b1 (NULL = 0), w2 as given to the forward; the
  *      forward's outputs logits, topk_idx, topk_w, slot, counts and out
  *      (the expert outputs, [E,C,d] or [S*k,d]); hidden: NULL (the hidden
@@ -254,8 +260,11 @@ moe_status moe_layer_forward(const moe_config *cfg, const void *x, const float *
  *      wanted), dw1 [E,h,d] act, db1 [E,h] act (NULL = not wanted),
  *      dw2 [E,d,h] act, db2 [E,d] act (NULL = not wanted).
  * Precision: fp32 accumulation everywhere; the hidden activations are the
- * forward's (bf16, saved or recomputed bit-identically), dO, du and the expert-side input
- * gradient are rounded to bf16 once; the router side is fp32.
+ * forward's (bf16, saved or recomputed bit-identically), dO, du and the
+ * expert-side input gradient are rounded to bf16 once.  dl is fp32; its
+ * products (dl Wg for dx, dl^T x for dWg) run on the bf16 MFMAs with dl, and
+ * for dx also Wg, split into hi + lo bf16 parts (relative error about 2^-16);
+ * dWg and dbg are fp32 sums over fixed token chunks (deterministic).
  * ws: at least moe_backward_workspace_bytes() bytes, 256-byte aligned.
  * stage_events: NULL, or MOE_NUM_BWD_EVENTS caller-created events recorded
  * on `stream` between the steps (NULL entries skipped). */

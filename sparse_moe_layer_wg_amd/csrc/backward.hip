@@ -136,86 +136,64 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     }
 }
 
-// dWg on the router side in fp32: C[j, i] = sum_s dl[s, j] x[s, i], 64x64
-// tiles, 4x4 results per thread (contiguous, read from LDS as float4), k-steps
-// of 16 tokens staged as [k][row].  The tokens are split into gridDim.z chunks
-// of kchunk: chunk z writes its partial sums to part + z*E*d, and the blocks
-// of column tile 0 also the partial column sums of dl to pdbg + z*E (both
-// summed in a fixed order by router_dw_reduce_kernel).
-constexpr int RT = 64, RK = 16;
-__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
-                                                        const bf16_t* __restrict__ x,
-                                                        float* __restrict__ part,
-                                                        float* __restrict__ pdbg, int S, int d,
-                                                        int E, int kchunk) {
-    __shared__ __attribute__((aligned(16))) float As[RK][RT];
-    __shared__ __attribute__((aligned(16))) float Bs[RK][RT];
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    const int m0 = blockIdx.y * RT, n0 = blockIdx.x * RT;
-    const int kbeg = blockIdx.z * kchunk;
-    const int K = min(S, kbeg + kchunk);
-    float acc[4][4];
+// dWg and dbg from the chunked weight-gradient GEMM over [dl_hi | dl_lo]:
+// part [nchunk][2E'][d] and bpart [nchunk][2E'] hold each token chunk's
+// products with the hi and the lo plane; both planes of every chunk are
+// added in chunk order (fixed, so the sums are deterministic).
+__global__ __launch_bounds__(256) void router_dw_sum_kernel(const float* __restrict__ part,
+                                                            const float* __restrict__ bpart,
+                                                            int nchunk, int E, int Ep, int d,
+                                                            float* __restrict__ dwg,
+                                                            float* __restrict__ dbg) {
+    // 64 four-column outputs per block (d is a multiple of 16); thread group
+    // g of 4 adds chunks [g*nchunk/4, (g+1)*nchunk/4) in order, then group
+    // 0 adds the four group sums in order
+    __shared__ f32x4_t s_sum[4][64];
+    const int g = threadIdx.x >> 6, o = threadIdx.x & 63;
+    const int64_t i4 = (int64_t)blockIdx.x * 64 + o;
+    const int64_t n4 = (int64_t)E * d / 4, slab = (int64_t)2 * Ep * d, lo = (int64_t)Ep * d;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (i4 < n4) {
+        const int64_t i = 4 * i4;
+        const int c_beg = g * nchunk / 4, c_end = (g + 1) * nchunk / 4;
+        for (int c0 = c_beg; c0 < c_end; c0 += 4) {
+            // the loads of four chunks first, then the additions in order
+            f32x4_t v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u < c_end ? c0 + u : c_end - 1;
+                v[2 * u] = *reinterpret_cast<const f32x4_t*>(part + c * slab + i);
+                v[2 * u + 1] = *reinterpret_cast<const f32x4_t*>(part + c * slab + lo + i);
+            }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    float csum = 0.f;  // column tile 0: sum of dl[., m0 + tid] over the chunk
-    const int kk = tid / 16, cc = (tid % 16) * 4;  // this thread's loads
-    for (int k0 = kbeg; k0 < K; k0 += RK) {
-        __syncthreads();
-        const bool krow = k0 + kk < K;
+            for (int u = 0; u < 4; ++u)
+                if (c0 + u < c_end) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            As[kk][cc + c] = (krow && m0 + cc + c < E) ? dl[(int64_t)(k0 + kk) * E + m0 + cc + c]
-                                                       : 0.f;
-            Bs[kk][cc + c] =
-                (krow && n0 + cc + c < d) ? bf16_to_f32(x[(int64_t)(k0 + kk) * d + n0 + cc + c])
-                                          : 0.f;
-        }
-        __syncthreads();
-        if (blockIdx.x == 0 && tid < RT) {
-#pragma unroll
-            for (int q = 0; q < RK; ++q) csum += As[q][tid];
-        }
-#pragma unroll
-        for (int q = 0; q < RK; ++q) {
-            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&As[q][ty * 4]);
-            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&Bs[q][tx * 4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+                    for (int q = 0; q < 4; ++q) {
+                        acc[q] += v[2 * u][q];
+                        acc[q] += v[2 * u + 1][q];
+                    }
+                }
         }
     }
-    float* out = part + (int64_t)blockIdx.z * E * d;
+    s_sum[g][o] = acc;
+    __syncthreads();
+    if (g == 0 && i4 < n4) {
+        f32x4_t t = s_sum[0][o];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + ty * 4 + i;
-        if (m >= E) continue;
+        for (int u = 1; u < 4; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + tx * 4 + j;
-            if (n < d) out[(int64_t)m * d + n] = acc[i][j];
+            for (int q = 0; q < 4; ++q) t[q] += s_sum[u][o][q];
+        *reinterpret_cast<f32x4_t*>(dwg + 4 * i4) = t;
+    }
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (dbg && j < E) {
+        float a = 0.f;
+        for (int c = 0; c < nchunk; ++c) {
+            a += bpart[(int64_t)c * 2 * Ep + j];
+            a += bpart[(int64_t)c * 2 * Ep + Ep + j];
         }
-    }
-    if (blockIdx.x == 0 && tid < RT && m0 + tid < E) pdbg[(int64_t)blockIdx.z * E + m0 + tid] = csum;
-}
-
-// dwg = sum over chunks of the partial products, dbg likewise (chunk order).
-__global__ void router_dw_reduce_kernel(const float* __restrict__ part,
-                                        const float* __restrict__ pdbg, int nsplit, int E, int d,
-                                        float* __restrict__ dwg, float* __restrict__ dbg) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n = (int64_t)E * d;
-    if (i < n) {
-        float acc = 0.f;
-        for (int z = 0; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
-        dwg[i] = acc;
-    }
-    if (dbg && i < E) {
-        float acc = 0.f;
-        for (int z = 0; z < nsplit; ++z) acc += pdbg[(int64_t)z * E + i];
-        dbg[i] = acc;
+        dbg[j] = a;
     }
 }
 
@@ -229,16 +207,22 @@ __global__ void zero_bytes_kernel(uint32_t* __restrict__ p, size_t n) {
         reinterpret_cast<uint16_t*>(p)[2 * words] = 0u;
 }
 
-// Router part of dx on the bf16 MFMAs: dl [S,E] and Wg [E,d] are fp32; with
+// Router gradients on the bf16 MFMAs: dl [S,E] and Wg [E,d] are fp32; with
 // v = hi + lo (hi = bf16(v), lo = bf16(v - hi)) for both, dl Wg is taken as
-// dl_hi W_hi + dl_hi W_lo + dl_lo W_hi (the dropped lo*lo term is 2^-16 of the
+// dl_hi W_hi + dl_lo W_hi + dl_hi W_lo (the dropped lo*lo term is 2^-16 of the
 // product, far below the bf16 rounding of dx).  The three products become one
 // GEMM over K = 3E' (E' = E rounded up to 64, zero padded):
-//   A [S, 3E'] = [dl_hi | dl_hi | dl_lo],  B [3E', d] = [W_hi ; W_lo ; W_hi].
-// count1 receives S (the one "expert" of that GEMM).
+//   A [S, 3E'] = [dl_hi | dl_lo | dl_hi],  B [3E', d] = [W_hi ; W_hi ; W_lo].
+// The first 2E' columns of A also serve dWg = dl^T x = dl_hi^T x + dl_lo^T x
+// (x is bf16, so that split is the only approximation).  count1 receives S
+// (the one "expert" of the dx GEMM); occc the token count of each of the
+// nchunk chunks of kc tokens that the dWg GEMM takes as its "experts"; ctr
+// its 8 tile counters are zeroed.
 __global__ void router_dx_split_kernel(const float* __restrict__ dl, const float* __restrict__ wg,
                                        int S, int E, int Ep, int d, bf16_t* __restrict__ a,
-                                       bf16_t* __restrict__ b, int32_t* __restrict__ count1) {
+                                       bf16_t* __restrict__ b, int32_t* __restrict__ count1,
+                                       int32_t* __restrict__ occc, int nchunk, int kc,
+                                       int32_t* __restrict__ ctr) {
     const int64_t na = (int64_t)S * Ep, nb = (int64_t)Ep * d;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na + nb;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -250,8 +234,8 @@ __global__ void router_dx_split_kernel(const float* __restrict__ dl, const float
             const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
             bf16_t* row = a + s * 3 * Ep;
             row[j] = hi;
-            row[Ep + j] = hi;
-            row[2 * Ep + j] = lo;
+            row[Ep + j] = lo;
+            row[2 * Ep + j] = hi;
         } else {
             const int64_t q = i - na;
             const int j = (int)(q / d), c = (int)(q - (int64_t)j * d);
@@ -259,11 +243,18 @@ __global__ void router_dx_split_kernel(const float* __restrict__ dl, const float
             const bf16_t hi = f32_to_bf16(v);
             const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
             b[(int64_t)j * d + c] = hi;
-            b[((int64_t)Ep + j) * d + c] = lo;
-            b[((int64_t)2 * Ep + j) * d + c] = hi;
+            b[((int64_t)Ep + j) * d + c] = hi;
+            b[((int64_t)2 * Ep + j) * d + c] = lo;
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) count1[0] = S;
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) count1[0] = S;
+        if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+        for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+            const int64_t left = (int64_t)S - (int64_t)c * kc;
+            occc[c] = (int32_t)(left < kc ? left : kc);
+        }
+    }
 }
 
 // dx[s] = bf16(dxr[s] + sum over kept r of dX[u(s,r)]): one wave per token,
@@ -337,42 +328,82 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
     return hipGetLastError();
 }
 
-size_t router_dx_workspace(int S, int d, int E) {
-    const size_t Ep = (size_t)(E + 63) / 64 * 64;
-    size_t o = 0;
-    auto take = [&](size_t n) { o += (n + 255) & ~(size_t)255; };
-    take((size_t)S * 3 * Ep * 2);                        // A
-    take(3 * Ep * (size_t)d * 2);                        // B
-    take((size_t)S * d * 2);                             // dxr
-    take((2 + 1 + 2 + mtile_table_len(1, S, (size_t)S)) * 4);  // count, occ, m-tiles
-    take(8 * 4);                                         // tile counters
-    return o;
+namespace {
+// Token chunks of the dWg GEMM: about one output tile per compute unit, each
+// chunk a multiple of 64 tokens and at least 256.
+int router_dw_chunks(int S, int d, int E, int* kc) {
+    const int Ep = (E + 63) / 64 * 64;
+    const long long per = ceil_div(2 * Ep, 256) * ceil_div(d, 256);   // tiles per chunk
+    long long n = ceil_div((long long)device_cus(), per);
+    const long long most = ceil_div(S, 256);
+    if (n > most) n = most;
+    if (n < 1) n = 1;
+    long long c = ceil_div(ceil_div(S, n), 64) * 64;
+    if (c < 1) c = 64;
+    *kc = (int)c;
+    return (int)ceil_div(S, c);
 }
 
-hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
-                            const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
-                            int E, int k, int stride, int limit, void* work, hipStream_t st) {
-    if (S == 0) return hipSuccess;
-    const int Ep = (E + 63) / 64 * 64;
-    char* o = static_cast<char*>(work);
+// Workspace layout of the router gradients (byte offsets).
+struct RouterWork {
+    size_t A, B, dxr, tab, ctr, occc, ctr2, part, bpart, end;
+};
+RouterWork router_work(int S, int d, int E) {
+    const size_t Ep = (size_t)(E + 63) / 64 * 64;
+    int kc = 0;
+    const size_t nchunk = S > 0 ? (size_t)router_dw_chunks(S, d, E, &kc) : 0;
+    RouterWork w{};
+    size_t o = 0;
     auto take = [&](size_t n) {
-        char* at = o;
+        const size_t at = o;
         o += (n + 255) & ~(size_t)255;
         return at;
     };
-    bf16_t* A = reinterpret_cast<bf16_t*>(take((size_t)S * 3 * Ep * 2));
-    bf16_t* B = reinterpret_cast<bf16_t*>(take((size_t)3 * Ep * d * 2));
-    void* dxr = take((size_t)S * d * 2);
-    int32_t* tab = reinterpret_cast<int32_t*>(take((2 + 1 + 2 + mtile_table_len(1, S, (size_t)S)) * 4));
-    int32_t* ctr = reinterpret_cast<int32_t*>(take(8 * 4));
+    w.A = take((size_t)S * 3 * Ep * 2);
+    w.B = take(3 * Ep * (size_t)d * 2);
+    w.dxr = take((size_t)S * d * 2);
+    w.tab = take((2 + 1 + 2 + mtile_table_len(1, S, (size_t)S)) * 4);
+    w.ctr = take(8 * 4);
+    w.occc = take(nchunk * 4);
+    w.ctr2 = take(8 * 4);
+    w.part = take(nchunk * 2 * Ep * (size_t)d * 4);
+    w.bpart = take(nchunk * 2 * Ep * 4);
+    w.end = o;
+    return w;
+}
+}  // namespace
+
+size_t router_grads_workspace(int S, int d, int E) { return router_work(S, d, E).end; }
+
+hipError_t launch_router_grads(const float* dl, const float* wg, const void* x, const void* dX,
+                               const int32_t* topk_idx, const int32_t* slot, void* dx,
+                               float* dwg, float* dbg, int S, int d, int E, int k, int stride,
+                               int limit, void* work, hipStream_t st) {
+    if (S == 0) return hipSuccess;
+    const int Ep = (E + 63) / 64 * 64;
+    int kc = 0;
+    const int nchunk = router_dw_chunks(S, d, E, &kc);
+    const RouterWork w = router_work(S, d, E);
+    char* base = static_cast<char*>(work);
+    bf16_t* A = reinterpret_cast<bf16_t*>(base + w.A);
+    bf16_t* B = reinterpret_cast<bf16_t*>(base + w.B);
+    void* dxr = base + w.dxr;
+    int32_t* tab = reinterpret_cast<int32_t*>(base + w.tab);
+    int32_t* ctr = reinterpret_cast<int32_t*>(base + w.ctr);
+    int32_t* occc = reinterpret_cast<int32_t*>(base + w.occc);
+    int32_t* ctr2 = reinterpret_cast<int32_t*>(base + w.ctr2);
+    float* part = reinterpret_cast<float*>(base + w.part);
+    float* bpart = reinterpret_cast<float*>(base + w.bpart);
     int32_t* count1 = tab;   // [1]
     int32_t* occ1 = tab + 1; // [1]
     int32_t* mt1 = tab + 2;  // [2] prefix, then the m-tile experts
     const int64_t n = (int64_t)S * Ep + (int64_t)Ep * d;
     const unsigned g = (unsigned)(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192);
-    router_dx_split_kernel<<<g, 256, 0, st>>>(dl, wg, S, E, Ep, d, A, B, count1);
+    router_dx_split_kernel<<<g, 256, 0, st>>>(dl, wg, S, E, Ep, d, A, B, count1, occc, nchunk, kc,
+                                              ctr2);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // dx: one "expert" of S rows, K = 3E'
     err = launch_occupancy(count1, 1, 1, S, 256, 0, occ1, mt1, nullptr, S, ctr, 8, st);
     if (err != hipSuccess) return err;
     BwdGemmParams b{};
@@ -393,36 +424,29 @@ hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
     dx_assemble_kernel<<<(unsigned)ceil_div(S, kTokPerBlock), 256, 0, st>>>(
         static_cast<const u32x4_t*>(dxr), static_cast<const u32x4_t*>(dX), topk_idx, slot,
         static_cast<u32x4_t*>(dx), S, d / 8, k, E, stride, limit);
-    return hipGetLastError();
-}
-
-int router_dw_splits(int S, int d, int E) {
-    // enough token chunks for ~1024 blocks, chunks of at least 256 tokens
-    const long long tiles = ceil_div(d, RT) * ceil_div(E, RT);
-    long long n = ceil_div(1024, tiles);
-    const long long most = ceil_div(S, 256);
-    if (n > most) n = most;
-    return (int)(n < 1 ? 1 : n);
-}
-
-size_t router_dw_workspace(int S, int d, int E) {
-    const size_t n = (size_t)router_dw_splits(S, d, E);
-    return n * (size_t)E * d * 4 + n * (size_t)E * 4;
-}
-
-hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,
-                            int E, void* part, hipStream_t st) {
-    const int nsplit = router_dw_splits(S, d, E);
-    const int kchunk = (int)ceil_div(S, nsplit);
-    float* pw = static_cast<float*>(part);
-    float* pb = pw + (size_t)nsplit * E * d;
-    dim3 grid((unsigned)ceil_div(d, RT), (unsigned)ceil_div(E, RT), (unsigned)nsplit);
-    router_dw_kernel<<<grid, 256, 0, st>>>(dl, static_cast<const bf16_t*>(x), pw, pb, S, d, E,
-                                           kchunk);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    const int64_t n = (int64_t)E * d;
-    router_dw_reduce_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(pw, pb, nsplit, E, d,
-                                                                        dwg, dbg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // dWg: a weight gradient over token chunks ("experts" of kc rows), M = 2E'
+    // ([dl_hi | dl_lo], rows 3E' apart), N = d, fp32 partials and column sums
+    BwdGemmParams r{};
+    r.A = A;
+    r.lda = 3 * Ep;
+    r.B = x;
+    r.Cout = part;
+    r.bias_grad = bpart;
+    r.out_f32 = true;
+    r.occ = occc;
+    r.tile_ctr = ctr2;
+    r.E = nchunk;
+    r.C = kc;
+    r.M = 2 * Ep;
+    r.N = d;
+    r.rows = (size_t)S;
+    err = launch_bwd_gemm(r, true, false, st);
+    if (err != hipSuccess) return err;
+    const int64_t nblk = ceil_div((int64_t)E * d / 4, 64);
+    router_dw_sum_kernel<<<(unsigned)(nblk * 256 >= E ? nblk : ceil_div(E, 256)), 256, 0, st>>>(
+        part, bpart, nchunk, E, Ep, d, dwg, dbg);
     return hipGetLastError();
 }
 

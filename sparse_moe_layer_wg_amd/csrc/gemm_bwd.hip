@@ -134,7 +134,10 @@ __device__ __forceinline__ BwdTile decode_tile(const BwdGemmParams& p, int t, in
     return u;
 }
 
-template <bool WGRAD, bool MASK>
+// OUTF32 (weight gradients only): Cout and bias_grad in fp32, stored
+// straight from the accumulators (four consecutive columns per lane and
+// register quad), and A rows p.lda elements apart.
+template <bool WGRAD, bool MASK, bool OUTF32>
 __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
     __shared__ float s_bias[WGRAD ? NTH / 64 : 1][WGRAD ? BM : 1];
@@ -176,7 +179,8 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                     const size_t ar = u.row_e + k;
                     const size_t br =
                         p.b_rows ? (size_t)__builtin_amdgcn_readfirstlane(p.b_rows[ar]) : ar;
-                    va[r] = *reinterpret_cast<const uint2*>(Ac + ar * u.M * 2 +
+                    const size_t lda = OUTF32 && p.lda > 0 ? (size_t)p.lda : (size_t)u.M;
+                    va[r] = *reinterpret_cast<const uint2*>(Ac + ar * lda * 2 +
                                                             (uint32_t)u.ca * 2u);
                     vb[r] = *reinterpret_cast<const uint2*>(Bc + br * N * 2 +
                                                             (uint32_t)u.cb * 2u);
@@ -364,47 +368,67 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) s_bias[wave][4 * lane + c] = csum[c];
         }
-        char* ep = smem + wave * (WM * EPS);
+        if constexpr (OUTF32) {
+            float* __restrict__ Cf = static_cast<float*>(p.Cout) + (size_t)cur.e * p.M * N;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i) {
+                const int m = cur.m0 + wm * WM + i * 32 + frow;
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nl = j * 32 + 8 * q + 4 * fhalf;
-                    const f32x16_t& a = acc[i][j];
-                    *reinterpret_cast<uint2*>(ep + (i * 32 + frow) * EPS + nl * 2) =
-                        make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]),
-                                   pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
-                }
-        __builtin_amdgcn_wave_barrier();
-        constexpr int CPR = WNT * 2 / 16;   // 16-byte chunks per staged row
-        constexpr int NIT = WM * CPR / 64;  // chunks per lane
-        const int nw = cur.n0 + wn * WNT;
-        bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) +
-                                    (WGRAD ? (size_t)cur.e * p.M * N : cur.row_e * N);
-        const bf16_t* __restrict__ mk = MASK ? static_cast<const bf16_t*>(p.mask) + cur.row_e * N
-                                             : nullptr;
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = cur.n0 + wn * WNT + j * 32 + 8 * q + 4 * fhalf;
+                        if (m < cur.M && n < N) {
+                            f32x4_t v;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
-            const int m = cur.m0 + wm * WM + row, n = nw + ch * 8;
-            u32x4_t ov = *reinterpret_cast<const u32x4_t*>(ep + row * EPS + ch * 16);
-            if (m < cur.M && n < N) {
-                if constexpr (MASK) {
-                    // dReLU: keep the gradient where the forward's hidden
-                    // value is positive (bf16 > 0: sign clear, not zero)
-                    const u32x4_t hv =
-                        *reinterpret_cast<const u32x4_t*>(mk + (size_t)m * N + n);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const uint32_t hlo = hv[c] & 0xffffu, hhi = hv[c] >> 16;
-                        const uint32_t keep = ((hlo != 0u && hlo < 0x8000u) ? 0xffffu : 0u) |
-                                              ((hhi != 0u && hhi < 0x8000u) ? 0xffff0000u : 0u);
-                        ov[c] &= keep;
+                            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+                            *reinterpret_cast<f32x4_t*>(Cf + (size_t)m * N + n) = v;
+                        }
                     }
+            }
+        } else {
+            char* ep = smem + wave * (WM * EPS);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = j * 32 + 8 * q + 4 * fhalf;
+                        const f32x16_t& a = acc[i][j];
+                        *reinterpret_cast<uint2*>(ep + (i * 32 + frow) * EPS + nl * 2) =
+                            make_uint2(pack_bf16x2(a[4 * q], a[4 * q + 1]),
+                                       pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
+                    }
+            __builtin_amdgcn_wave_barrier();
+            constexpr int CPR = WNT * 2 / 16;   // 16-byte chunks per staged row
+            constexpr int NIT = WM * CPR / 64;  // chunks per lane
+            const int nw = cur.n0 + wn * WNT;
+            bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) +
+                                        (WGRAD ? (size_t)cur.e * p.M * N : cur.row_e * N);
+            const bf16_t* __restrict__ mk =
+                MASK ? static_cast<const bf16_t*>(p.mask) + cur.row_e * N : nullptr;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+                const int m = cur.m0 + wm * WM + row, n = nw + ch * 8;
+                u32x4_t ov = *reinterpret_cast<const u32x4_t*>(ep + row * EPS + ch * 16);
+                if (m < cur.M && n < N) {
+                    if constexpr (MASK) {
+                        // dReLU: keep the gradient where the forward's hidden
+                        // value is positive (bf16 > 0: sign clear, not zero)
+                        const u32x4_t hv =
+                            *reinterpret_cast<const u32x4_t*>(mk + (size_t)m * N + n);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint32_t hlo = hv[c] & 0xffffu, hhi = hv[c] >> 16;
+                            const uint32_t keep = ((hlo != 0u && hlo < 0x8000u) ? 0xffffu : 0u) |
+                                                  ((hhi != 0u && hhi < 0x8000u) ? 0xffff0000u : 0u);
+                            ov[c] &= keep;
+                        }
+                    }
+                    *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = ov;
                 }
-                *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = ov;
             }
         }
         if (bias) {
@@ -413,8 +437,11 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                 float v = 0.f;
 #pragma unroll
                 for (int w = 0; w < NTH / 64; ++w) v += s_bias[w][tid];
-                static_cast<bf16_t*>(p.bias_grad)[(size_t)cur.e * cur.M + cur.m0 + tid] =
-                    f32_to_bf16(v);
+                if constexpr (OUTF32)
+                    static_cast<float*>(p.bias_grad)[(size_t)cur.e * cur.M + cur.m0 + tid] = v;
+                else
+                    static_cast<bf16_t*>(p.bias_grad)[(size_t)cur.e * cur.M + cur.m0 + tid] =
+                        f32_to_bf16(v);
             }
         }
         t = tn;
@@ -437,12 +464,14 @@ hipError_t launch_bwd_gemm(const BwdGemmParams& p, bool wgrad, bool mask, hipStr
     const long long slots = (long long)(device_cus() / 8) * 8;
     const unsigned grid = (unsigned)(tiles < slots ? ceil_div(tiles, 8) * 8 : slots);
     if (grid == 0) return hipSuccess;
-    if (wgrad)
-        gemm_bwd_kernel<true, false><<<grid, NTH, 0, st>>>(p);
+    if (wgrad && p.out_f32)
+        gemm_bwd_kernel<true, false, true><<<grid, NTH, 0, st>>>(p);
+    else if (wgrad)
+        gemm_bwd_kernel<true, false, false><<<grid, NTH, 0, st>>>(p);
     else if (mask)
-        gemm_bwd_kernel<false, true><<<grid, NTH, 0, st>>>(p);
+        gemm_bwd_kernel<false, true, false><<<grid, NTH, 0, st>>>(p);
     else
-        gemm_bwd_kernel<false, false><<<grid, NTH, 0, st>>>(p);
+        gemm_bwd_kernel<false, false, false><<<grid, NTH, 0, st>>>(p);
     return hipGetLastError();
 }
 

@@ -163,6 +163,8 @@ struct BwdGemmParams {
     int32_t* tile_ctr;         // 8 counters, zero at launch
     int E, C, M, N, K;
     size_t rows;               // rows of the expert buffers (E*C or S*k)
+    int lda;                   // wgrad: row stride of A in elements (0: M)
+    bool out_f32;              // wgrad: Cout and bias_grad fp32 (else bf16)
 };
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, bool wgrad, bool mask, hipStream_t st);
 
@@ -184,21 +186,18 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
                              const float* dw, const int32_t* counts, float g_aux, float g_z,
                              float* dl, int S, int E, int k, bool topk_from_logits,
                              hipStream_t st);
-// Router side of the input gradient:
+// Router side of the gradients, on the bf16 MFMAs with two-term splits
+// (v = hi + lo, hi = bf16(v), lo = bf16(v - hi); relative error about 2^-16):
 //   dx[s, i] = bf16(sum_j dl[s, j] wg[j, i] + sum over kept r of dX[u(s,r), i])
-// the first sum on the bf16 MFMAs with a two-term split of dl and wg (relative
-// error about 2^-16, below dx's bf16 rounding); `work` holds
-// router_dx_workspace bytes.
-size_t router_dx_workspace(int S, int d, int E);
-hipError_t launch_router_dx(const float* dl, const float* wg, const void* dX,
-                            const int32_t* topk_idx, const int32_t* slot, void* dx, int S, int d,
-                            int E, int k, int stride, int limit, void* work, hipStream_t st);
-// Router weight gradient in fp32:
-//   dwg[j, i] = sum_s dl[s, j] x[s, i];  dbg[j] = sum_s dl[s, j]
-// (dwg over token chunks: `part` holds router_dw_workspace bytes of partials)
-size_t router_dw_workspace(int S, int d, int E);
-hipError_t launch_router_dw(const float* dl, const void* x, float* dwg, float* dbg, int S, int d,
-                            int E, void* part, hipStream_t st);
+//   dwg[j, i] = sum_s dl[s, j] x[s, i];   dbg[j] = sum_s dl[s, j]  (fp32;
+//   dbg may be NULL)
+// dwg runs as a weight-gradient GEMM over token chunks with fp32 partials,
+// summed in chunk order.  `work` holds router_grads_workspace bytes.
+size_t router_grads_workspace(int S, int d, int E);
+hipError_t launch_router_grads(const float* dl, const float* wg, const void* x, const void* dX,
+                               const int32_t* topk_idx, const int32_t* slot, void* dx,
+                               float* dwg, float* dbg, int S, int d, int E, int k, int stride,
+                               int limit, void* work, hipStream_t st);
 // Fill n bytes with zero (a kernel, so that it can sit in a captured graph).
 hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st);
 

@@ -443,7 +443,7 @@ constexpr int kBwdCounters = 40;
 //   operands and tables, H then dU [R,h], dO then dX
 //   [R,d], the dispatched rows of x [R,d]   (R = rows)
 struct BwdCarve {
-    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, rpart, rdx, H, G, X, end;
+    size_t occ, mt_fwd, mt_bwd, seg, ctr, inv, dw, dl, rgrad, H, G, X, end;
 };
 
 BwdCarve bwd_carve(const Plan& p) {
@@ -463,8 +463,7 @@ BwdCarve bwd_carve(const Plan& p) {
     c.inv = take(p.rows * 4);
     c.dw = take((size_t)p.S * p.k * 4);
     c.dl = take((size_t)p.S * p.E * 4);
-    c.rpart = take(router_dw_workspace(p.S, p.d, p.E));
-    c.rdx = take(router_dx_workspace(p.S, p.d, p.E));
+    c.rgrad = take(router_grads_workspace(p.S, p.d, p.E));
     c.H = take(p.rows * p.h * 2);
     c.G = take(p.rows * p.d * 2);
     c.X = take(p.rows * p.d * 2);
@@ -514,7 +513,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     if (!counts) return MOE_ERR_INVALID_ARG;
     if (!isfinite(g_aux) || !isfinite(g_z)) return MOE_ERR_INVALID_ARG;
     for (const void* q : {x, w1, b1, w2, out, hidden, dy, (const void*)dx, (const void*)dw1,
-                          (const void*)db1, (const void*)dw2, (const void*)db2})
+                          (const void*)db1, (const void*)dw2, (const void*)db2,
+                          (const void*)dw_gate})
         if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
     if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
     const BwdCarve cv = bwd_carve(p);
@@ -652,10 +652,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
     record(ev, 7, stream);
 
     // dx = dispatch backward + dl Wg; dWg = dl^T x; dbg = colsum dl
-    MOE_TRY(launch_router_dx(dl, w_gate, G, topk_idx, slot, dx, p.S, p.d, p.E, p.k, stride, limit,
-                             at<void>(ws, cv.rdx), stream));
-    MOE_TRY(launch_router_dw(dl, x, dw_gate, db_gate, p.S, p.d, p.E, at<void>(ws, cv.rpart),
-                             stream));
+    MOE_TRY(launch_router_grads(dl, w_gate, x, G, topk_idx, slot, dx, dw_gate, db_gate, p.S, p.d,
+                                p.E, p.k, stride, limit, at<void>(ws, cv.rgrad), stream));
     record(ev, 8, stream);
     return MOE_OK;
 }

@@ -165,14 +165,15 @@ def test_backward_validation_on_host():
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
     f = ctypes.c_float
 
-    def call(ws_bytes=need, g_aux=0.0, drop=None):
+    def call(ws_bytes=need, g_aux=0.0, drop=None, dw_gate=fake):
         args = [fake] * 13
         args[11] = None                                  # hidden: optional
         if drop is not None:
             args[drop] = None
-        return lib.moe_layer_backward(ctypes.byref(cfg), *args, f(g_aux), f(0.0), fake, fake,
+        return lib.moe_layer_backward(ctypes.byref(cfg), *args, f(g_aux), f(0.0), fake, dw_gate,
                                       None, fake, None, fake, None, fake, ws_bytes, None, None)
     assert call(ws_bytes=need - 1) == 3                 # workspace too small
+    assert call(dw_gate=ctypes.c_void_p((1 << 20) + 4)) == 1   # dw_gate not 16-byte aligned
     assert call(drop=12) == 1                           # dy missing
     assert call(drop=10) == 1                           # forward expert outputs missing
     assert call(g_aux=float("nan")) == 1                # loss weight not finite
