@@ -247,3 +247,70 @@ def test_backward_full_size_sampled(name, ntok, reroute):
 def dy_h_f64(a):
     """bf16 bit patterns (uint16) as float64."""
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_backward_replays_in_a_hip_graph():
+    """moe_layer_backward enqueues kernels only, so a forward + backward step
+    can be captured in a HIP graph: every replay, with new upstream
+    gradients and eager work between replays, equals an eager step bit for
+    bit."""
+    from sparse_moe_layer_wg_amd.layer import MoELayer
+    w = BWD[0]
+    inputs = _with_biases(w, mw.generate(w, "cuda"), w.seed + 100)
+    cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype)
+    layers = [MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False,
+                                   keep_hidden=True) for _ in range(2)]
+    dys = [torch.zeros((w.S, w.d), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    grads = [None, None]
+
+    def step(i):
+        layers[i].forward(inputs["x"])
+        grads[i] = run_backward_nosync(w, inputs, layers[i], dys[i], 0.7, 0.3,
+                                       hidden=layers[i].hidden, out=grads[i])
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step(1)                              # warm-up outside the capture (allocates)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(1)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    for rep in range(3):
+        dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        dys[1].copy_(dy)
+        dys[0].copy_(dy)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(0)
+        torch.cuda.synchronize()
+        for key in grads[0]:
+            if grads[0][key] is not None:
+                assert torch.equal(grads[0][key], grads[1][key]), (rep, key)
+
+
+def run_backward_nosync(w, inputs, layer, dy, g_aux, g_z, hidden=None, out=None):
+    """moe_layer_backward into the buffers of `out` (allocated when None),
+    without a host synchronisation (so that it can be captured)."""
+    cfg = layer.cfg
+    E, d, h = w.E, w.d, w.h
+    dev, at = "cuda", torch.bfloat16
+    if out is None:
+        out = dict(dx=torch.empty((w.S, d), dtype=at, device=dev),
+                   dwg=torch.empty((E, d), dtype=torch.float32, device=dev),
+                   dbg=torch.empty((E,), dtype=torch.float32, device=dev),
+                   dw1=torch.empty((E, h, d), dtype=at, device=dev),
+                   db1=torch.empty((E, h), dtype=at, device=dev),
+                   dw2=torch.empty((E, d, h), dtype=at, device=dev),
+                   db2=torch.empty((E, d), dtype=at, device=dev),
+                   ws=torch.empty(moe.backward_workspace_bytes(cfg), dtype=torch.uint8,
+                                  device=dev))
+    moe.layer_backward(cfg, inputs["x"], inputs["wg"], inputs["w1"], inputs["b1"], inputs["w2"],
+                       layer.logits, layer.topk_idx, layer.topk_w, layer.slot, layer.counts,
+                       layer.out, dy, out["dx"], out["dwg"], out["dw1"], out["dw2"], out["ws"],
+                       db_gate=out["dbg"], db1=out["db1"], db2=out["db2"], g_aux=g_aux, g_z=g_z,
+                       hidden=hidden)
+    return out

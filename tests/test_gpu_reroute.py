@@ -178,3 +178,36 @@ def test_reroute_full_size_sampled():
     assert rep["rerouted"] > 0
     del layer, inputs
     torch.cuda.empty_cache()
+
+
+def test_reroute_forward_replays_in_a_hip_graph():
+    """The re-routing pass enqueues kernels only, so a re-routing forward can
+    be captured in a HIP graph: every replay, with new token values and eager
+    work between replays, equals an eager run bit for bit."""
+    w = REROUTE_MID[0]
+    inputs = mw.generate(w, "cuda")
+    cfg = moe.config(w.S, w.d, w.h, w.E, w.k, w.capacity_factor, dtype=w.dtype, reroute=True)
+    eager = MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False)
+    graphed = MoELayer.from_inputs(cfg, inputs, keep=True, dispatch_buffer=False)
+    x_static = inputs["x"].clone()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graphed.forward(x_static)          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graphed.forward(x_static)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    for rep in range(4):
+        x_new = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        x_static.copy_(x_new)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager.forward(x_new)
+        torch.cuda.synchronize()
+        assert int(eager.counts[w.k].sum()) > 0, "the inputs must make re-routing happen"
+        for name in ("y", "topk_idx", "slot", "counts", "losses", "logits"):
+            assert torch.equal(getattr(graphed, name), getattr(eager, name)), (rep, name)
