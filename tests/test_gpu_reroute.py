@@ -211,3 +211,40 @@ def test_reroute_forward_replays_in_a_hip_graph():
         assert int(eager.counts[w.k].sum()) > 0, "the inputs must make re-routing happen"
         for name in ("y", "topk_idx", "slot", "counts", "losses", "logits"):
             assert torch.equal(getattr(graphed, name), getattr(eager, name)), (rep, name)
+
+
+# S, E, k, C: ragged S, E not a multiple of 64, tiny and large E, capacity 1
+REROUTE_ROUTE_CASES = [
+    (1, 2, 1, 1), (63, 3, 2, 5), (65, 8, 2, 16), (1000, 65, 3, 40), (777, 128, 2, 9),
+    (2048, 256, 8, 70), (300, 1000, 4, 2), (129, 2048, 8, 1), (500, 9, 7, 60),
+]
+
+
+@pytest.mark.parametrize("S,E,k,C", REROUTE_ROUTE_CASES)
+def test_reroute_route_from_logits_bit_exact(S, E, k, C):
+    """moe_gate with re-routing and MOE_GATE_LOGITS_IN on logits full of ties
+    (small integers and +-0): serving experts, rows and the counts with
+    their extra row equal the oracle's bit for bit, so alternative experts
+    are ranked exactly as the router ranks (logit descending, index
+    ascending, -0 equal to +0)."""
+    print(f"\n[rr route] S={S} E={E} k={k} C={C}", flush=True)
+    rng = np.random.default_rng(S * 7919 + E + 1)
+    lg = rng.integers(-3, 4, (S, E)).astype(np.float32) / 2
+    lg[rng.random((S, E)) < 0.05] = -0.0
+    cfg = moe.config(S, 64, 64, E, k, capacity=C, dtype="bf16", reroute=True)
+    dev = torch.device("cuda")
+    L = torch.from_numpy(lg).to(dev)
+    idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((S, k), dtype=torch.float32, device=dev)
+    slot = torch.empty((S, k), dtype=torch.int32, device=dev)
+    counts = torch.empty((k + 1, E), dtype=torch.int32, device=dev)
+    losses = torch.empty(2, dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    moe.gate(cfg, None, None, None, L, idx, tw, slot, counts, losses, ws, logits_in=True)
+    torch.cuda.synchronize()
+    r = oracle.route(lg, k, C, reroute=True)
+    assert np.array_equal(idx.cpu().numpy(), r["serve"])
+    assert np.array_equal(slot.cpu().numpy(), r["slot"])
+    assert np.array_equal(counts.cpu().numpy(), r["counts"])
+    moved = int((r["serve"] != r["idx"]).sum())
+    print(f"[rr route] re-routed {moved}, still dropped {int((r['slot'] < 0).sum())}", flush=True)
