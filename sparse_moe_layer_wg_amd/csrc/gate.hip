@@ -116,12 +116,14 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 // so x . w = x . hi + x . (lo1 + lo2) with fp32 accumulation throughout:
 // v_mfma_f32_32x32x16_bf16 accumulates x . hi in one accumulator and the two
 // small terms in another, which are added (with the bias) at the end.
-// Block tile 64 tokens x 64 experts x 64 k, 4 waves of 32 x 32; operands are
-// staged through registers into two LDS buffers (x and the three weight
-// planes, XOR-swizzled by row).  Rows past S or E
-// load a clamped valid row and are never stored.
+// Block tile 128 tokens x 64 experts x 64 k, 8 waves (4 x 2) of 32 x 32; the
+// taller tile reads each weight-plane tile once for 128 tokens, which halves
+// the plane traffic from L2 per MFMA (the kernel is bound by that traffic).
+// Operands are staged through registers into two LDS buffers (x and the
+// three weight planes, XOR-swizzled by row).  Rows past S or E load a
+// clamped valid row and are never stored.
 namespace {
-constexpr int GM_BM = 64, GM_BN = 64, GM_BK = 64, GM_CH = GM_BK / 8;
+constexpr int GM_BM = 128, GM_BN = 64, GM_BK = 64, GM_CH = GM_BK / 8, GM_NT = 512;
 
 __device__ __forceinline__ int gm_swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
 
@@ -143,50 +145,51 @@ __global__ __launch_bounds__(256) void split_router_weight_kernel(const float* _
     }
 }
 
-__global__ __launch_bounds__(256, 2) void gate_logits_mfma_kernel(const bf16_t* __restrict__ x,
+__global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t* __restrict__ x,
                                                                   const bf16_t* __restrict__ wp,
                                                                   const float* __restrict__ bg,
                                                                   float* __restrict__ logits,
                                                                   int S, int d, int E) {
-    // stage: A [64][8 chunks], then three weight planes [64][8 chunks]
+    // stage: A [128][8 chunks], then three weight planes [64][8 chunks]
     constexpr int A_SZ = GM_BM * GM_CH, B_SZ = GM_BN * GM_CH, STAGE = A_SZ + 3 * B_SZ;
     __shared__ u32x4_t smem[2 * STAGE];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int s0 = blockIdx.x * GM_BM, j0 = blockIdx.y * GM_BN;
 
-    // loader: x and weight-plane chunks c = tid + 256*i (i < 2): row c/8,
-    // chunk c%8 (8 consecutive k)
+    // loader: x chunks c = tid + GM_NT*i (i < 2) and one chunk of each weight
+    // plane, c = tid: row c/8, chunk c%8 (8 consecutive k)
+    constexpr int XI = GM_BM * GM_CH / GM_NT;
+    static_assert(GM_BN * GM_CH == GM_NT, "one weight-plane chunk per thread");
     const size_t plane = (size_t)E * d;
-    const bf16_t* xa[2];
-    const bf16_t* wb[2];
-    int ald[2], bld[2];
+    const bf16_t* xa[XI];
+    int ald[XI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+    for (int i = 0; i < XI; ++i) {
+        const int c = tid + GM_NT * i, row = c >> 3, ch = c & 7;
         xa[i] = x + (size_t)min(s0 + row, S - 1) * d + ch * 8;
-        wb[i] = wp + (size_t)min(j0 + row, E - 1) * d + ch * 8;
         ald[i] = row * GM_CH + gm_swz(row, ch);
-        bld[i] = A_SZ + row * GM_CH + gm_swz(row, ch);
     }
-    u32x4_t rx[2], rw[2][3];
+    const bf16_t* wb;
+    int bld;
+    {
+        const int row = tid >> 3, ch = tid & 7;
+        wb = wp + (size_t)min(j0 + row, E - 1) * d + ch * 8;
+        bld = A_SZ + row * GM_CH + gm_swz(row, ch);
+    }
+    u32x4_t rx[XI], rw[3];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
+        for (int i = 0; i < XI; ++i) rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
 #pragma unroll
-            for (int q = 0; q < 3; ++q)
-                rw[i][q] = *reinterpret_cast<const u32x4_t*>(wb[i] + q * plane + k0);
-        }
+        for (int q = 0; q < 3; ++q) rw[q] = *reinterpret_cast<const u32x4_t*>(wb + q * plane + k0);
     };
     auto sstore = [&](int buf) {
         u32x4_t* st = smem + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            st[ald[i]] = rx[i];
+        for (int i = 0; i < XI; ++i) st[ald[i]] = rx[i];
 #pragma unroll
-            for (int q = 0; q < 3; ++q) st[bld[i] + q * B_SZ] = rw[i][q];
-        }
+        for (int q = 0; q < 3; ++q) st[bld + q * B_SZ] = rw[q];
     };
 
     f32x16_t acc_hi, acc_lo;
@@ -243,8 +246,8 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const
         split_router_weight_kernel<<<(unsigned)(nblk < 2048 ? nblk : 2048), 256, 0, st>>>(wg, n,
                                                                                           planes);
         dim3 grid((unsigned)ceil_div(S, GM_BM), (unsigned)ceil_div(E, GM_BN));
-        gate_logits_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), planes, bg,
-                                                      logits, S, d, E);
+        gate_logits_mfma_kernel<<<grid, GM_NT, 0, st>>>(static_cast<const bf16_t*>(x), planes,
+                                                        bg, logits, S, d, E);
     } else {
         dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
         if (x_bf16)
