@@ -47,31 +47,43 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int s = __builtin_amdgcn_readfirstlane(blockIdx.x * kTokPerBlock + wave);
     if (s >= S) return;
-    for (int r = 0; r < k; ++r) {
-        const int64_t q = (int64_t)s * k + r;
-        const int64_t u = assignment_row(topk_idx, slot, q, E, stride, limit);
-        float dot = 0.f;
-        if (u >= 0) {
-            const float w = topk_w[q];
-            const u32x4_t* o = out + u * nvec;
-            u32x4_t* g = dO + u * nvec;
-            const u32x4_t* y = dy + (int64_t)s * nvec;
-            for (int i = lane; i < nvec; i += kWave) {
-                const u32x4_t yv = y[i], ov = o[i];
-                u32x4_t gv;
+    // all ranks in one pass over the columns: dy is read once and the k
+    // expert-output rows are loaded together (u[r] < 0: absent or dropped)
+    int64_t u[kMaxK];
+    float w[kMaxK], dot[kMaxK];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float y0 = __uint_as_float(yv[c] << 16);
-                    const float y1 = __uint_as_float(yv[c] & 0xffff0000u);
-                    dot = fmaf(y0, __uint_as_float(ov[c] << 16), dot);
-                    dot = fmaf(y1, __uint_as_float(ov[c] & 0xffff0000u), dot);
-                    gv[c] = pack_bf16x2(w * y0, w * y1);
-                }
-                g[i] = gv;
+    for (int r = 0; r < kMaxK; ++r) {
+        u[r] = r < k ? assignment_row(topk_idx, slot, (int64_t)s * k + r, E, stride, limit) : -1;
+        w[r] = u[r] >= 0 ? topk_w[(int64_t)s * k + r] : 0.f;
+        dot[r] = 0.f;
+    }
+    const u32x4_t* y = dy + (int64_t)s * nvec;
+    for (int i = lane; i < nvec; i += kWave) {
+        const u32x4_t yv = y[i];
+        u32x4_t ov[kMaxK];
+#pragma unroll
+        for (int r = 0; r < kMaxK; ++r)
+            if (u[r] >= 0) ov[r] = out[u[r] * nvec + i];
+#pragma unroll
+        for (int r = 0; r < kMaxK; ++r) {
+            if (u[r] < 0) continue;
+            u32x4_t gv;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float y0 = __uint_as_float(yv[c] << 16);
+                const float y1 = __uint_as_float(yv[c] & 0xffff0000u);
+                dot[r] = fmaf(y0, __uint_as_float(ov[r][c] << 16), dot[r]);
+                dot[r] = fmaf(y1, __uint_as_float(ov[r][c] & 0xffff0000u), dot[r]);
+                gv[c] = pack_bf16x2(w[r] * y0, w[r] * y1);
             }
-            dot = wave_sum_f32(dot);
+            dO[u[r] * nvec + i] = gv;
         }
-        if (lane == 0) dw[q] = dot;
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r) {
+        if (r >= k) break;
+        const float t = u[r] >= 0 ? wave_sum_f32(dot[r]) : 0.f;
+        if (lane == 0) dw[(int64_t)s * k + r] = t;
     }
 }
 

@@ -288,7 +288,7 @@ def test_backward_replays_in_a_hip_graph():
         step(0)
         torch.cuda.synchronize()
         for key in grads[0]:
-            if grads[0][key] is not None:
+            if key != "ws" and grads[0][key] is not None:   # (ws: scratch)
                 assert torch.equal(grads[0][key], grads[1][key]), (rep, key)
 
 
