@@ -256,88 +256,98 @@ __global__ __launch_bounds__(256) void occupancy_kernel(const int32_t* __restric
 // (virtual rank by virtual rank, tokens in order), so the tile histogram,
 // scan and in-tile ballot ranks of the capacity pass serve again.
 
-// Largest order key among experts not yet taken (wave-uniform); marks it.
-template <int EQ>
-__device__ __forceinline__ int next_ranked(const float (&v)[EQ], int E, int lane,
-                                           uint32_t& taken) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int q = 0; q < EQ; ++q) {
-        const int j = lane + kWave * q;
-        if (j < E && !((taken >> q) & 1u)) {
-            const uint64_t key = (static_cast<uint64_t>(float_order_key(v[q])) << 32) |
-                                 (0xffffffffu - static_cast<uint32_t>(j));
-            best = key > best ? key : best;
-        }
-    }
-    best = wave_max_u64(best);
-    const int j = (int)(0xffffffffu - __builtin_amdgcn_readfirstlane((uint32_t)best));
-    if ((j & (kWave - 1)) == lane) taken |= 1u << (j / kWave);
-    return j;
-}
-
-// One block per 64-token routing tile, one wave per token at a time: the
-// token's offers (expert, original rank) for virtual ranks j < its dropped
-// count (-1 elsewhere), then the tile's offer histogram written whole into
+// One block per 64-token routing tile.  A token's offers (expert, original
+// rank) for virtual ranks j < its dropped count (-1 elsewhere) are found by
+// L lanes, each holding V of its logits (experts li + L*q): per offer, every
+// lane takes its largest order key (logit descending, index ascending) among
+// experts not yet taken and the L lanes reduce it with shuffles; 64/L tokens
+// share a wave.  The tile's offer histogram is then written whole into
 // hist[e][j*nb + b] (every entry, zeros included, so nothing is cleared
 // beforehand).  Dynamic LDS: k*E ints.
-constexpr int kOfferWaves = 16;
+constexpr int kOfferThreads = 256;
 
-template <int EQ>
-__global__ __launch_bounds__(64 * kOfferWaves) void reroute_offers_kernel(
+template <int L, int V>
+__global__ __launch_bounds__(kOfferThreads) void reroute_offers_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ slot, int S, int E, int k, int nb, int32_t* __restrict__ offer_e,
     int32_t* __restrict__ offer_r, int32_t* __restrict__ hist) {
+    static_assert(V <= 32, "taken bits per lane");
     extern __shared__ int s_h[];                  // [k][E] offers of this tile
     __shared__ int s_off[kMaxK][kTokBlock];       // offered expert per (j, token)
+    constexpr int TPW = kWave / L;                // tokens per wave and round
+    constexpr int TPR = TPW * (kOfferThreads / kWave);   // tokens per block and round
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int g = lane / L, li = lane % L;
     const int b = blockIdx.x;
-    for (int i = tid; i < k * E; i += 64 * kOfferWaves) s_h[i] = 0;
-    for (int t = wave; t < kTokBlock; t += kOfferWaves) {
-        const int s = b * kTokBlock + t;           // wave-uniform
-        if (s >= S) {
-            if (lane < k) s_off[lane][t] = -1;
-            continue;
-        }
-        float v[EQ];
+    for (int i = tid; i < k * E; i += kOfferThreads) s_h[i] = 0;
+    for (int t0 = 0; t0 < kTokBlock; t0 += TPR) {
+        const int t = t0 + wave * TPW + g;         // this group's token in the tile
+        const int s = b * kTokBlock + t;
+        const bool live = s < S;
+        float v[V];
 #pragma unroll
-        for (int q = 0; q < EQ; ++q) {
-            const int j = lane + kWave * q;
-            v[q] = j < E ? logits[(size_t)s * E + j] : 0.f;
+        for (int q = 0; q < V; ++q) {
+            const int j = li + L * q;
+            v[q] = live && j < E ? logits[(size_t)s * E + j] : 0.f;
         }
         uint32_t taken = 0;   // the top-k are not alternatives
+        uint32_t drop = 0;    // dropped ranks of the token
         for (int r = 0; r < k; ++r) {
-            const int e = topk_idx[(size_t)s * k + r];
-            if ((e & (kWave - 1)) == lane) taken |= 1u << (e / kWave);
+            const int e = live ? topk_idx[(size_t)s * k + r] : -1;
+            if (e >= 0 && e % L == li) taken |= 1u << (e / L);
+            if (live && slot[(size_t)s * k + r] < 0) drop |= 1u << r;
         }
         int j = 0;
-        for (int r = 0; r < k; ++r) {
-            if (slot[(size_t)s * k + r] >= 0) continue;   // wave-uniform
-            const int e = k + j < E ? next_ranked<EQ>(v, E, lane, taken) : -1;
-            if (lane == 0) {
-                offer_e[(size_t)s * k + j] = e;
-                offer_r[(size_t)s * k + j] = r;
-                s_off[j][t] = e;
+        for (int r = 0; r < k; ++r) {   // every group takes part in every step
+            const bool want = ((drop >> r) & 1u) && k + j < E;
+            uint64_t best = 0;
+            if (want) {
+#pragma unroll
+                for (int q = 0; q < V; ++q) {
+                    const int e = li + L * q;
+                    if (e < E && !((taken >> q) & 1u)) {
+                        const uint64_t key = (static_cast<uint64_t>(float_order_key(v[q])) << 32) |
+                                             (0xffffffffu - static_cast<uint32_t>(e));
+                        best = key > best ? key : best;
+                    }
+                }
             }
-            ++j;
+#pragma unroll
+            for (int off = 1; off < L; off <<= 1) {
+                const uint64_t o = __shfl_xor(best, off, kWave);
+                best = o > best ? o : best;
+            }
+            if ((drop >> r) & 1u) {
+                const int e = want ? (int)(0xffffffffu - static_cast<uint32_t>(best)) : -1;
+                if (e >= 0 && e % L == li) taken |= 1u << (e / L);
+                if (li == 0) {
+                    offer_e[(size_t)s * k + j] = e;
+                    offer_r[(size_t)s * k + j] = r;
+                    s_off[j][t] = e;
+                }
+                ++j;
+            }
         }
-        if (lane == 0)
+        if (li == 0) {
             for (; j < k; ++j) {
-                offer_e[(size_t)s * k + j] = -1;
-                offer_r[(size_t)s * k + j] = -1;
+                if (live) {
+                    offer_e[(size_t)s * k + j] = -1;
+                    offer_r[(size_t)s * k + j] = -1;
+                }
                 s_off[j][t] = -1;
             }
+        }
     }
     __syncthreads();
-    if (tid < k * kTokBlock) {
-        const int e = s_off[tid / kTokBlock][tid % kTokBlock];
-        if (e >= 0) atomicAdd(&s_h[(tid / kTokBlock) * E + e], 1);
+    for (int i = tid; i < k * kTokBlock; i += kOfferThreads) {
+        const int e = s_off[i / kTokBlock][i % kTokBlock];
+        if (e >= 0) atomicAdd(&s_h[(i / kTokBlock) * E + e], 1);
     }
     __syncthreads();
     const size_t T = (size_t)k * nb;
-    for (int i = tid; i < k * E; i += 64 * kOfferWaves) {
-        const int j = i / E, e = i - j * E;
-        hist[(size_t)e * T + (size_t)j * nb + b] = s_h[i];
+    for (int i = tid; i < k * E; i += kOfferThreads) {
+        const int jj = i / E, e = i - jj * E;
+        hist[(size_t)e * T + (size_t)jj * nb + b] = s_h[i];
     }
 }
 
@@ -483,19 +493,20 @@ hipError_t launch_reroute(const float* logits, int32_t* topk_idx, int32_t* slot,
                           int32_t* offer_e, int32_t* offer_r, int32_t* hist, hipStream_t st) {
     if (S == 0) return hipSuccess;
     const size_t lds = (size_t)k * E * sizeof(int);
-    const int eq = (E + kWave - 1) / kWave;
     auto offers = [&](auto kern) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        kern<<<nb, 64 * kOfferWaves, lds, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e,
-                                                offer_r, hist);
+        kern<<<nb, kOfferThreads, lds, st>>>(logits, topk_idx, slot, S, E, k, nb, offer_e,
+                                             offer_r, hist);
     };
-    if (eq <= 1) offers(&reroute_offers_kernel<1>);
-    else if (eq <= 2) offers(&reroute_offers_kernel<2>);
-    else if (eq <= 4) offers(&reroute_offers_kernel<4>);
-    else if (eq <= 8) offers(&reroute_offers_kernel<8>);
-    else if (eq <= 16) offers(&reroute_offers_kernel<16>);
-    else offers(&reroute_offers_kernel<32>);
+    // L lanes per token: the smallest power of two giving at most 16 logits
+    // per lane (32 for E > 1024)
+    if (E <= 64) offers(&reroute_offers_kernel<4, 16>);
+    else if (E <= 128) offers(&reroute_offers_kernel<8, 16>);
+    else if (E <= 256) offers(&reroute_offers_kernel<16, 16>);
+    else if (E <= 512) offers(&reroute_offers_kernel<32, 16>);
+    else if (E <= 1024) offers(&reroute_offers_kernel<64, 16>);
+    else offers(&reroute_offers_kernel<64, 32>);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     reroute_scan_kernel<<<E, 256, 0, st>>>(hist, E, k, nb, C, counts, occ);
