@@ -44,9 +44,15 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    # MOE_ORACLE_LIBRARY: a separately built copy of the same source (the
+    # sanitizer test loads an instrumented build this way)
+    override = os.environ.get("MOE_ORACLE_LIBRARY")
+    if override:
+        lib = ctypes.CDLL(override)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     vp = ctypes.c_void_p
     i32 = ctypes.c_int
     lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double]
