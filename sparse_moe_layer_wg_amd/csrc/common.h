@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace moe {
@@ -43,25 +45,81 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-wide reductions on DPP lane moves (register to register, a few
+// cycles each) rather than shuffles through the LDS crossbar: within each
+// 16-lane row, quad_perm [1,0,3,2] and [2,3,0,1], then half-row and row
+// mirrors, leave the row's result in all 16 lanes; the four rows are then
+// read out as scalars (lanes 0, 16, 32, 48) and combined in that order.  All
+// 64 lanes must be active.  The result is the same in every lane.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v),
+                                                             static_cast<int>(v), CTRL, 0xf, 0xf,
+                                                             false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(v));
+    const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), l);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_u64<kDppXor1>(v);
+    v = o > v ? o : v;
+    o = dpp_u64<kDppXor2>(v);
+    v = o > v ? o : v;
+    o = dpp_u64<kDppHalfMirror>(v);
+    v = o > v ? o : v;
+    o = dpp_u64<kDppMirror>(v);
+    v = o > v ? o : v;
+    uint64_t r = readlane_u64(v, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, kWave);
-        v = o > v ? o : v;
+    for (int l = 16; l < kWave; l += 16) {
+        o = readlane_u64(v, l);
+        r = o > r ? o : r;
     }
-    return v;
+    return r;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
+    v += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v)));
+    float r = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    for (int l = 16; l < kWave; l += 16)
+        r += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), l));
+    return r;
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
+    auto mv = [](double x, auto ctrl_tag) {
+        constexpr int C = decltype(ctrl_tag)::value;
+        return __longlong_as_double(static_cast<long long>(
+            dpp_u64<C>(static_cast<uint64_t>(__double_as_longlong(x)))));
+    };
+    v += mv(v, std::integral_constant<int, kDppXor1>{});
+    v += mv(v, std::integral_constant<int, kDppXor2>{});
+    v += mv(v, std::integral_constant<int, kDppHalfMirror>{});
+    v += mv(v, std::integral_constant<int, kDppMirror>{});
+    const auto rd = [&](int l) {
+        return __longlong_as_double(static_cast<long long>(
+            readlane_u64(static_cast<uint64_t>(__double_as_longlong(v)), l)));
+    };
+    double r = rd(0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    for (int l = 16; l < kWave; l += 16) r += rd(l);
+    return r;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
