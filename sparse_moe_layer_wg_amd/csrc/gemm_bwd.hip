@@ -408,6 +408,21 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                                         (WGRAD ? (size_t)cur.e * p.M * N : cur.row_e * N);
             const bf16_t* __restrict__ mk =
                 MASK ? static_cast<const bf16_t*>(p.mask) + cur.row_e * N : nullptr;
+            // the mask chunks of all of this lane's rows are loaded together
+            // (rows and columns clamped into range; unused ones are never
+            // applied), so their latency is paid once per tile, not per row;
+            // each chunk is read before this lane overwrites it (dU may
+            // replace H in place)
+            u32x4_t hvs[MASK ? NIT : 1];
+            if constexpr (MASK) {
+#pragma unroll
+                for (int it = 0; it < NIT; ++it) {
+                    const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+                    const int m = min(cur.m0 + wm * WM + row, cur.M - 1);
+                    const int n = min(nw + ch * 8, N - 8);
+                    hvs[it] = *reinterpret_cast<const u32x4_t*>(mk + (size_t)m * N + n);
+                }
+            }
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
@@ -417,8 +432,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bwd_kernel(BwdGemmParams p) {
                     if constexpr (MASK) {
                         // dReLU: keep the gradient where the forward's hidden
                         // value is positive (bf16 > 0: sign clear, not zero)
-                        const u32x4_t hv =
-                            *reinterpret_cast<const u32x4_t*>(mk + (size_t)m * N + n);
+                        const u32x4_t hv = hvs[it];
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
                             const uint32_t hlo = hv[c] & 0xffffu, hhi = hv[c] >> 16;
