@@ -33,8 +33,9 @@
 //   one that reloads all of W.
 //   The MFMAs take the weight fragment as their first operand, so each lane
 //   ends with four consecutive output columns per register quad; bias, ReLU
-//   and bf16 rounding are applied there and the tile leaves through LDS as
-//   16-byte row-contiguous stores.
+//   and bf16 rounding are applied there, and lane pairs (l, l+32) exchange
+//   halves with v_permlane32_swap so that each lane stores 8 consecutive
+//   columns as one 16-byte chunk straight from registers.
 //   With a_rows set, A rows are gathered from the token rows through the
 //   inverse slot map (the dispatch permute fused into the loads).  With row0
 //   set, expert e's rows start at row0[e] instead of e*C: the compact expert
@@ -300,9 +301,7 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         // operand, so a 32x32 accumulator block is (n x m): lane l holds row
         // m = l%32 and register r column n = 8*(r/4) + 4*(l/32) + r%4, i.e.
         // four consecutive columns per register quad.  Bias and ReLU are
-        // applied there; the bf16 results pass through LDS (the stage
-        // buffers are free after the k-loop's last barrier; each wave uses
-        // its own region) and leave as 16-byte row-contiguous stores.
+        // applied there.
         bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.Cout) + row_e * N;
         const bf16_t* bias = p.bias ? static_cast<const bf16_t*>(p.bias) + (size_t)e * N : nullptr;
         auto finish4 = [&](const f32x16_t& a, int q, int n) {
@@ -322,38 +321,38 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
             }
             return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         };
-        constexpr int EPS = WNT * 2 + 8;            // LDS bytes per staged row
-        static_assert(NTH / 64 * WM * EPS <= 2 * STAGE, "epilogue staging fits LDS");
-        char* ep = smem + wave * (WM * EPS);
+        // Lanes l and l+32 hold columns 4 apart: one swap of the upper half's
+        // even quads with the lower half's odd quads (v_permlane32_swap) gives
+        // every lane 8 consecutive columns, stored as one 16-byte chunk
+        // straight from registers (32 bytes of a row per lane pair).
         const int nw = n0 + wn * WNT;               // first column of this wave
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WM + i * 32 + frow;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nl = j * 32 + 8 * q + 4 * fhalf;
-                    *reinterpret_cast<uint2*>(ep + (i * 32 + frow) * EPS + nl * 2) =
-                        finish4(acc[i][j], q, nw + nl);
+                for (int h = 0; h < 2; ++h) {
+                    const int c = nw + j * 32 + 16 * h;   // 16 columns of quads 2h, 2h+1
+                    const uint2 v0 = finish4(acc[i][j], 2 * h, c + 4 * fhalf);
+                    const uint2 v1 = finish4(acc[i][j], 2 * h + 1, c + 8 + 4 * fhalf);
+                    // lower lane: own v0 | upper's v0; upper lane: lower's v1 | own v1
+                    const auto sx = __builtin_amdgcn_permlane32_swap(v0.x, v1.x, false, false);
+                    const auto sy = __builtin_amdgcn_permlane32_swap(v0.y, v1.y, false, false);
+                    const int n = c + 8 * fhalf;
+                    if (m < M && n < N) {
+                        u32x4_t o;
+                        o[0] = sx[0];
+                        o[1] = sy[0];
+                        o[2] = sx[1];
+                        o[3] = sy[1];
+                        *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = o;
+                    }
                 }
+        }
         // publish the next tile (every wave read s_next before the k-loop's
         // first barrier; the atomic has long returned)
         if (tid == 0) s_next = nx;
-        __builtin_amdgcn_wave_barrier();
-        constexpr int CPR = WNT * 2 / 16;           // 16-byte chunks per row
-        constexpr int NIT = WM * CPR / 64;          // chunks per lane
-        u32x4_t ov[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
-            ov[it] = *reinterpret_cast<const u32x4_t*>(ep + row * EPS + ch * 16);
-        }
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int row = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
-            const int m = m0 + wm * WM + row, n = nw + ch * 8;
-            if (m < M && n < N) *reinterpret_cast<u32x4_t*>(Cout + (size_t)m * N + n) = ov[it];
-        }
         if (strip) {
             const int m = m0 + BM + frow;
             if (m < M) {
