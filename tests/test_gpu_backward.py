@@ -84,6 +84,13 @@ BWD = [
                 seed=53, gate_bias="zipf1.2"),
     mw.Workload("bwd_dropless_skew", S=700, d=128, h=320, E=24, k=2, capacity_factor=1.0,
                 dtype="bf16", seed=54, gate_bias="zipf1.2", dropless=True),
+    # degenerate routing: with top-1 the renormalised weight is the constant 1,
+    # so only the aux and z terms reach the router; with one expert the aux
+    # loss is constant too and only z remains
+    mw.Workload("bwd_top1", S=517, d=128, h=192, E=8, k=1, capacity_factor=1.0, dtype="bf16",
+                seed=55),
+    mw.Workload("bwd_one_expert", S=300, d=64, h=128, E=1, k=1, capacity_factor=0.5,
+                dtype="bf16", seed=56),
 ]
 
 

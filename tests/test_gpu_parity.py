@@ -153,6 +153,12 @@ MID = [
                 dtype="bf16", seed=13, gate_bias="zipf1.2"),
     mw.Workload("mid_f32_bias", S=333, d=96, h=160, E=6, k=2, capacity_factor=0.8, dtype="f32",
                 seed=14, ffn_bias="zeros"),
+    # degenerate routing: top-1 (every renormalised weight is 1) and a single
+    # expert that keeps only the first C = S/2 tokens
+    mw.Workload("mid_bf16_top1", S=517, d=128, h=192, E=8, k=1, capacity_factor=1.0,
+                dtype="bf16", seed=15),
+    mw.Workload("mid_bf16_one_expert", S=300, d=64, h=128, E=1, k=1, capacity_factor=0.5,
+                dtype="bf16", seed=16),
 ]
 
 
