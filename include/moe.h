@@ -60,8 +60,8 @@
  *   Buffers.  Slots of xd/out past an expert's occupancy are left as they
  *     were (never read by later steps).  NaN/Inf inputs are not supported.
  *   Alignment.  Activation-typed arrays (x, xd, out, y, W1, b1, W2, b2,
- *     hidden, dy, dx and the expert weight gradients) and dw_gate start on
- *     16-byte boundaries; a misaligned one is MOE_ERR_INVALID_ARG.
+ *     hidden, dy, dx and the expert weight gradients), w_gate and dw_gate
+ *     start on 16-byte boundaries; a misaligned one is MOE_ERR_INVALID_ARG.
  *   Workspace.  `ws` is device scratch of at least moe_workspace_bytes()
  *     bytes, 256-byte aligned; its contents do not persist between calls.
  *     Calls that share a workspace must be ordered on one stream.

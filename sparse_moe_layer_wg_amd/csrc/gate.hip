@@ -112,7 +112,8 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 // Router logits for bf16 activations on the MFMA units.  Each fp32 router
 // weight is split exactly into three bf16 terms, w = hi + lo1 + lo2 (hi is w
 // rounded to bf16, lo1 the rounded remainder, lo2 what is left; 3 x 8
-// significand bits cover fp32's 24), once per call into three planes.  A bf16 x bf16 product is exact in fp32,
+// significand bits cover fp32's 24), in registers as the weight tile is
+// staged into LDS (three planes).  A bf16 x bf16 product is exact in fp32,
 // so x . w = x . hi + x . (lo1 + lo2) with fp32 accumulation throughout:
 // v_mfma_f32_32x32x16_bf16 accumulates x . hi in one accumulator and the two
 // small terms in another, which are added (with the bias) at the end.
@@ -120,33 +121,34 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 // taller tile reads each weight-plane tile once for 128 tokens, which halves
 // the plane traffic from L2 per MFMA (the kernel is bound by that traffic).
 // Operands are staged through registers into two LDS buffers (x and the
-// three weight planes, XOR-swizzled by row).  Rows past S or E load a
+// three weight planes, XOR-swizzled by row); the fp32 weights are read once
+// per block, 32 bytes per thread per k-tile.  Rows past S or E load a
 // clamped valid row and are never stored.
 namespace {
 constexpr int GM_BM = 128, GM_BN = 64, GM_BK = 64, GM_CH = GM_BK / 8, GM_NT = 512;
 
 __device__ __forceinline__ int gm_swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
 
-// Exact three-way bf16 split of the router weight, once per call: plane 0
-// holds hi = bf16(w), plane 1 lo1 = bf16(w - hi), plane 2 lo2 = w - hi - lo1
-// (exact in bf16), each [E,d].
-__global__ __launch_bounds__(256) void split_router_weight_kernel(const float* __restrict__ wg,
-                                                                  size_t n,
-                                                                  bf16_t* __restrict__ planes) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x) {
-        const float w = wg[i];
-        const bf16_t h = f32_to_bf16(w);
-        const float r1 = w - bf16_to_f32(h);
-        const bf16_t m = f32_to_bf16(r1);
-        planes[i] = h;
-        planes[n + i] = m;
-        planes[2 * n + i] = f32_to_bf16(r1 - bf16_to_f32(m));
+// Exact three-way bf16 split of 8 fp32 weights into three chunks of 8 bf16:
+// hi = bf16(w), lo1 = bf16(w - hi), lo2 = w - hi - lo1 (exact in bf16).
+__device__ __forceinline__ void split3(const f32x4_t& w0, const f32x4_t& w1, u32x4_t& hi,
+                                       u32x4_t& lo1, u32x4_t& lo2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        // weights 2q, 2q+1, two at a time through the packed conversion
+        const float a = q < 2 ? w0[2 * q] : w1[2 * q - 4];
+        const float b = q < 2 ? w0[2 * q + 1] : w1[2 * q - 3];
+        const uint32_t h = pack_bf16x2(a, b);
+        const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xffff0000u);
+        const uint32_t m = pack_bf16x2(ra, rb);
+        hi[q] = h;
+        lo1[q] = m;
+        lo2[q] = pack_bf16x2(ra - __uint_as_float(m << 16), rb - __uint_as_float(m & 0xffff0000u));
     }
 }
 
 __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t* __restrict__ x,
-                                                                  const bf16_t* __restrict__ wp,
+                                                                  const float* __restrict__ wg,
                                                                   const float* __restrict__ bg,
                                                                   float* __restrict__ logits,
                                                                   int S, int d, int E) {
@@ -157,11 +159,10 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
     const int wm = wave >> 1, wn = wave & 1;
     const int s0 = blockIdx.x * GM_BM, j0 = blockIdx.y * GM_BN;
 
-    // loader: x chunks c = tid + GM_NT*i (i < 2) and one chunk of each weight
-    // plane, c = tid: row c/8, chunk c%8 (8 consecutive k)
+    // loader: x chunks c = tid + GM_NT*i (i < 2) and 8 consecutive fp32
+    // weights, c = tid: row c/8, k 8*(c%8) .. +7, one chunk of each plane
     constexpr int XI = GM_BM * GM_CH / GM_NT;
     static_assert(GM_BN * GM_CH == GM_NT, "one weight-plane chunk per thread");
-    const size_t plane = (size_t)E * d;
     const bf16_t* xa[XI];
     int ald[XI];
 #pragma unroll
@@ -170,26 +171,30 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
         xa[i] = x + (size_t)min(s0 + row, S - 1) * d + ch * 8;
         ald[i] = row * GM_CH + gm_swz(row, ch);
     }
-    const bf16_t* wb;
+    const float* wb;
     int bld;
     {
         const int row = tid >> 3, ch = tid & 7;
-        wb = wp + (size_t)min(j0 + row, E - 1) * d + ch * 8;
+        wb = wg + (size_t)min(j0 + row, E - 1) * d + ch * 8;
         bld = A_SZ + row * GM_CH + gm_swz(row, ch);
     }
-    u32x4_t rx[XI], rw[3];
+    u32x4_t rx[XI];
+    f32x4_t rw[2];
     auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < XI; ++i) rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
 #pragma unroll
-        for (int q = 0; q < 3; ++q) rw[q] = *reinterpret_cast<const u32x4_t*>(wb + q * plane + k0);
+        for (int q = 0; q < 2; ++q) rw[q] = *reinterpret_cast<const f32x4_t*>(wb + k0 + 4 * q);
     };
     auto sstore = [&](int buf) {
         u32x4_t* st = smem + buf * STAGE;
 #pragma unroll
         for (int i = 0; i < XI; ++i) st[ald[i]] = rx[i];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) st[bld + q * B_SZ] = rw[q];
+        u32x4_t hi, lo1, lo2;
+        split3(rw[0], rw[1], hi, lo1, lo2);
+        st[bld] = hi;
+        st[bld + B_SZ] = lo1;
+        st[bld + 2 * B_SZ] = lo2;
     };
 
     f32x16_t acc_hi, acc_lo;
@@ -234,20 +239,12 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
 }
 }  // namespace
 
-bool gate_uses_split(bool x_bf16, int d) { return x_bf16 && d % GM_BK == 0; }
-
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
-                              float* logits, int S, int d, int E, void* split,
-                              hipStream_t st) {
-    if (gate_uses_split(x_bf16, d)) {
-        bf16_t* planes = static_cast<bf16_t*>(split);
-        const size_t n = (size_t)E * d;
-        const int64_t nblk = ceil_div((int64_t)n, 256);
-        split_router_weight_kernel<<<(unsigned)(nblk < 2048 ? nblk : 2048), 256, 0, st>>>(wg, n,
-                                                                                          planes);
+                              float* logits, int S, int d, int E, hipStream_t st) {
+    if (x_bf16 && d % GM_BK == 0) {
         dim3 grid((unsigned)ceil_div(S, GM_BM), (unsigned)ceil_div(E, GM_BN));
-        gate_logits_mfma_kernel<<<grid, GM_NT, 0, st>>>(static_cast<const bf16_t*>(x), planes,
-                                                        bg, logits, S, d, E);
+        gate_logits_mfma_kernel<<<grid, GM_NT, 0, st>>>(static_cast<const bf16_t*>(x), wg, bg,
+                                                        logits, S, d, E);
     } else {
         dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
         if (x_bf16)

@@ -9,12 +9,8 @@ namespace moe {
 
 // ------------------------------------------------------------------ gate
 // logits[s,j] = sum_i x[s,i] * wg[j,i] + bg[j]   (fp32 accumulation)
-// split: workspace of 3*E*d bf16 (the router weight's exact bf16 split)
-// when gate_uses_split(x_bf16, d), else unused.
-bool gate_uses_split(bool x_bf16, int d);
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
-                              float* logits, int S, int d, int E, void* split,
-                              hipStream_t st);
+                              float* logits, int S, int d, int E, hipStream_t st);
 
 struct RouteParams {
     float* logits;          // [S,E]; refined entries are written back

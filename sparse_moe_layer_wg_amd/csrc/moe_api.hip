@@ -93,7 +93,7 @@ constexpr int kTileCounters = 16;
 // with R = rows: E*C padded, S*k compact (dropless).
 struct Carve {
     size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, seg, ctr,
-        inv, wsplit, offer_e, offer_r, rhist;
+        inv, offer_e, offer_r, rhist;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -122,7 +122,6 @@ Carve carve(const Plan& p) {
     c.seg = take((size_t)p.E * 4);
     c.ctr = take(kTileCounters * 4);
     c.inv = take(p.rows * 4);
-    c.wsplit = gate_uses_split(p.bf16, p.d) ? take((size_t)3 * p.E * p.d * 2) : o;
     if (p.reroute) {
         c.offer_e = take((size_t)p.S * p.k * 4);
         c.offer_r = take((size_t)p.S * p.k * 4);
@@ -168,8 +167,7 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
     if (!logits_in)
-        MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, at<void>(ws, cv.wsplit),
-                                   st));
+        MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, st));
     record(ev, 1, st);
     RouteParams rp{};
     rp.logits = logits;
@@ -308,7 +306,7 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const float* w_gate,
     if (!counts || !losses) return MOE_ERR_INVALID_ARG;
     if (p.S > 0 && (!topk_idx || !topk_w || !slot)) return MOE_ERR_INVALID_ARG;
     if (p.S > 0 && (logits_in ? !logits : (!x || !w_gate))) return MOE_ERR_INVALID_ARG;
-    if (!logits_in && !aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+    if (!logits_in && (!aligned(x, 16) || !aligned(w_gate, 16))) return MOE_ERR_INVALID_ARG;
     if (p.S == 0) {
         MOE_TRY(launch_zero_outputs(counts, p.crows * p.E, losses, stream));
         return MOE_OK;
@@ -384,8 +382,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const float* 
     if (s != MOE_OK) return s;
     if (!w_gate || !w1 || !w2 || !ws) return MOE_ERR_INVALID_ARG;
     if (p.S > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
-    for (const void* q : {x, w1, b1, w2, b2, (const void*)y, (const void*)xd, (const void*)out,
-                          (const void*)hidden})
+    for (const void* q : {x, (const void*)w_gate, w1, b1, w2, b2, (const void*)y,
+                          (const void*)xd, (const void*)out, (const void*)hidden})
         if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
     if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
     const Carve cv = carve(p);
@@ -512,8 +510,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const float*
         return MOE_ERR_INVALID_ARG;
     if (!counts) return MOE_ERR_INVALID_ARG;
     if (!isfinite(g_aux) || !isfinite(g_z)) return MOE_ERR_INVALID_ARG;
-    for (const void* q : {x, w1, b1, w2, out, hidden, dy, (const void*)dx, (const void*)dw1,
-                          (const void*)db1, (const void*)dw2, (const void*)db2,
+    for (const void* q : {x, (const void*)w_gate, w1, b1, w2, out, hidden, dy, (const void*)dx,
+                          (const void*)dw1, (const void*)db1, (const void*)dw2, (const void*)db2,
                           (const void*)dw_gate})
         if (q && !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
     if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;

@@ -102,6 +102,9 @@ int main(void) {
     EXPECT(moe_gate(&c, fake, ff, NULL, ff, fi, ff, fi, fi, ff, 0u, fake, 256, NULL) ==
                MOE_ERR_WORKSPACE,
            "gate with a small workspace");
+    EXPECT(moe_gate(&c, fake, (const float*)odd, NULL, ff, fi, ff, fi, fi, ff, 0u, fake, ws,
+                    NULL) == MOE_ERR_INVALID_ARG,
+           "gate with misaligned w_gate");
     EXPECT(moe_dispatch(&c, fake, fi, fi, odd, NULL) == MOE_ERR_INVALID_ARG,
            "dispatch with misaligned xd");
     EXPECT(moe_combine(&c, fake, fi, fi, ff, odd, NULL) == MOE_ERR_INVALID_ARG,

@@ -133,6 +133,15 @@ def test_workspace_size_and_errors_before_launch():
     st = lib.moe_dispatch(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 2), vp(), vp(), vp(),
                           None)
     assert st == 1
+    # router weight not 16-byte aligned -> INVALID_ARG (gate and whole layer)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    st = lib.moe_gate(ctypes.byref(cfg), vp(), odd, None, None, vp(), vp(), vp(), vp(), vp(),
+                      0, vp(), n.value, None)
+    assert st == 1
+    st = lib.moe_layer_forward(ctypes.byref(cfg), vp(), odd, None, vp(), None, vp(), None, vp(),
+                               None, None, None, None, None, None, None, None, None, vp(),
+                               n.value, None, None)
+    assert st == 1
     # unknown gate flag -> INVALID_ARG
     st = lib.moe_gate(ctypes.byref(cfg), vp(), vp(), None, None, vp(), vp(), vp(), vp(), vp(),
                       2, vp(), n.value, None)
@@ -165,8 +174,9 @@ def test_backward_validation_on_host():
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
     f = ctypes.c_float
 
-    def call(ws_bytes=need, g_aux=0.0, drop=None, dw_gate=fake):
+    def call(ws_bytes=need, g_aux=0.0, drop=None, dw_gate=fake, w_gate=fake):
         args = [fake] * 13
+        args[1] = w_gate
         args[11] = None                                  # hidden: optional
         if drop is not None:
             args[drop] = None
@@ -174,6 +184,7 @@ def test_backward_validation_on_host():
                                       None, fake, None, fake, None, fake, ws_bytes, None, None)
     assert call(ws_bytes=need - 1) == 3                 # workspace too small
     assert call(dw_gate=ctypes.c_void_p((1 << 20) + 4)) == 1   # dw_gate not 16-byte aligned
+    assert call(w_gate=ctypes.c_void_p((1 << 20) + 4)) == 1    # w_gate not 16-byte aligned
     assert call(drop=12) == 1                           # dy missing
     assert call(drop=10) == 1                           # forward expert outputs missing
     assert call(g_aux=float("nan")) == 1                # loss weight not finite
