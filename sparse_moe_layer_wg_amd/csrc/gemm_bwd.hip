@@ -66,8 +66,9 @@ __device__ __forceinline__ u32x4_t column8(const uint2 (&v)[8], bool hi_word, ui
 // each column as a 16-byte chunk of LDS row 4l + col.  Rows 4 apart are 576
 // bytes apart, a multiple of the bank width, so writing column c in every
 // lane at once would put 16 lanes on the same banks.  Store c instead writes
-// column (c + l/4) % 4: the 64 lanes then spread evenly over the banks (four
-// per 16-byte bank group, the minimum for a 1 KiB store).
+// column (c + l/2) % 4: each group of 8 lanes (128 bytes, written together)
+// then covers every bank once; with (c + l/4) % 4 two lanes of a group still
+// shared banks (SQ_LDS_BANK_CONFLICT 1.2-1.9e7 cycles per launch, now 0).
 struct KMajorStore {
     int off[4];        // LDS byte offset of store c (row and K chunk)
     uint32_t sel[4];   // byte selector of the column's half
@@ -75,7 +76,7 @@ struct KMajorStore {
     __device__ KMajorStore(int lane, int wave, int rs) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int col = (c + (lane >> 2)) & 3;
+            const int col = (c + (lane >> 1)) & 3;
             off[c] = (4 * lane + col) * rs + wave * 16;
             sel[c] = (col & 1) ? 0x07060302u : 0x05040100u;
             hi[c] = (col >> 1) != 0;
