@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="balanced_bf16", choices=mw.ORDER)
+    # default: the largest single-GPU workload, where the expert GEMMs are
+    # bound by the matrix cores rather than by streaming the weights
+    ap.add_argument("--workload", default="large_bf16", choices=mw.ORDER)
     ap.add_argument("--dropless", action="store_true",
                     help="no capacity limit: compact [S*k,d] expert segments, no drops")
     ap.add_argument("--reroute", action="store_true",
@@ -122,6 +124,37 @@ def filled_rows(counts: np.ndarray, C: int, k: int) -> np.ndarray:
     return occ + counts[k] if counts.shape[0] > k else occ
 
 
+def host_cpu() -> dict:
+    """The host the CPU baseline runs on: CPU model (lscpu), OMP_NUM_THREADS
+    and the number of cores this process may run on."""
+    import subprocess
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    return {"cpu_model": model, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "affinity_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+
+
+def oracle_threads() -> int:
+    """Threads the OpenMP oracle runs with: OMP_NUM_THREADS when set, else
+    libgomp's default, one per core in the affinity mask."""
+    return int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float, backward=False) -> dict:
     import oracle
     host = {n: mw.to_numpy(t) for n, t in inputs.items()}
@@ -150,8 +183,8 @@ def cpu_baseline(w: mw.Workload, inputs: dict, target_s: float, backward=False) 
     n = int(min(w.S, max(n0, n0 * target_s / max(t0, 1e-3))))
     n = max(64, (n // 64) * 64) if n >= 64 else n
     t = run(n) if n != n0 else t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": n / t, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"first {n} of the {w.S} tokens of the same workload (same E, d, h, k, "
                       + ("dropless routing" if w.dropless else
                          "capacity_factor; C scaled with the sample"
@@ -425,9 +458,9 @@ def bench_ep_share(a, sh) -> dict:
         t_m0 = run(m0)
         m = int(min(counts.min(), max(m0, m0 * a.cpu_seconds / max(t_m0, 1e-3))))
         tc = run(m) if m != m0 else t_m0
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
         out_d["cpu_baseline"] = {"value": sh.E_local * m / tc, "unit": "rows/s",
-                                 "cores": threads, "kind": "oracle",
+                                 "cores": oracle_threads(), "kind": "oracle",
+                                 "host": host_cpu(),
                                  "sample": f"the first {m} rows of each of the {sh.E_local} local "
                                            f"experts through the fp64 oracle FFN, {tc:.1f} s"}
     return out_d

@@ -36,8 +36,9 @@
  * Conventions shared by every entry point
  *   Pointers.  Every array argument is a DEVICE pointer to memory the caller
  *     owns (for example a torch tensor's data_ptr()).  The config is host
- *     memory.  The library allocates and frees nothing, keeps no pointer after
- *     a call returns, and holds no global mutable state.
+ *     memory.  The library allocates and frees nothing and keeps no pointer
+ *     after a call returns.  Its only process-wide state is a per-device
+ *     cache of the compute-unit count (filled on first use, never changed).
  *   Execution.  Work is enqueued on `stream` (0 = the null stream) and is
  *     asynchronous: outputs are valid once the stream has been synchronised.
  *     The library performs no host<->device copies and no synchronisation.
@@ -91,7 +92,14 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * capacity_factor > 0 when capacity == 0; capacity >= 0.
  * Supported by the kernels (else MOE_ERR_UNSUPPORTED): E <= 2048, k <= 8,
  * k * E <= 16384, d_model and d_ff multiples of 64 for bf16 and of 4 for
- * fp32, and R * max(d_model, d_ff) < 2^31 with R = moe_dispatch_rows. */
+ * fp32, R * max(d_model, d_ff) < 2^31 with R = moe_dispatch_rows,
+ * S * max(d_model, E) < 2^31, and one expert matrix under 4 GiB
+ * (d_model * d_ff * element size < 2^32 bytes).
+ * Source of the shape: "GShard: Scaling Giant Models with Conditional
+ * Computation and Automatic Sharding" (paper card), method paragraph (top-2
+ * of E experts, capacity from capacity_factor); k > 2 generalises the top-2
+ * rule ("GShard: Scaling Giant Neural Networks with Conditional Computation"
+ * (blog), "Mixture-of-Experts Implementation": top-k). */
 typedef struct moe_config {
     int32_t S;               /* tokens on this GPU                         */
     int32_t d_model;         /* d: model width                             */
@@ -121,9 +129,9 @@ typedef struct moe_config {
 #define MOE_CFG_DROPLESS 1u
 
 /* moe_config.flags: overflow re-routing (not with MOE_CFG_DROPLESS).  The
- * pages allow overflowing tokens to be "routed to alternative experts"
- * ("GShard: Scaling Giant Neural Networks with Conditional Computation"
- * (blog), paragraph "Expert Capacity") and give no rule; this library's rule:
+ * blog ("GShard: Scaling Giant Neural Networks with Conditional Computation",
+ * paragraph "Expert Capacity") lets tokens over capacity go to other experts
+ * instead of being dropped, and gives no rule for it; this library's rule:
  * after the capacity pass, the j-th dropped assignment of token s (dropped
  * ranks in rank order) is offered to the token's (k+j)-th ranked expert (all
  * E experts ordered by logit descending, index ascending; none when
@@ -150,21 +158,28 @@ typedef struct moe_config {
 
 /* Capacity C of the config (capacity if > 0, else ceil(cf*k*S/E); S with
  * MOE_CFG_DROPLESS, which no expert can exceed), or -1 if the config is
- * invalid. */
+ * invalid.  Source: blog, paragraph "Expert Capacity" (a per-expert token
+ * limit set by the capacity factor); paper card, method paragraph. */
 int32_t moe_capacity(const moe_config *cfg);
 
 /* Rows of the dispatch buffer xd and the expert output out: E*C in capacity
- * mode, S*k with MOE_CFG_DROPLESS; -1 if the config is invalid. */
+ * mode, S*k with MOE_CFG_DROPLESS; -1 if the config is invalid.  Source: the
+ * per-expert buffers of the dispatch step (atlas, "In plain words"). */
 int64_t moe_dispatch_rows(const moe_config *cfg);
 
 /* Device workspace bytes that moe_layer_forward needs (enough for every
- * other entry point too) when all of its optional outputs are NULL. */
+ * other entry point too) when all of its optional outputs are NULL.  (No
+ * passage: the workspace is this library's own scratch.) */
 moe_status moe_workspace_bytes(const moe_config *cfg, size_t *bytes);
 
 /* Static text for a status code. */
 const char *moe_status_string(int32_t status);
 
-/* Router, top-k and capacity slots.
+/* Router, top-k and capacity slots.  Source: blog, "Mixture-of-Experts
+ * Implementation" (G(x) = Softmax(x . W_g), the top-k experts of it); paper
+ * card, method paragraph (top-2 gating, softmax-normalised top-2 weights,
+ * auxiliary loss and z-loss, tokens over capacity dropped); blog, paragraph
+ * "Expert Capacity".
  * In:  x [S,d] act, w_gate [E,d] fp32, gate_bias [E] fp32 or NULL
  *      (all unused with MOE_GATE_LOGITS_IN).
  * Out: logits [S,E] fp32 (input with MOE_GATE_LOGITS_IN; may be NULL
@@ -179,13 +194,16 @@ moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,
                     uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Permute token rows into per-expert capacity buffers (the local stand-in
- * for the dispatch all-to-all): xd[idx[s,r], slot[s,r], :] = x[s, :] for
+ * for the dispatch all-to-all; source: atlas "GShard (Expert Parallelism)",
+ * "In plain words": tokens are sent to their experts by an all-to-all): xd[idx[s,r], slot[s,r], :] = x[s, :] for
  * every slot[s,r] >= 0 (with MOE_CFG_DROPLESS: xd[slot[s,r], :] = x[s, :]).
  * Bit-exact copy.  Needs no workspace. */
 moe_status moe_dispatch(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                         const int32_t *slot, void *xd, hipStream_t stream);
 
-/* Expert FFNs over the filled slots: for e < E and c < occ_e =
+/* Expert FFNs over the filled slots (source: blog, section "Core
+ * Components", "Expert Networks": each expert is a feed-forward network; the
+ * ReLU two-layer form is the workload's): for e < E and c < occ_e =
  * min(sum_r counts[r,e], C): out[e,c] = ReLU(xd[e,c] W1_e^T + b1_e) W2_e^T
  * + b2_e, fp32 accumulation; the hidden activations are rounded to act_dtype
  * (they live in ws).  Rows c >= occ_e of out are not written.  With
@@ -198,7 +216,9 @@ moe_status moe_expert_ffn(const moe_config *cfg, const void *xd, const int32_t *
                           void *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Gate-weighted combine back to token order (the local stand-in for the
- * second all-to-all): y[s] = sum over slot[s,r] >= 0 of
+ * second all-to-all; source: research-vault claim IX2-0404, "WideEP",
+ * "Evidence": results return by a second all-to-all; the weights are the
+ * paper card's softmax-normalised top-2 weights): y[s] = sum over slot[s,r] >= 0 of
  * topk_w[s,r] * out[topk_idx[s,r], slot[s,r]], fp32 accumulation, rounded
  * to act_dtype; y[s] = 0 when every assignment of s was dropped.  With
  * MOE_CFG_DROPLESS the row read is out[slot[s,r]].  Needs no workspace. */
@@ -207,7 +227,8 @@ moe_status moe_combine(const moe_config *cfg, const void *out, const int32_t *to
                        hipStream_t stream);
 
 /* The whole forward pass: gate, slots, dispatch, expert FFNs, combine and
- * losses, enqueued back to back with no host synchronisation.
+ * losses, enqueued back to back with no host synchronisation (the passages
+ * cited at moe_gate, moe_dispatch, moe_expert_ffn and moe_combine).
  * Required: x, w_gate, w1, w2, y, ws.  Optional (NULL = not wanted, kept in
  * ws): gate_bias, b1, b2, logits, topk_idx, topk_w, slot, counts, losses,
  * xd, out, hidden.  When xd and out are both NULL one workspace buffer serves

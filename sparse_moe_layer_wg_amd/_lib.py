@@ -79,15 +79,18 @@ _lib = None
 
 
 def library():
-    """Load ``libmoe.so`` (building it first if it does not exist)."""
+    """Load ``libmoe.so``, building it first when it is missing or was built
+    from sources other than the ones in the tree (a digest of csrc/ and
+    include/ is stored beside the library); a failed build raises."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(library_path):
-        from . import _build
+    from . import _build
+    if not _build.is_current(library_path, library_path + ".srcsha"):
         _build.build()
-    if not os.path.exists(library_path):
-        raise RuntimeError(f"HIP library {library_path} is missing and could not be built")
+    if not _build.is_current(library_path, library_path + ".srcsha"):
+        raise RuntimeError(f"HIP library {library_path} is missing or stale and could not be "
+                           f"built from the sources")
     lib = ctypes.CDLL(library_path)
     vp, cfgp = ctypes.c_void_p, ctypes.POINTER(MoeConfig)
     lib.moe_capacity.argtypes = [cfgp]

@@ -54,6 +54,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <atomic>
+
 #include <type_traits>
 
 namespace moe {
@@ -441,19 +443,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 
 }  // namespace
 
-// Compute units of the current device (one-time query per process and device).
+// Compute units of the current device.  The attribute is queried once per
+// device and kept in a process-wide table (every writer stores the same
+// value, so concurrent first calls agree).
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n < 8)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // m-tile height: 256 when experts average at least 160 rows (each weight

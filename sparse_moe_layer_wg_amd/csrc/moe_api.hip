@@ -64,6 +64,9 @@ moe_status make_plan(const moe_config* c, Plan* pl) {
     if (rows * wide >= 2147483648.0) return MOE_ERR_UNSUPPORTED;
     if ((double)c->S * wide >= 2147483648.0 || (double)c->S * c->E >= 2147483648.0)
         return MOE_ERR_UNSUPPORTED;
+    // one expert's weight matrix is addressed with 32-bit byte offsets
+    if ((double)c->d_model * c->d_ff * (bf16 ? 2.0 : 4.0) >= 4294967296.0)
+        return MOE_ERR_UNSUPPORTED;
     pl->S = c->S;
     pl->d = c->d_model;
     pl->h = c->d_ff;

@@ -19,6 +19,10 @@ import sparse_moe_layer_wg_amd as moe
 from sparse_moe_layer_wg_amd.layer import MoELayer
 
 TOL = {"f32": 1e-5, "bf16": 1e-2}
+# every single row (of y, of the expert outputs) within this multiple of the
+# whole-tensor bar: a lost, doubled or misplaced GEMM tile shows up in the
+# rows it covers even where the whole-tensor error would stay below the bar
+ROW_FACTOR = 3.0
 LOSS_TOL = 1e-5
 AGREEMENT = 0.9999
 
@@ -28,6 +32,52 @@ def rel_fro(a, b) -> float:
     b = np.asarray(b, np.float64)
     nb = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def row_rel(a, b) -> np.ndarray:
+    """Relative error of every row (last axis) of a against b.  A row that is
+    zero in b must be exactly zero in a (error 0, else inf)."""
+    a = np.asarray(a, np.float64).reshape(-1, np.shape(a)[-1])
+    b = np.asarray(b, np.float64).reshape(-1, np.shape(b)[-1])
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    safe = np.where(den > 0, den, 1.0)
+    return np.where(den > 0, num / safe, np.where(num == 0, 0.0, np.inf))
+
+
+def check_rows(rep: dict, key: str, a, b, tol: float):
+    """Whole-tensor relative Frobenius error and the largest row error, both
+    recorded in rep and asserted against tol and ROW_FACTOR * tol."""
+    rep[key + "_rel"] = rel_fro(a, b)
+    rows = row_rel(a, b)
+    rep[key + "_row_max"] = float(rows.max()) if rows.size else 0.0
+    rep[key + "_rows"] = int(rows.size)
+    assert rep[key + "_rel"] <= tol, rep
+    assert rep[key + "_row_max"] <= ROW_FACTOR * tol, rep
+
+
+def expert_ffn_chunked(xd, occ, w1, b1, w2, b2, chunk_flop: float = 1.5e12) -> np.ndarray:
+    """oracle.expert_ffn over groups of experts, printing a line after each
+    group (a full-size check runs the oracle for minutes)."""
+    import time
+    E, C, d = xd.shape
+    h = w1.shape[1]
+    out = np.zeros((E, C, d), np.float64)
+    t0 = time.perf_counter()
+    e0 = 0
+    while e0 < E:
+        e1, fl = e0, 0.0
+        while e1 < E and (e1 == e0 or fl + 4.0 * d * h * occ[e1] <= chunk_flop):
+            fl += 4.0 * d * h * occ[e1]
+            e1 += 1
+        out[e0:e1] = oracle.expert_ffn(xd[e0:e1], occ[e0:e1], w1[e0:e1],
+                                       None if b1 is None else b1[e0:e1], w2[e0:e1],
+                                       None if b2 is None else b2[e0:e1])
+        if E > 1:
+            print(f"  oracle experts {e0}..{e1 - 1} of {E}: {time.perf_counter() - t0:.1f} s",
+                  flush=True)
+        e0 = e1
+    return out
 
 
 def as_f64(t) -> np.ndarray:
@@ -93,12 +143,12 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
         if xd_gpu is not None:
             xd_h = mw.to_numpy(xd_gpu)
             assert np.array_equal(xd_h[filled], xd_or[filled]), "dispatch buffer is not a bit copy"
-        out_or = oracle.expert_ffn(xd_or, occ, host["w1"], host["b1"], host["w2"], host["b2"])
-        rep["out_rel"] = rel_fro(as_f64(out_gpu)[filled], out_or[filled])
-        assert rep["out_rel"] <= tol, rep
+        out_or = expert_ffn_chunked(xd_or, occ, host["w1"], host["b1"], host["w2"], host["b2"])
+        del xd_or
+        check_rows(rep, "out", as_f64(out_gpu)[filled], out_or[filled], tol)
         y_or = oracle.combine(out_or, r["serve"], r["slot"], r["w"], S)
-        rep["y_rel"] = rel_fro(y_gpu, y_or)
-        assert rep["y_rel"] <= tol, rep
+        del out_or
+        check_rows(rep, "y", y_gpu, y_or, tol)
         dropped_all = (r["slot"] < 0).all(axis=1)
         assert np.all(y_gpu[dropped_all] == 0)
         return rep
@@ -120,8 +170,7 @@ def check_layer(w: mw.Workload, inputs, layer, full: bool, n_sample: int = 96, s
                 assert np.array_equal(row, host["x"][s]), "dispatch row differs"
     y_or = oracle.token_output(tok, host["x"], host["w1"], host["b1"], host["w2"], host["b2"],
                                r["serve"], r["slot"], r["w"])
-    rep["y_rel"] = rel_fro(y_gpu[tok], y_or)
-    assert rep["y_rel"] <= tol, rep
+    check_rows(rep, "y", y_gpu[tok], y_or, tol)
     return rep
 
 
@@ -168,10 +217,8 @@ def _check_dropless(w, inputs, layer, r, full, n_sample, seed, rep):
         if layer.xd is not None:
             assert np.array_equal(mw.to_numpy(layer.xd), res["xd_rows"]), \
                 "compact dispatch buffer is not a bit copy"
-        rep["out_rel"] = rel_fro(as_f64(layer.out), res["out_rows"])
-        assert rep["out_rel"] <= tol, rep
-        rep["y_rel"] = rel_fro(y_gpu, res["y"])
-        assert rep["y_rel"] <= tol, rep
+        check_rows(rep, "out", as_f64(layer.out), res["out_rows"], tol)
+        check_rows(rep, "y", y_gpu, res["y"], tol)
         return rep
     rng = np.random.default_rng(seed)
     tok = np.sort(rng.choice(w.S, size=min(n_sample, w.S), replace=False))
@@ -181,6 +228,5 @@ def _check_dropless(w, inputs, layer, r, full, n_sample, seed, rep):
                 assert np.array_equal(mw.to_numpy(layer.xd[rows[s, rr]]), host["x"][s])
     y_or = oracle.token_output(tok, host["x"], host["w1"], host["b1"], host["w2"], host["b2"],
                                r["idx"], r["slot"], r["w"])
-    rep["y_rel"] = rel_fro(y_gpu[tok], y_or)
-    assert rep["y_rel"] <= tol, rep
+    check_rows(rep, "y", y_gpu[tok], y_or, tol)
     return rep

@@ -103,8 +103,14 @@ def test_unsupported_shapes_rejected_on_host():
                 moe.config(10, 64, 100, 4, 2, dtype="bf16"),    # h not a multiple of 64
                 moe.config(10, 66, 64, 4, 2, dtype="f32"),      # d not a multiple of 4
                 moe.config(10, 64, 64, 4096, 2),                # E > 2048
-                moe.config(10, 64, 64, 16, 9)]:                 # k > 8
+                moe.config(10, 64, 64, 16, 9),                  # k > 8
+                # one expert matrix of 4 GiB or more: its byte offsets are 32-bit
+                moe.config(1, 65536, 32768, 1, 1, capacity=1, dtype="bf16"),
+                moe.config(1, 32768, 32768, 1, 1, capacity=1, dtype="f32")]:
         assert lib.moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 2
+    # just under the limit: supported
+    ok = moe.config(1, 65536, 32704, 1, 1, capacity=1, dtype="bf16")
+    assert lib.moe_workspace_bytes(ctypes.byref(ok), ctypes.byref(n)) == 0
 
 
 def test_workspace_size_and_errors_before_launch():
@@ -189,3 +195,43 @@ def test_backward_validation_on_host():
     assert call(drop=10) == 1                           # forward expert outputs missing
     assert call(g_aux=float("nan")) == 1                # loss weight not finite
     assert moe.backward_workspace_bytes(moe.config(2000, 128, 256, 8, 2, dropless=True)) > 0
+
+
+def test_stale_library_is_rebuilt(tmp_path, monkeypatch):
+    """library() builds again when the sources differ from those the loaded
+    library was built from (the digest stored beside it), and loads it
+    without a build when they match."""
+    import shutil
+    from sparse_moe_layer_wg_amd import _build
+    src = tmp_path / "csrc"
+    inc = tmp_path / "include"
+    shutil.copytree(_build.CSRC, src)
+    shutil.copytree(_build.INCLUDE, inc)
+    lib = tmp_path / "libmoe.so"
+    lib.write_bytes(b"")
+    stamp = tmp_path / "libmoe.so.srcsha"
+    paths = _build.sources(str(src), str(inc))
+    stamp.write_text(_build.source_digest(paths) + "\n")
+    assert _build.is_current(str(lib), str(stamp), paths)
+    # the digest covers every source file, headers included
+    one = src / "permute.hip"
+    one.write_text(one.read_text() + "\n// edited\n")
+    assert not _build.is_current(str(lib), str(stamp), paths)
+    (inc / "moe.h").write_text((inc / "moe.h").read_text())   # unchanged content
+    stamp.write_text(_build.source_digest(paths) + "\n")
+    assert _build.is_current(str(lib), str(stamp), paths)
+    (inc / "moe.h").write_text((inc / "moe.h").read_text() + " ")
+    assert not _build.is_current(str(lib), str(stamp), paths)
+    assert not _build.is_current(str(tmp_path / "missing.so"), str(stamp), paths)
+
+    # library() itself: a stale stamp triggers exactly one build
+    calls = []
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_build, "is_current",
+                        lambda *a, **k: len(calls) > 0)
+    monkeypatch.setattr(_build, "build", lambda *a, **k: calls.append(1))
+    monkeypatch.setattr(_lib.ctypes, "CDLL", lambda path: (_ for _ in ()).throw(
+        RuntimeError("loaded")))
+    with pytest.raises(RuntimeError, match="loaded"):
+        _lib.library()
+    assert calls == [1]

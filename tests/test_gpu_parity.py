@@ -226,18 +226,38 @@ def test_fused_gather_matches_dispatch_buffer(w):
 
 
 # --------------------------------------------------------------------- full sizes
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["balanced_bf16", "skewed_bf16", "large_bf16", "deepseek_bf16"])
-def test_full_size_sampled(name):
+def test_full_size_whole(name):
     """Full-size workloads in the benchmark's launch configuration (no dispatch
     buffer: the gather is fused into the first expert GEMM): all routing
-    checked exactly, y checked on sampled tokens (including dropped ones)."""
+    checked exactly, and every filled expert-output row and every row of y
+    against the oracle, each row on its own as well as the whole tensor."""
+    import time
     w = mw.get(name)
     print(f"\n[full] {w}", flush=True)
     inputs, layer = run_layer(w, dispatch_buffer=False)
-    rep = check_layer(w, inputs, layer, full=False)
+    t0 = time.perf_counter()
+    rep = check_layer(w, inputs, layer, full=True)
+    rep["oracle_s"] = time.perf_counter() - t0
     _print(name, rep)
     del layer, inputs
     torch.cuda.empty_cache()
+
+
+# Many more GEMM tiles than compute units (512 per forward GEMM against 256
+# CUs), so every persistent block claims several tiles in a row: the tile
+# counters, the claim of the next tile during an epilogue and the reuse of
+# LDS between tiles all run, and every row is checked.
+MANY_TILES = mw.Workload("many_tiles_bf16", S=8192, d=2048, h=2048, E=16, k=2,
+                         capacity_factor=1.0, dtype="bf16", seed=17)
+
+
+@pytest.mark.timeout(600)
+def test_many_tiles_whole():
+    print(f"\n[many tiles] {MANY_TILES}", flush=True)
+    inputs, layer = run_layer(MANY_TILES, dispatch_buffer=False)
+    _print(MANY_TILES.name, check_layer(MANY_TILES, inputs, layer, full=True))
 
 
 # --------------------------------------------------------------------- near-tie refinement
