@@ -53,6 +53,9 @@ def parse():
                     help="time a training step: forward + moe_layer_backward")
     ap.add_argument("--ep-share", default=None, choices=list(mw.EP_SHARES),
                     help="time the expert FFN at one GPU's expert-parallel share instead")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the expert FFN at uniform occupancy (S*k/E rows per expert) "
+                         "against the same GEMMs through hipBLASLt (torch.bmm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -207,6 +210,9 @@ def main():
         print(json.dumps(out), flush=True)
         return
     w = mw.get(a.workload)
+    if a.vendor_gemm:
+        print(json.dumps(bench_vendor_gemm(a, w)), flush=True)
+        return
     if a.dropless and a.reroute:
         print("--dropless drops nothing: --reroute does not apply", file=sys.stderr)
         sys.exit(2)
@@ -464,6 +470,64 @@ def bench_ep_share(a, sh) -> dict:
                                  "sample": f"the first {m} rows of each of the {sh.E_local} local "
                                            f"experts through the fp64 oracle FFN, {tc:.1f} s"}
     return out_d
+
+
+def bench_vendor_gemm(a, w: mw.Workload) -> dict:
+    """Both expert GEMMs at uniform occupancy, m = ceil(S*k/E) rows per
+    expert: moe_expert_ffn (this library) against torch.bmm, which runs
+    hipBLASLt, on the same operands (the weights transposed once, outside the
+    timed region, into the [K,N] layout bmm takes contiguously; ReLU between
+    the two products).  Median of `steps` timed calls after `warmup`."""
+    S, d, h, E, k = w.S, w.d, w.h, w.E, w.k
+    m = -(-S * k // E)
+    inp = mw.generate(w, "cuda")
+    w1, w2 = inp["w1"], inp["w2"]
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 7)
+    xd = torch.randn((E, m, d), generator=g, device="cuda").to(w.torch_dtype)
+    cfg = moe.config(E * m, d, h, E, 1, capacity=m, dtype=w.dtype)
+    cnt = torch.full((1, E), m, dtype=torch.int32, device="cuda")
+    out = torch.empty((E, m, d), dtype=w.torch_dtype, device="cuda")
+    ws = torch.empty(moe.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    w1t = w1.transpose(1, 2).contiguous()      # [E,d,h]
+    w2t = w2.transpose(1, 2).contiguous()      # [E,h,d]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(a.steps)]
+        torch.cuda.synchronize()
+        for b, e in evs:
+            b.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([b.elapsed_time(e) * 1000.0 for b, e in evs]))
+
+    ours = timed(lambda: moe.expert_ffn(cfg, xd, cnt, w1, None, w2, None, out, ws))
+    hbuf = torch.empty((E, m, h), dtype=w.torch_dtype, device="cuda")
+    obuf = torch.empty((E, m, d), dtype=w.torch_dtype, device="cuda")
+    g1 = timed(lambda: torch.bmm(xd, w1t, out=hbuf))
+    g2 = timed(lambda: torch.bmm(hbuf, w2t, out=obuf))
+    relu = timed(lambda: hbuf.relu_())
+    # the two paths agree (same operands, fp32 accumulation in both)
+    torch.bmm(xd, w1t, out=hbuf)
+    hbuf.relu_()
+    torch.bmm(hbuf, w2t, out=obuf)
+    moe.expert_ffn(cfg, xd, cnt, w1, None, w2, None, out, ws)
+    torch.cuda.synchronize()
+    diff = float((out.float() - obuf.float()).norm() / obuf.float().norm())
+    flops = 2 * 2.0 * E * m * d * h
+    return {"metric": "expert FFN at uniform occupancy: moe_expert_ffn vs hipBLASLt (torch.bmm)",
+            "config": {"workload": w.name, "E": E, "rows_per_expert": m, "d_model": d, "d_ff": h},
+            "steps": a.steps, "warmup": a.warmup,
+            "moe_expert_ffn_us": ours,
+            "hipblaslt_gemm1_us": g1, "hipblaslt_gemm2_us": g2, "relu_us": relu,
+            "hipblaslt_gemms_us": g1 + g2,
+            "moe_expert_ffn_tflops": flops / ours / 1e6,
+            "hipblaslt_tflops": flops / (g1 + g2) / 1e6,
+            "rel_diff": diff}
 
 
 BWD_STAGES = ["setup", "recompute_h", "combine_router_bwd", "wgrad2", "dgrad2", "wgrad1",
