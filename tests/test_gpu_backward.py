@@ -143,14 +143,46 @@ def test_backward_many_tiles_whole():
                                 mw.to_numpy(dy), 0.7, 0.3)
     rep = {key: rel_fro(as_f64(grads[key]), ref[key])
            for key in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2")}
-    rep["dx_row_max"] = float(row_rel(as_f64(grads["dx"]), ref["dx"]).max())
+    rows = row_rel(as_f64(grads["dx"]), ref["dx"])
     rep["dw1_tile_max"] = _block_rel_max(as_f64(grads["dw1"]), ref["dw1"])
     rep["dw2_tile_max"] = _block_rel_max(as_f64(grads["dw2"]), ref["dw2"])
     rep["db1_row_max"] = float(row_rel(as_f64(grads["db1"]), ref["db1"]).max())
     rep["db2_row_max"] = float(row_rel(as_f64(grads["db2"]), ref["db2"]).max())
+    # dx rows: a hidden pre-activation within fp32 rounding of zero can land
+    # on the other side of the ReLU in the GPU's fp32 accumulation than in
+    # the oracle's fp64, and that unit's whole W1 row then enters dx or not
+    # (about 1/sqrt(active units) of the row, ~3% at d_ff = 2048).  A row
+    # above the per-row bar must hold such a unit (|u| within 1e-5 of the
+    # pre-activations' rms); such rows must be rare and stay below 0.1.
+    over = np.nonzero(rows > 3 * TOL)[0]
+    slot = layer.slot.cpu().numpy()
+    idx = layer.topk_idx.cpu().numpy()
+    for s in over:
+        assert rows[s] <= 0.1, (s, rows[s])
+        assert _near_kink(host, idx[s], slot[s], s), (s, rows[s])
+    assert len(over) <= max(2, w.S // 1000), len(over)
+    rep["dx_rows_over_bar"] = int(len(over))
+    rep["dx_row_max_else"] = float(np.delete(rows, over).max())
     _print(w.name + "_bwd", rep)
     for key, err in rep.items():
-        assert err <= (3 * TOL if key.endswith("_max") else TOL), (key, rep)
+        if key != "dx_rows_over_bar":
+            assert err <= (3 * TOL if key.endswith(("_max", "_else")) else TOL), (key, rep)
+
+
+def _near_kink(host, idx_s, slot_s, s, rel=1e-5):
+    """Whether token s has, in one of its kept experts, a hidden
+    pre-activation u = W1_e x_s + b1_e (fp64) within rel * rms(u) of zero."""
+    f64 = lambda a: (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    x = f64(host["x"][s])
+    for e, c in zip(idx_s, slot_s):
+        if c < 0:
+            continue
+        u = f64(host["w1"][e]) @ x
+        if host["b1"] is not None:
+            u += f64(host["b1"][e])
+        if np.abs(u).min() <= rel * np.sqrt(np.mean(u * u)):
+            return True
+    return False
 
 
 def test_backward_saved_hidden_matches_recompute():
