@@ -38,7 +38,9 @@
  *     owns (for example a torch tensor's data_ptr()).  The config is host
  *     memory.  The library allocates and frees nothing and keeps no pointer
  *     after a call returns.  Its only process-wide state is a per-device
- *     cache of the compute-unit count (filled on first use, never changed).
+ *     cache of the compute-unit count and, for moe_gate_noalloc, the
+ *     per-device address of its static scratch (both filled on first use,
+ *     never changed).
  *   Execution.  Work is enqueued on `stream` (0 = the null stream) and is
  *     asynchronous: outputs are valid once the stream has been synchronised.
  *     The library performs no host<->device copies and no synchronisation.
@@ -83,7 +85,9 @@ typedef enum moe_status {
     MOE_ERR_INVALID_ARG = 1,
     MOE_ERR_UNSUPPORTED = 2,
     MOE_ERR_WORKSPACE = 3,
-    MOE_ERR_HIP = 4
+    MOE_ERR_HIP = 4,
+    MOE_ERR_SCRATCH_LIMIT = 5  /* moe_gate_noalloc: the shape needs more scratch
+                                  than MOE_STATIC_SCRATCH_BYTES */
 } moe_status;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -192,6 +196,31 @@ moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,
                     const float *gate_bias, float *logits, int32_t *topk_idx,
                     float *topk_w, int32_t *slot, int32_t *counts, float *losses,
                     uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of the library's static device scratch (per GPU), the most that
+ * moe_gate_noalloc may use. */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* moe_gate without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments (minus ws, ws_bytes), same kernels and
+ * same results as moe_gate.  Its scratch is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES bytes inside the library: each GPU the library
+ * runs on holds its own copy from the first call on that GPU until the
+ * process ends.  The call allocates and frees nothing.  Its first call on a
+ * device looks the array's address up once (hipGetSymbolAddress) and keeps
+ * it; later calls reuse it.  A shape whose router scratch would exceed the
+ * array (the router part of moe_workspace_bytes: room for the logits, the
+ * per-tile histograms and probability partials, the m-tile table and the
+ * re-routing offers) is refused with MOE_ERR_SCRATCH_LIMIT before anything
+ * is enqueued; the five benchmark shapes fit (the largest, S = 65536 tokens
+ * over E = 64 experts, needs about 19 MiB).  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (nothing in it needs to start at zero): calls that
+ * overlap on one GPU race, so order them on one stream or serialise them. */
+moe_status moe_gate_noalloc(const moe_config *cfg, const void *x, const float *w_gate,
+                            const float *gate_bias, float *logits, int32_t *topk_idx,
+                            float *topk_w, int32_t *slot, int32_t *counts, float *losses,
+                            uint32_t flags, hipStream_t stream);
 
 /* Permute token rows into per-expert capacity buffers (the local stand-in
  * for the dispatch all-to-all; source: atlas "GShard (Expert Parallelism)",

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MOE_GATE_LOGITS_IN,
     MOE_NUM_BWD_EVENTS,
     MOE_NUM_STAGE_EVENTS,
+    MOE_STATIC_SCRATCH_BYTES,
     MoeConfig,
     MoeError,
     backward_workspace_bytes,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     dispatch_rows,
     expert_ffn,
     gate,
+    gate_noalloc,
     layer_backward,
     layer_forward,
     library,

@@ -22,8 +22,10 @@ MOE_CFG_REROUTE = 2
 MOE_NUM_STAGE_EVENTS = 9
 MOE_NUM_BWD_EVENTS = 9
 
+MOE_STATIC_SCRATCH_BYTES = 32 << 20
+
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
-           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP", 5: "MOE_ERR_SCRATCH_LIMIT"}
 
 
 class MoeError(RuntimeError):
@@ -102,6 +104,8 @@ def library():
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_gate.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp,
                              ctypes.c_size_t, vp]
+    lib.moe_gate_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_uint32, vp]
     lib.moe_dispatch.argtypes = [cfgp, vp, vp, vp, vp, vp]
     lib.moe_expert_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
@@ -110,7 +114,7 @@ def library():
     f32 = ctypes.c_float
     lib.moe_layer_backward.argtypes = [cfgp] + [vp] * 13 + [f32, f32] + [vp] * 8 + \
         [ctypes.c_size_t, vp, vp]
-    for f in ("moe_workspace_bytes", "moe_gate", "moe_dispatch", "moe_expert_ffn",
+    for f in ("moe_workspace_bytes", "moe_gate", "moe_gate_noalloc", "moe_dispatch", "moe_expert_ffn",
               "moe_combine", "moe_layer_forward", "moe_backward_workspace_bytes",
               "moe_layer_backward"):
         getattr(lib, f).restype = ctypes.c_int32
@@ -202,6 +206,27 @@ def gate(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, loss
         _arg(losses, "losses", torch.float32, 2),
         MOE_GATE_LOGITS_IN if logits_in else 0, wsp, wsb, _stream(stream))
     _check(st, "moe_gate")
+
+
+def gate_noalloc(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, losses,
+                 logits_in=False, stream=None):
+    """``moe_gate`` on the library's static scratch (``moe_gate_noalloc``): no
+    workspace argument, nothing allocated."""
+    S, d, E, k = cfg.S, cfg.d_model, cfg.E, cfg.k
+    at = cfg.torch_dtype
+    st = library().moe_gate_noalloc(
+        ctypes.byref(cfg),
+        _arg(x, "x", at, S * d, required=not logits_in),
+        _arg(w_gate, "w_gate", torch.float32, E * d, required=not logits_in),
+        _arg(gate_bias, "gate_bias", torch.float32, E, required=False),
+        _arg(logits, "logits", torch.float32, S * E, required=logits_in),
+        _arg(topk_idx, "topk_idx", torch.int32, S * k),
+        _arg(topk_w, "topk_w", torch.float32, S * k),
+        _arg(slot, "slot", torch.int32, S * k),
+        _arg(counts, "counts", torch.int32, cfg.count_rows * E),
+        _arg(losses, "losses", torch.float32, 2),
+        MOE_GATE_LOGITS_IN if logits_in else 0, _stream(stream))
+    _check(st, "moe_gate_noalloc")
 
 
 def dispatch(cfg, x, topk_idx, slot, xd, stream=None):

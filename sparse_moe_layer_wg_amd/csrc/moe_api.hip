@@ -7,6 +7,17 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
+// Scratch of moe_gate_noalloc, for callers that cannot allocate: a
+// device-side array of the code object, so each GPU the library runs on holds
+// its own copy from the module's load until the process ends.  Host code
+// never uses this name as an address (on the host it is only a stand-in for
+// the symbol): the device address is looked up with hipGetSymbolAddress,
+// once per device, and that pointer is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace moe;
@@ -246,6 +257,63 @@ moe_status run_ffn(const Plan& p, const void* xd, const int32_t* a_rows, const v
     return MOE_OK;
 }
 
+// Device address of the current device's copy of `scratch`, looked up with
+// hipGetSymbolAddress the first time a device asks and kept per device.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+                return MOE_ERR_HIP;
+            g_scratch[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return MOE_OK;
+}
+
+// moe_gate's body.  use_static: the scratch is this device's static array
+// (ws ignored) and a shape whose scratch exceeds it is refused.
+moe_status gate_call(const moe_config* cfg, const void* x, const float* w_gate,
+                     const float* gate_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     int32_t* slot, int32_t* counts, float* losses, uint32_t flags, void* ws,
+                     size_t ws_bytes, bool use_static, hipStream_t stream) {
+    Plan p;
+    moe_status s = make_plan(cfg, &p);
+    if (s != MOE_OK) return s;
+    if (flags & ~MOE_GATE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+    const bool logits_in = (flags & MOE_GATE_LOGITS_IN) != 0;
+    if (!counts || !losses) return MOE_ERR_INVALID_ARG;
+    if (p.S > 0 && (!topk_idx || !topk_w || !slot)) return MOE_ERR_INVALID_ARG;
+    if (p.S > 0 && (logits_in ? !logits : (!x || !w_gate))) return MOE_ERR_INVALID_ARG;
+    if (!logits_in && (!aligned(x, 16) || !aligned(w_gate, 16))) return MOE_ERR_INVALID_ARG;
+    if (p.S == 0) {
+        MOE_TRY(launch_zero_outputs(counts, p.crows * p.E, losses, stream));
+        return MOE_OK;
+    }
+    const Carve cv = carve(p);
+    if (use_static) {
+        if (cv.route_end > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_LIMIT;
+        s = scratch_address(&ws);
+        if (s != MOE_OK) return s;
+    } else {
+        if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+        if (ws_bytes < cv.route_end) return MOE_ERR_WORKSPACE;
+    }
+    float* L = logits ? logits : at<float>(ws, cv.logits);
+    return run_gate(p, cv, x, w_gate, gate_bias, L, logits_in, topk_idx, topk_w, slot, counts,
+                    losses, ws, nullptr, nullptr, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +361,9 @@ const char* moe_status_string(int32_t status) {
         case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype not supported";
         case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
         case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch failed";
+        case MOE_ERR_SCRATCH_LIMIT:
+            return "MOE_ERR_SCRATCH_LIMIT: shape needs more than the static scratch "
+                   "(MOE_STATIC_SCRATCH_BYTES)";
         default: return "unknown moe_status";
     }
 }
@@ -301,25 +372,16 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const float* w_gate,
                     const float* gate_bias, float* logits, int32_t* topk_idx, float* topk_w,
                     int32_t* slot, int32_t* counts, float* losses, uint32_t flags, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
-    Plan p;
-    moe_status s = make_plan(cfg, &p);
-    if (s != MOE_OK) return s;
-    if (flags & ~MOE_GATE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
-    const bool logits_in = (flags & MOE_GATE_LOGITS_IN) != 0;
-    if (!counts || !losses) return MOE_ERR_INVALID_ARG;
-    if (p.S > 0 && (!topk_idx || !topk_w || !slot)) return MOE_ERR_INVALID_ARG;
-    if (p.S > 0 && (logits_in ? !logits : (!x || !w_gate))) return MOE_ERR_INVALID_ARG;
-    if (!logits_in && (!aligned(x, 16) || !aligned(w_gate, 16))) return MOE_ERR_INVALID_ARG;
-    if (p.S == 0) {
-        MOE_TRY(launch_zero_outputs(counts, p.crows * p.E, losses, stream));
-        return MOE_OK;
-    }
-    if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
-    const Carve cv = carve(p);
-    if (ws_bytes < cv.route_end) return MOE_ERR_WORKSPACE;
-    float* L = logits ? logits : at<float>(ws, cv.logits);
-    return run_gate(p, cv, x, w_gate, gate_bias, L, logits_in, topk_idx, topk_w, slot, counts,
-                    losses, ws, nullptr, nullptr, stream);
+    return gate_call(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, losses,
+                     flags, ws, ws_bytes, false, stream);
+}
+
+moe_status moe_gate_noalloc(const moe_config* cfg, const void* x, const float* w_gate,
+                            const float* gate_bias, float* logits, int32_t* topk_idx,
+                            float* topk_w, int32_t* slot, int32_t* counts, float* losses,
+                            uint32_t flags, hipStream_t stream) {
+    return gate_call(cfg, x, w_gate, gate_bias, logits, topk_idx, topk_w, slot, counts, losses,
+                     flags, nullptr, MOE_STATIC_SCRATCH_BYTES, true, stream);
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,

@@ -235,3 +235,26 @@ def test_stale_library_is_rebuilt(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="loaded"):
         _lib.library()
     assert calls == [1]
+
+
+def test_noalloc_gate_refuses_shapes_beyond_the_static_scratch():
+    """moe_gate_noalloc refuses, on the host and before anything is enqueued,
+    a valid shape whose router scratch exceeds MOE_STATIC_SCRATCH_BYTES
+    (here 64 MiB of logits alone); bad arguments fail as in moe_gate."""
+    lib = moe.library()
+    fake = ctypes.c_void_p(1 << 20)     # never dereferenced
+    big = moe.config(262144, 64, 64, 64, 2, 1.0, dtype="bf16")
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > moe.MOE_STATIC_SCRATCH_BYTES
+    for logits in (None, fake):
+        st = lib.moe_gate_noalloc(ctypes.byref(big), fake, fake, None, logits, fake, fake, fake,
+                                  fake, fake, 0, None)
+        assert st == 5
+    assert b"SCRATCH_LIMIT" in lib.moe_status_string(5)
+    # argument checks come first, as in moe_gate
+    small = moe.config(100, 64, 64, 8, 2, 1.0, dtype="bf16")
+    assert lib.moe_gate_noalloc(ctypes.byref(small), fake, fake, None, None, fake, fake, fake,
+                                None, fake, 0, None) == 1        # counts missing
+    assert lib.moe_gate_noalloc(ctypes.byref(small), fake, fake, None, None, fake, fake, fake,
+                                fake, fake, 8, None) == 1        # unknown flag
