@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="time the expert FFN at uniform occupancy (S*k/E rows per expert) "
                          "against the same GEMMs through hipBLASLt (torch.bmm)")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="time plain device-to-device copies (read + write) of 64 MiB to "
+                         "1 GiB: the HBM rate a streaming kernel can reach on this GPU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -208,6 +211,9 @@ def main():
         if a.copy_calibration_mb > 0:
             out["copy_calibration_bytes"] = calibration_copy(a.copy_calibration_mb)
         print(json.dumps(out), flush=True)
+        return
+    if a.copy_reference:
+        print(json.dumps(bench_copy_reference(a)), flush=True)
         return
     w = mw.get(a.workload)
     if a.vendor_gemm:
@@ -470,6 +476,33 @@ def bench_ep_share(a, sh) -> dict:
                                  "sample": f"the first {m} rows of each of the {sh.E_local} local "
                                            f"experts through the fp64 oracle FFN, {tc:.1f} s"}
     return out_d
+
+
+def bench_copy_reference(a) -> dict:
+    """Plain device copies (torch copy_, read + write) of several sizes:
+    median of `steps` timed copies after `warmup`, bytes counted both ways."""
+    out = {"metric": "device-to-device copy rate (read + write bytes)", "unit": "TB/s",
+           "steps": a.steps, "warmup": a.warmup, "copies": {}}
+    stream = torch.cuda.current_stream()
+    for mib in (64, 256, 1024):
+        src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(a.warmup):
+            dst.copy_(src)
+        ts = []
+        for _ in range(a.steps):
+            b = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            dst.copy_(src)
+            e.record(stream)
+            torch.cuda.synchronize()
+            ts.append(b.elapsed_time(e) * 1000.0)
+        us = float(np.median(ts))
+        out["copies"][f"{mib}MiB"] = {"us": us, "TB_s": 2.0 * (mib << 20) / us / 1e6}
+        del src, dst
+    return out
 
 
 def bench_vendor_gemm(a, w: mw.Workload) -> dict:

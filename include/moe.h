@@ -190,8 +190,13 @@ const char *moe_status_string(int32_t status);
  *      otherwise, then kept in ws), topk_idx [S,k], topk_w [S,k],
  *      slot [S,k] (-1 = dropped; with MOE_CFG_DROPLESS the global row in
  *      xd/out), counts [k,E] ([k+1,E] with MOE_CFG_REROUTE), losses [2].
- * Logits within a small margin of a top-k decision are re-evaluated in fp64
- * and rounded once to fp32, and the stored logits hold those values. */
+ * A top-k decision of token s between logits closer than the margin
+ * tau_s = 32 * 2^-24 * (|x_s| max_j |Wg_j| + max_j |bg_j| / 8) (Euclidean
+ * row norms) is re-evaluated: the tied logits are recomputed with fp64
+ * accumulation and rounded once to fp32, and the stored logits hold those
+ * values.  The margin scales with the inputs as the logit GEMM's rounding
+ * error does, so it stays well above that error at any scale of x, Wg and
+ * bg, and the decisions are those of an exactly rounded fp32 router. */
 moe_status moe_gate(const moe_config *cfg, const void *x, const float *w_gate,
                     const float *gate_bias, float *logits, int32_t *topk_idx,
                     float *topk_w, int32_t *slot, int32_t *counts, float *losses,

@@ -102,6 +102,27 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return r;
 }
 
+// Largest of non-negative floats across the wave (their bit patterns order
+// as unsigned integers); the result is the same in every lane.
+__device__ __forceinline__ float wave_max_nonneg_f32(float v) {
+    uint32_t u = __float_as_uint(v), o;
+    o = dpp_u32<kDppXor1>(u);
+    u = o > u ? o : u;
+    o = dpp_u32<kDppXor2>(u);
+    u = o > u ? o : u;
+    o = dpp_u32<kDppHalfMirror>(u);
+    u = o > u ? o : u;
+    o = dpp_u32<kDppMirror>(u);
+    u = o > u ? o : u;
+    uint32_t r = __builtin_amdgcn_readlane(u, 0);
+#pragma unroll
+    for (int l = 16; l < kWave; l += 16) {
+        o = __builtin_amdgcn_readlane(u, l);
+        r = o > r ? o : r;
+    }
+    return __uint_as_float(r);
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
     auto mv = [](double x, auto ctrl_tag) {
         constexpr int C = decltype(ctrl_tag)::value;

@@ -28,7 +28,9 @@ template <bool XBF16>
 __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict__ xv,
                                                           const float* __restrict__ wg,
                                                           const float* __restrict__ bg,
-                                                          float* __restrict__ logits, int S,
+                                                          float* __restrict__ logits,
+                                                          float* __restrict__ xn2,
+                                                          float* __restrict__ wn2, int S,
                                                           int d, int E) {
     __shared__ float As[GL_BK][GL_BM + 1];
     __shared__ float Bs[GL_BK][GL_BN + 1];
@@ -44,6 +46,7 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    float xsq = 0.f, wsq = 0.f;   // this thread's share of the row norms
 
     for (int k0 = 0; k0 < d; k0 += GL_BK) {
         float av[8], bv[8];
@@ -80,6 +83,8 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
         for (int q = 0; q < 8; ++q) {
             As[lk + q][lrow] = av[q];
             Bs[lk + q][lrow] = bv[q];
+            xsq = fmaf(av[q], av[q], xsq);
+            wsq = fmaf(bv[q], bv[q], wsq);
         }
         __syncthreads();
 #pragma unroll 8
@@ -104,6 +109,17 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
             const int e = j0 + tx + 16 * j;
             if (e < E) logits[(size_t)s * E + e] = acc[i][j] + (bg ? bg[e] : 0.f);
         }
+    }
+    // row norms: the 4 loader threads of a row (consecutive lanes) add their
+    // shares; x from the first expert tile's blocks, wg from the first token
+    // tile's
+    xsq += __shfl_xor(xsq, 1);
+    xsq += __shfl_xor(xsq, 2);
+    wsq += __shfl_xor(wsq, 1);
+    wsq += __shfl_xor(wsq, 2);
+    if ((tid & 3) == 0) {
+        if (xn2 && blockIdx.x == 0 && s0 + lrow < S) xn2[s0 + lrow] = xsq;
+        if (wn2 && blockIdx.y == 0 && j0 + lrow < E) wn2[j0 + lrow] = wsq;
     }
 }
 }  // namespace
@@ -151,6 +167,8 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
                                                                   const float* __restrict__ wg,
                                                                   const float* __restrict__ bg,
                                                                   float* __restrict__ logits,
+                                                                  float* __restrict__ xn2,
+                                                                  float* __restrict__ wn2,
                                                                   int S, int d, int E) {
     // stage: A [128][8 chunks], then three weight planes [64][8 chunks]
     constexpr int A_SZ = GM_BM * GM_CH, B_SZ = GM_BN * GM_CH, STAGE = A_SZ + 3 * B_SZ;
@@ -180,6 +198,13 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
     }
     u32x4_t rx[XI];
     f32x4_t rw[2];
+    // this thread's shares of the squared row norms (x rows tid/8 + 64 i,
+    // router row tid/8), added as the chunks are staged by the blocks that
+    // store them: x by the first expert tile, wg by the first token tile
+    const bool xnorm = xn2 && blockIdx.y == 0, wnorm = wn2 && blockIdx.x == 0;
+    float xsq[XI], wsq = 0.f;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) xsq[i] = 0.f;
     auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < XI; ++i) rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
@@ -189,7 +214,23 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
     auto sstore = [&](int buf) {
         u32x4_t* st = smem + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < XI; ++i) st[ald[i]] = rx[i];
+        for (int i = 0; i < XI; ++i) {
+            st[ald[i]] = rx[i];
+            if (xnorm) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = __uint_as_float(rx[i][q] << 16);
+                    const float hi = __uint_as_float(rx[i][q] & 0xffff0000u);
+                    xsq[i] = fmaf(lo, lo, fmaf(hi, hi, xsq[i]));
+                }
+            }
+        }
+        if (wnorm) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) wsq = fmaf(rw[q][u], rw[q][u], wsq);
+        }
         u32x4_t hi, lo1, lo2;
         split3(rw[0], rw[1], hi, lo1, lo2);
         st[bld] = hi;
@@ -225,6 +266,25 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
         if (kt + 1 < KT) sstore(buf ^ 1);
         __syncthreads();
     }
+    // row norms: the 8 loader threads of a row (consecutive lanes) add their
+    // shares; x from the first expert tile's blocks, wg from the first token
+    // tile's
+#pragma unroll
+    for (int m = 1; m < GM_CH; m <<= 1) {
+#pragma unroll
+        for (int i = 0; i < XI; ++i) xsq[i] += __shfl_xor(xsq[i], m);
+        wsq += __shfl_xor(wsq, m);
+    }
+    if ((tid & (GM_CH - 1)) == 0) {
+        if (xnorm) {
+#pragma unroll
+            for (int i = 0; i < XI; ++i) {
+                const int row = (tid + GM_NT * i) / GM_CH;
+                if (s0 + row < S) xn2[s0 + row] = xsq[i];
+            }
+        }
+        if (wnorm && j0 + tid / GM_CH < E) wn2[j0 + tid / GM_CH] = wsq;
+    }
     // 32x32 accumulator layout: lane l holds column l%32, register r row
     // 8*(r/4) + 4*(l/32) + r%4.
     const int j = j0 + wn * 32 + frow;
@@ -240,17 +300,18 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
 }  // namespace
 
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
-                              float* logits, int S, int d, int E, hipStream_t st) {
+                              float* logits, float* xn2, float* wn2, int S, int d, int E,
+                              hipStream_t st) {
     if (x_bf16 && d % GM_BK == 0) {
         dim3 grid((unsigned)ceil_div(S, GM_BM), (unsigned)ceil_div(E, GM_BN));
         gate_logits_mfma_kernel<<<grid, GM_NT, 0, st>>>(static_cast<const bf16_t*>(x), wg, bg,
-                                                        logits, S, d, E);
+                                                        logits, xn2, wn2, S, d, E);
     } else {
         dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
         if (x_bf16)
-            gate_logits_kernel<true><<<grid, 256, 0, st>>>(x, wg, bg, logits, S, d, E);
+            gate_logits_kernel<true><<<grid, 256, 0, st>>>(x, wg, bg, logits, xn2, wn2, S, d, E);
         else
-            gate_logits_kernel<false><<<grid, 256, 0, st>>>(x, wg, bg, logits, S, d, E);
+            gate_logits_kernel<false><<<grid, 256, 0, st>>>(x, wg, bg, logits, xn2, wn2, S, d, E);
     }
     return hipGetLastError();
 }
@@ -270,7 +331,8 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const
 // Refinement: the logit GEMM accumulates in fp32, so its values can differ
 // by a few ulps from exactly rounded dot products.  The ordered top-k depends
 // only on the comparisons between sorted neighbours r, r+1 for r < k.  When
-// such a pair differs by less than `tau` (well above the GEMM's error), the
+// such a pair differs by less than the token's margin tau (well above the
+// GEMM's error, and scaled with the token's magnitudes: margin_scale), the
 // chain of sorted neighbours linked by differences below tau is recomputed
 // with fp64 accumulation, rounded once to fp32 (the stored logits are
 // overwritten) and the selection is redone.  Experts outside the chain differ
@@ -381,13 +443,45 @@ __device__ __forceinline__ void apply_refined(float (&v)[EQ], float* lrow, const
     }
 }
 
+// Scale of the refinement margin, computed by every wave for itself (all 64
+// lanes active): wmax = max_j |wg[j,:]| and bmax = max_j |bg[j]|.  Token s
+// then refines a top-k decision closer than p.tau * (|x[s,:]| wmax + bmax/8).
+// By Cauchy-Schwarz |x_s . w_j| <= |x_s| |w_j|: the first term follows the
+// magnitude of the partial sums whose fp32 roundings make the logit GEMM's
+// error, whatever the scale of x and Wg; the second covers the single
+// rounding of the bias addition (a quarter ulp of the bias at p.tau = 32 ulp
+// of 1.0).
+struct MarginScale {
+    float wmax, bmax;
+};
+__device__ __forceinline__ MarginScale margin_scale(const RouteParams& p, int lane) {
+    MarginScale m{0.f, 0.f};
+    if (p.tau > 0.f) {
+        float w = 0.f, b = 0.f;
+        for (int j = lane; j < p.E; j += kWave) {
+            w = fmaxf(w, p.wn2[j]);
+            if (p.bg) b = fmaxf(b, fabsf(p.bg[j]));
+        }
+        m.wmax = sqrtf(wave_max_nonneg_f32(w));
+        m.bmax = wave_max_nonneg_f32(b);
+    }
+    return m;
+}
+__device__ __forceinline__ float token_margin(const RouteParams& p, const MarginScale& m, int s) {
+    return p.tau > 0.f ? p.tau * (sqrtf(p.xn2[s]) * m.wmax + 0.125f * m.bmax) : 0.f;
+}
+
 // Routes token s with the whole wave (lane l holds experts l, l+64, ...):
 // top-k with near-tie refinement, softmax, renormalised weights, outputs and
 // the histogram; adds the token's probabilities to pacc and lse^2 to zacc.
 // s_cand: kMaxSel ints of LDS private to this wave.
 template <int EQ>
-__device__ void route_token_wave(const RouteParams& p, int s, int lane, int* s_hist, int* s_cand,
-                                 float (&pacc)[EQ], float& zacc) {
+// lds_row: NULL (the logits are read from p.logits), or the token's raw
+// logits in LDS, which are read and then zeroed; tau_in: the token's margin
+// when already known (>= 0), else computed here.
+__device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, int s, int lane,
+                                 int* s_hist, int* s_cand, float (&pacc)[EQ], float& zacc,
+                                 float* lds_row, float tau_in) {
     const int E = p.E, k = p.k;
     const int nsel = k + 1 <= E ? k + 1 : E;
     float* lrow = p.logits + (size_t)s * E;
@@ -395,7 +489,8 @@ __device__ void route_token_wave(const RouteParams& p, int s, int lane, int* s_h
 #pragma unroll
     for (int q = 0; q < EQ; ++q) {
         const int j = lane + kWave * q;
-        v[q] = j < E ? lrow[j] : 0.f;
+        v[q] = j < E ? (lds_row ? lds_row[j] : lrow[j]) : 0.f;
+        if (lds_row && j < E) lds_row[j] = 0.f;
     }
     // top[r]: key of the r-th largest logit (wave-uniform)
     uint64_t top[kMaxSel];
@@ -404,34 +499,35 @@ __device__ void route_token_wave(const RouteParams& p, int s, int lane, int* s_h
     for (int r = 0; r < kMaxK + 1; ++r)
         if (r < nsel) top[r] = select_next<EQ>(v, E, lane, taken);
 
-    if (p.tau > 0.f && nsel > 1) {
+    const float tau = tau_in >= 0.f ? tau_in : token_margin(p, ms, s);
+    if (tau > 0.f && nsel > 1) {
         // Pair r joins sorted positions r and r+1 and is "close" when their
         // difference is below tau.  Pairs r < k decide the ordered top-k.
         bool need = false;
 #pragma unroll
         for (int r = 0; r < kMaxK; ++r)
             if (r < k && r + 1 < nsel)
-                need |= key_value(top[r]) - key_value(top[r + 1]) < p.tau;
+                need |= key_value(top[r]) - key_value(top[r + 1]) < tau;
         if (need) {
             // follow a chain of close pairs past position k
             int n = nsel;
 #pragma unroll
             for (int r = 2; r < kMaxSel; ++r) {
-                if (r == n && n < E && key_value(top[r - 2]) - key_value(top[r - 1]) < p.tau) {
+                if (r == n && n < E && key_value(top[r - 2]) - key_value(top[r - 1]) < tau) {
                     top[r] = select_next<EQ>(v, E, lane, taken);
                     ++n;
                 }
             }
             const bool overflow =
                 n == kMaxSel && n < E &&
-                key_value(top[kMaxSel - 2]) - key_value(top[kMaxSel - 1]) < p.tau;
+                key_value(top[kMaxSel - 2]) - key_value(top[kMaxSel - 1]) < tau;
             int ncand = 0;
             if (!overflow) {
                 // members of the close chains that contain a pair r < k
                 uint32_t closebits = 0;
 #pragma unroll
                 for (int r = 0; r + 1 < kMaxSel; ++r)
-                    if (r + 1 < n && key_value(top[r]) - key_value(top[r + 1]) < p.tau)
+                    if (r + 1 < n && key_value(top[r]) - key_value(top[r + 1]) < tau)
                         closebits |= 1u << r;
                 uint32_t members = 0;
                 int r = 0;
@@ -515,6 +611,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int b = blockIdx.x;
+    const MarginScale ms = margin_scale(p, lane);
     for (int i = tid; i < k * E; i += blockDim.x) s_hist[i] = 0;
     __syncthreads();
 
@@ -526,7 +623,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
     for (int t = 0; t < kTokBlock / NW; ++t) {
         const int s = b * kTokBlock + wave * (kTokBlock / NW) + t;
         if (s >= p.S) break;
-        route_token_wave<EQ>(p, s, lane, s_hist, s_cand[wave], pacc, zacc);
+        route_token_wave<EQ>(p, ms, s, lane, s_hist, s_cand[wave], pacc, zacc, nullptr, -1.f);
     }
 
     // deterministic block reduction of the probability and lse^2 partials
@@ -575,7 +672,7 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
     int* s_hist = reinterpret_cast<int*>(smem);                  // [k][E]
     float* s_pt = reinterpret_cast<float*>(s_hist + k * E);      // [64][EP] probabilities
     float* s_slow = s_pt + kTokBlock * EP;                       // [L][E] slow-path sums
-    __shared__ float s_lse2[kTokBlock], s_z[L];
+    __shared__ float s_lse2[kTokBlock], s_z[L], s_tau[kTokBlock];
     __shared__ int s_flag[kTokBlock], s_list[kTokBlock], s_nlist;
     __shared__ int s_cand[L][kMaxSel];
 
@@ -584,9 +681,8 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
     const int b = blockIdx.x;
     const int s = b * kTokBlock + t;
     const bool live = s < p.S;
-    for (int i = tid; i < k * E; i += NT) s_hist[i] = 0;
-
-    // this lane's logits (16-byte loads when every row is 16-byte aligned)
+    // this lane's logits (16-byte loads when every row is 16-byte aligned),
+    // issued first so that their latency covers the set-up below
     float v[32];
     const float* lrow = p.logits + (size_t)(live ? s : 0) * E;
     const bool vec = (E & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
@@ -602,6 +698,8 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
             for (int u = 0; u < 4; ++u) v[4 * i + u] = live && j0 + u < E ? lrow[j0 + u] : 0.f;
         }
     }
+    const MarginScale ms = margin_scale(p, lane);
+    for (int i = tid; i < k * E; i += NT) s_hist[i] = 0;
     // Local top-K1.  Experts are visited in decreasing index order, so a new
     // entry has a lower index than every listed one and an entry carried down
     // sorted above its neighbours: ">=" on the key alone orders by (key
@@ -668,12 +766,25 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
         return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
     };
     bool flag = false;
-    if (p.tau > 0.f && nsel > 1) {
+    const float tau = live ? token_margin(p, ms, s) : 0.f;
+    if (tau > 0.f && nsel > 1) {
 #pragma unroll
         for (int r = 0; r + 1 < K1; ++r)
-            if (r < k && r + 1 < nsel) flag |= kval(gk[r]) - kval(gk[r + 1]) < p.tau;
+            if (r < k && r + 1 < nsel) flag |= kval(gk[r]) - kval(gk[r + 1]) < tau;
     }
     const bool fast = live && !flag;
+    // a flagged token's raw logits and margin go to LDS for the wave router
+    // (its probability row is written there only by that router, as zeros)
+    if (live && flag) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = 4 * (l + L * i) + u;
+                if (j < E) s_pt[t * EP + j] = v[4 * i + u];
+            }
+    }
+    if (l == 0) s_tau[t] = tau;
 
     // softmax over the token's E logits, stabilised by the largest
     // (__expf: the hardware exp2 of x*log2(e), within ~2e-6 relative here)
@@ -696,7 +807,7 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = 4 * (l + L * i) + u;
-            if (j < E) s_pt[t * EP + j] = fast ? v[4 * i + u] * inv : 0.f;
+            if (j < E && !(live && flag)) s_pt[t * EP + j] = fast ? v[4 * i + u] * inv : 0.f;
         }
     if (l == 0) {
         const float lse = m + logf(part);
@@ -733,7 +844,8 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
     float zacc = 0.f;
     const int nl = s_nlist;
     for (int f = wave; f < nl; f += L)
-        route_token_wave<EQ>(p, b * kTokBlock + s_list[f], lane, s_hist, s_cand[wave], pacc, zacc);
+        route_token_wave<EQ>(p, ms, b * kTokBlock + s_list[f], lane, s_hist, s_cand[wave], pacc,
+                             zacc, s_pt + s_list[f] * EP, s_tau[s_list[f]]);
 #pragma unroll
     for (int q = 0; q < EQ; ++q) {
         const int j = lane + 64 * q;

@@ -48,9 +48,9 @@
 //   its blocks take that chunk's tiles in order from an atomic counter, so
 //   the blocks of one XCD work on neighbouring tiles (sharing A and B tiles
 //   through L2) at the same time and tiles of unequal cost balance out.
-//   On random bf16 data this kernel is power-bound: the shader clock settles
-//   near 1.4 GHz (2.2 GHz on constant data), so data moved per MFMA, not
-//   issue slots, sets the rate.
+//   The shader clock falls with the matrix work: about 1.7 GHz while the
+//   large (MFMA-bound) shapes run, 2.1 GHz at the weight-streaming ones, so
+//   data moved per MFMA, not issue slots alone, sets the rate.
 #include "common.h"
 #include "kernels.h"
 

@@ -8,9 +8,12 @@
 namespace moe {
 
 // ------------------------------------------------------------------ gate
-// logits[s,j] = sum_i x[s,i] * wg[j,i] + bg[j]   (fp32 accumulation)
+// logits[s,j] = sum_i x[s,i] * wg[j,i] + bg[j]   (fp32 accumulation); also
+// the squared row norms xn2[s] = |x[s,:]|^2 and wn2[j] = |wg[j,:]|^2, the
+// scale of the router's refinement margin.
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
-                              float* logits, int S, int d, int E, hipStream_t st);
+                              float* logits, float* xn2, float* wn2, int S, int d, int E,
+                              hipStream_t st);
 
 struct RouteParams {
     float* logits;          // [S,E]; refined entries are written back
@@ -19,7 +22,9 @@ struct RouteParams {
     const float* wg;
     const float* bg;
     int S, d, E, k, nb;     // nb = ceil(S / kTokBlock)
-    float tau;              // refinement margin; 0 disables refinement
+    float tau;              // margin per unit of logit scale; 0 disables refinement
+    const float* xn2;       // [S] squared norms of the token rows (with tau > 0)
+    const float* wn2;       // [E] squared norms of the router rows (with tau > 0)
     int32_t* topk_idx;      // [S,k]
     float* topk_w;          // [S,k]
     int32_t* hist;          // [E][k*nb] per-(rank, token block) expert counts

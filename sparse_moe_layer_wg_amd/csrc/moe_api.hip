@@ -107,7 +107,7 @@ constexpr int kTileCounters = 16;
 // with R = rows: E*C padded, S*k compact (dropless).
 struct Carve {
     size_t logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ, mt_start, seg, ctr,
-        inv, offer_e, offer_r, rhist;
+        inv, xn2, wn2, offer_e, offer_r, rhist;
     size_t route_end, H, ffn_end, xo, end;
 };
 
@@ -136,6 +136,8 @@ Carve carve(const Plan& p) {
     c.seg = take((size_t)p.E * 4);
     c.ctr = take(kTileCounters * 4);
     c.inv = take(p.rows * 4);
+    c.xn2 = take((size_t)p.S * 4);
+    c.wn2 = take((size_t)p.E * 4);
     if (p.reroute) {
         c.offer_e = take((size_t)p.S * p.k * 4);
         c.offer_r = take((size_t)p.S * p.k * 4);
@@ -154,9 +156,11 @@ T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Router margin below which a top-k decision is re-evaluated in fp64: 32
-// ulps of 1.0 scaled by sqrt(d), the growth of fp32 accumulation error.
-float refine_tau(int d) { return (float)(ldexp(32.0, -24) * sqrt((double)d)); }
+// Router margin per unit of logit scale: a top-k decision closer than
+// 32 * 2^-24 * (|x_s| max_j |w_j| + max_j |b_j| / 8) is re-evaluated in fp64.
+// For unit-scale rows (|x_s| about sqrt(d), |w_j| about 1) that is 32 ulps
+// of 1.0 times sqrt(d), the growth of fp32 accumulation error over d terms.
+constexpr float kRefineTau = 32.0f / 16777216.0f;
 
 #define MOE_TRY(call)                                  \
     do {                                               \
@@ -180,8 +184,10 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     double* psum = at<double>(ws, cv.psum);
     int32_t* occ = at<int32_t>(ws, cv.occ);
     int32_t* mt = at<int32_t>(ws, cv.mt_start);
+    float* xn2 = at<float>(ws, cv.xn2);
+    float* wn2 = at<float>(ws, cv.wn2);
     if (!logits_in)
-        MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, p.S, p.d, p.E, st));
+        MOE_TRY(launch_gate_logits(x, p.bf16, wg, bg, logits, xn2, wn2, p.S, p.d, p.E, st));
     record(ev, 1, st);
     RouteParams rp{};
     rp.logits = logits;
@@ -194,7 +200,9 @@ moe_status run_gate(const Plan& p, const Carve& cv, const void* x, const float* 
     rp.E = p.E;
     rp.k = p.k;
     rp.nb = p.nb;
-    rp.tau = logits_in ? 0.f : refine_tau(p.d);
+    rp.tau = logits_in ? 0.f : kRefineTau;
+    rp.xn2 = xn2;
+    rp.wn2 = wn2;
     rp.topk_idx = topk_idx;
     rp.topk_w = topk_w;
     rp.hist = hist;

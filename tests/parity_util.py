@@ -80,6 +80,17 @@ def expert_ffn_chunked(xd, occ, w1, b1, w2, b2, chunk_flop: float = 1.5e12) -> n
     return out
 
 
+def router_margin(x, wg, bg) -> np.ndarray:
+    """Per-token refinement margin of the router, as the library defines it:
+    tau_s = 32 * 2^-24 * (|x_s| * max_j |wg_j| + max_j |bg_j| / 8)."""
+    x = np.asarray(x)
+    x64 = ((x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x)
+    x64 = x64.astype(np.float64)
+    wmax = np.sqrt((np.asarray(wg, np.float64) ** 2).sum(axis=1).max())
+    bmax = 0.0 if bg is None else float(np.abs(np.asarray(bg, np.float64)).max())
+    return 32.0 * 2.0 ** -24 * (np.sqrt((x64 ** 2).sum(axis=1)) * wmax + bmax / 8.0)
+
+
 def as_f64(t) -> np.ndarray:
     """Device/host tensor (fp32 or bf16) as a float64 numpy array."""
     return t.detach().to("cpu", torch.float64).numpy() if isinstance(t, torch.Tensor) \
@@ -188,12 +199,16 @@ def _check_routing_outputs(w, inputs, layer, r, rep):
     assert abs(losses[1] - r["z"]) <= LOSS_TOL * abs(r["z"]), (losses[1], r["z"])
     lg = layer.logits.cpu().numpy()
     lg_or = oracle.logits(host["x"], host["wg"], host["bg"])
-    rep["logit_max_abs_err"] = float(np.abs(lg.astype(np.float64) - lg_or).max())
-    # The router re-evaluates in fp64 every top-k decision closer than
-    # tau = 32 * sqrt(d) * 2^-24; that is exact only while the logit error
-    # stays well below tau / 2.
-    tau = 32.0 * np.sqrt(w.d) * 2.0 ** -24
-    rep["logit_err_over_tau"] = rep["logit_max_abs_err"] / tau
+    err = np.abs(lg.astype(np.float64) - lg_or)
+    rep["logit_max_abs_err"] = float(err.max()) if err.size else 0.0
+    # The router re-evaluates in fp64 every top-k decision of token s closer
+    # than its margin tau_s; that is exact only while the logit error stays
+    # well below tau_s / 2.
+    tau = router_margin(host["x"], host["wg"], host["bg"])
+    # (a zero margin means exact logits: an all-zero router and no bias)
+    emax = err.max(axis=1) if err.size else np.zeros(0)
+    ratio = np.where(tau > 0, emax / np.where(tau > 0, tau, 1.0), np.where(emax == 0, 0.0, np.inf))
+    rep["logit_err_over_tau"] = float(ratio.max()) if ratio.size else 0.0
     assert rep["logit_err_over_tau"] < 0.25, rep
     r_or = oracle.route(lg_or, w.k, layer.C, w.reroute)
     agree = np.all(layer.topk_idx.cpu().numpy() == r_or["serve"], axis=1)

@@ -279,6 +279,33 @@ def test_duplicated_router_rows_exact_ties():
         assert np.all(idx[pair, r] < idx[pair, r + 1])
 
 
+@pytest.mark.parametrize("scale", [1.0, 100.0])
+def test_near_tie_pairs_exact_at_any_input_scale(scale):
+    """Router rows in nearly tied pairs (row 2i+1 = row 2i + 7e-8 * N(0,1)
+    noise, so a token's two best experts are usually a pair whose logits
+    differ by about 7e-8 |x_s|) and x scaled by `scale`.  At scale 100 those
+    differences (about 1.6e-4) are as small as the fp32 GEMM's error there;
+    the refinement margin grows with |x_s| and max_j |w_j|, so every such
+    decision is re-evaluated in fp64 and the ordered top-k equals the
+    oracle's from its own logits for every token."""
+    w = mw.Workload("near_pairs", S=4000, d=512, h=128, E=64, k=2, capacity_factor=1.0,
+                    dtype="bf16", seed=33)
+    inputs = mw.generate(w, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(34)
+    base = inputs["wg"][0::2]
+    twin = base + 7e-8 * torch.randn(base.shape, generator=g, device="cuda")
+    inputs["wg"] = torch.stack([base, twin], dim=1).reshape(w.E, w.d).contiguous()
+    inputs["x"] = (inputs["x"].float() * scale).to(torch.bfloat16)
+    inputs, layer = run_layer(w, inputs, dispatch_buffer=False)
+    rep = check_layer(w, inputs, layer, full=True)
+    _print(f"near_pairs_x{scale:g}", rep)
+    assert rep["topk_mismatches"] == 0, rep
+    idx = layer.topk_idx.cpu().numpy()
+    rep_pairs = float(np.mean(idx[:, 0] // 2 == idx[:, 1] // 2))
+    print(f"  tokens whose top-2 is a tied pair: {rep_pairs:.3f}", flush=True)
+    assert rep_pairs > 0.5
+
+
 @pytest.mark.parametrize("E,k", [(8, 2), (64, 2), (40, 8)])
 def test_zero_router_closed_form(E, k):
     """All-zero router weight: every logit is 0, so the top-k is (0..k-1) with
