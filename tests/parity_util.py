@@ -218,6 +218,49 @@ def _check_routing_outputs(w, inputs, layer, r, rep):
     return host
 
 
+def dropless_whole(w, host, layer, r, rows, rep, tol):
+    """Every compact expert-output row and every row of y of a dropless run
+    against the oracle, without the oracle's [E, S, d] buffers (too large at
+    full size): each group of experts' rows go through oracle.expert_ffn as
+    compact [n_e, d] blocks, and y is the routing weights' sum of those rows
+    (the combine step's definition)."""
+    import time
+    S, k, E, d = w.S, w.k, w.E, w.d
+    n = np.bincount(r["idx"].reshape(-1), minlength=E)
+    seg = np.concatenate([[0], np.cumsum(n)[:-1]])
+    x = host["x"]
+    out_or = np.zeros((S * k, d), np.float64)
+    tok_of_row = np.empty(S * k, np.int64)
+    tok_of_row[rows.reshape(-1)] = np.repeat(np.arange(S), k)
+    t0 = time.perf_counter()
+    e0 = 0
+    while e0 < E:
+        e1, fl = e0, 0.0
+        while e1 < E and (e1 == e0 or fl + 4.0 * d * w.h * n[e1] <= 1.5e12):
+            fl += 4.0 * d * w.h * n[e1]
+            e1 += 1
+        m = int(n[e0:e1].max()) if e1 > e0 else 0
+        if m > 0:
+            xd = np.zeros((e1 - e0, m, d), x.dtype)
+            for e in range(e0, e1):
+                xd[e - e0, :n[e]] = x[tok_of_row[seg[e]:seg[e] + n[e]]]
+            o = oracle.expert_ffn(xd, n[e0:e1].astype(np.int32), host["w1"][e0:e1],
+                                  None if host["b1"] is None else host["b1"][e0:e1],
+                                  host["w2"][e0:e1],
+                                  None if host["b2"] is None else host["b2"][e0:e1])
+            for e in range(e0, e1):
+                out_or[seg[e]:seg[e] + n[e]] = o[e - e0, :n[e]]
+        print(f"  oracle experts {e0}..{e1 - 1} of {E}: {time.perf_counter() - t0:.1f} s",
+              flush=True)
+        e0 = e1
+    check_rows(rep, "out", as_f64(layer.out), out_or, tol)
+    y_or = np.zeros((S, d), np.float64)
+    for rr in range(k):
+        y_or += r["w"][:, rr:rr + 1].astype(np.float64) * out_or[rows[:, rr]]
+    check_rows(rep, "y", as_f64(layer.y), y_or, tol)
+    return rep
+
+
 def _check_dropless(w, inputs, layer, r, full, n_sample, seed, rep):
     """Dropless run: every assignment kept; compact [S*k,d] buffers."""
     tol = TOL[w.dtype]
@@ -225,6 +268,9 @@ def _check_dropless(w, inputs, layer, r, full, n_sample, seed, rep):
     rep["drops"] = 0
     rows = oracle.compact_rows(r["idx"], w.E)
     y_gpu = as_f64(layer.y)
+    # the oracle's padded [E, S, d] fp64 buffers above 2 GiB: compact blocks
+    if full and 8 * w.S * w.E * w.d > (1 << 31):
+        return dropless_whole(w, host, layer, r, rows, rep, tol)
     if full:
         res = oracle.layer_dropless(host["x"], host["wg"], host["bg"], host["w1"], host["b1"],
                                     host["w2"], host["b2"], w.k, lg=layer.logits.cpu().numpy())

@@ -124,30 +124,26 @@ def _block_rel_max(a, b, bm=256, bn=256):
     return worst
 
 
-@pytest.mark.timeout(600)
-def test_backward_many_tiles_whole():
-    """A backward with many more tiles than compute units (the forward GEMMs
-    512 tiles each, the weight gradients 1024): every gradient against the
-    oracle, each row of dx and each 256 x 256 output tile of dW1 and dW2 on
-    its own as well as the whole tensors."""
-    from test_gpu_parity import MANY_TILES as w
-    print(f"\n[bwd many tiles] {w}", flush=True)
-    inputs = _with_biases(w, mw.generate(w, "cuda"), w.seed + 100)
-    inputs, layer = run_layer(w, inputs, dispatch_buffer=False)
-    g = torch.Generator(device="cuda").manual_seed(w.seed + 200)
-    dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
-    grads = run_backward(w, inputs, layer, dy, g_aux=0.7, g_z=0.3)
+def _whole_backward(w, inputs, layer, grads, dy, g_aux, g_z):
+    """Every gradient against the oracle's: each whole tensor within the bar,
+    each row of dx, db1, db2 and each 256 x 256 output tile of dW1 and dW2
+    within 3x the bar (dx rows above it must be explained by a ReLU kink)."""
+    import time
     host = {n: mw.to_numpy(t) for n, t in inputs.items()}
+    t0 = time.perf_counter()
     ref = oracle.layer_backward(host["x"], host["wg"], host["w1"], host["b1"], host["w2"],
                                 host["b2"], w.k, layer.C, layer.logits.cpu().numpy(),
-                                mw.to_numpy(dy), 0.7, 0.3)
-    rep = {key: rel_fro(as_f64(grads[key]), ref[key])
-           for key in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2")}
+                                mw.to_numpy(dy), g_aux, g_z)
+    rep = {"oracle_s": time.perf_counter() - t0}
+    for key in ("dx", "dwg", "dbg", "dw1", "db1", "dw2", "db2"):
+        if grads[key] is not None:
+            rep[key] = rel_fro(as_f64(grads[key]), ref[key])
     rows = row_rel(as_f64(grads["dx"]), ref["dx"])
     rep["dw1_tile_max"] = _block_rel_max(as_f64(grads["dw1"]), ref["dw1"])
     rep["dw2_tile_max"] = _block_rel_max(as_f64(grads["dw2"]), ref["dw2"])
-    rep["db1_row_max"] = float(row_rel(as_f64(grads["db1"]), ref["db1"]).max())
-    rep["db2_row_max"] = float(row_rel(as_f64(grads["db2"]), ref["db2"]).max())
+    for key in ("db1", "db2"):
+        if grads[key] is not None:
+            rep[key + "_row_max"] = float(row_rel(as_f64(grads[key]), ref[key]).max())
     # dx rows: a hidden pre-activation within fp32 rounding of zero can land
     # on the other side of the ReLU in the GPU's fp32 accumulation than in
     # the oracle's fp64, and that unit's whole W1 row then enters dx or not
@@ -165,8 +161,41 @@ def test_backward_many_tiles_whole():
     rep["dx_row_max_else"] = float(np.delete(rows, over).max())
     _print(w.name + "_bwd", rep)
     for key, err in rep.items():
-        if key != "dx_rows_over_bar":
+        if key not in ("dx_rows_over_bar", "oracle_s"):
             assert err <= (3 * TOL if key.endswith(("_max", "_else")) else TOL), (key, rep)
+    return rep
+
+
+@pytest.mark.timeout(600)
+def test_backward_many_tiles_whole():
+    """A backward with many more tiles than compute units (the forward GEMMs
+    512 tiles each, the weight gradients 1024): every gradient against the
+    oracle, each row of dx and each 256 x 256 output tile of dW1 and dW2 on
+    its own as well as the whole tensors."""
+    from test_gpu_parity import MANY_TILES as w
+    print(f"\n[bwd many tiles] {w}", flush=True)
+    inputs = _with_biases(w, mw.generate(w, "cuda"), w.seed + 100)
+    inputs, layer = run_layer(w, inputs, dispatch_buffer=False)
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 200)
+    dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    grads = run_backward(w, inputs, layer, dy, g_aux=0.7, g_z=0.3)
+    _whole_backward(w, inputs, layer, grads, dy, 0.7, 0.3)
+
+
+@pytest.mark.timeout(900)
+def test_backward_balanced_full_size_whole():
+    """The balanced full-size workload in the training benchmark's
+    configuration (fused gather, the benchmark's loss weights): every
+    gradient against the oracle, whole and row by row / tile by tile."""
+    w = mw.get("balanced_bf16")
+    print(f"\n[bwd full whole] {w}", flush=True)
+    inputs, layer = run_layer(w, dispatch_buffer=False)
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    dy = torch.randn((w.S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    grads = run_backward(w, inputs, layer, dy, 0.01, 0.001)
+    _whole_backward(w, inputs, layer, grads, dy, 0.01, 0.001)
+    del layer, inputs, grads
+    torch.cuda.empty_cache()
 
 
 def _near_kink(host, idx_s, slot_s, s, rel=1e-5):
@@ -264,8 +293,7 @@ def test_backward_empty_input():
         assert not torch.any(t != 0), key
 
 
-@pytest.mark.parametrize("name,ntok,reroute", [("balanced_bf16", 24, False),
-                                               ("deepseek_bf16", 6, False),
+@pytest.mark.parametrize("name,ntok,reroute", [("deepseek_bf16", 6, False),
                                                ("skewed_bf16", 16, True)])
 def test_backward_full_size_sampled(name, ntok, reroute):
     """Full-size workloads in the training benchmark's configuration (fused

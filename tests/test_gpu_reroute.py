@@ -167,13 +167,14 @@ def test_reroute_backward_full_parity(w):
     check_backward(w, inputs, layer, grads, dy, 0.7, 0.3)
 
 
-def test_reroute_full_size_sampled():
+def test_reroute_full_size_whole():
     """The skewed full-size workload with re-routing, in the benchmark's
-    launch configuration: routing and rows exact, y on sampled tokens."""
+    launch configuration: routing and rows exact, every filled expert-output
+    row and every row of y against the oracle, each row on its own."""
     w = mw.get("skewed_bf16").with_(reroute=True, name="skewed_bf16_reroute")
     print(f"\n[rr full] {w}", flush=True)
     inputs, layer = run_layer(w, dispatch_buffer=False)
-    rep = check_layer(w, inputs, layer, full=False)
+    rep = check_layer(w, inputs, layer, full=True)
     _print(w.name, rep)
     assert rep["rerouted"] > 0
     del layer, inputs
