@@ -134,8 +134,10 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 // v_mfma_f32_32x32x16_bf16 accumulates x . hi in one accumulator and the two
 // small terms in another, which are added (with the bias) at the end.
 // Block tile 128 tokens x 64 experts x 64 k, 8 waves (4 x 2) of 32 x 32; the
-// taller tile reads each weight-plane tile once for 128 tokens, which halves
-// the plane traffic from L2 per MFMA (the kernel is bound by that traffic).
+// taller tile reads each weight tile once for 128 tokens, half the weight
+// traffic from L2 per MFMA of a 64-token tile (measured faster at every
+// shape; no single unit is saturated: matrix pipes busy a quarter to a third
+// of the time, the texture path a quarter, L2 hit rate 70-80%).
 // Operands are staged through registers into two LDS buffers (x and the
 // three weight planes, XOR-swizzled by row); the fp32 weights are read once
 // per block, 32 bytes per thread per k-tile.  Rows past S or E load a

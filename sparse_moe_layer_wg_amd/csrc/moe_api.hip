@@ -100,8 +100,9 @@ constexpr int kTileCounters = 16;
 // Workspace layout, every region 256-byte aligned:
 //   [route]  logits, idx, w, slot, counts, losses, hist, ppart, zpart, psum, occ,
 //            mt_start + m-tile experts, expert segment starts [E], GEMM tile
-//            counters, inverse slot map [R], router weight split into three
-//            bf16 planes [3,E,d] (bf16 x)
+//            counters, inverse slot map [R], squared row norms of x [S] and
+//            of the router weight [E]; with re-routing also the overflow
+//            offers [S,k] x 2 and their tile histograms [E,k,nb]
 //   [ffn]    H [R,h]
 //   [layer]  one [R,d] buffer (dispatch buffer and expert output)
 // with R = rows: E*C padded, S*k compact (dropless).
