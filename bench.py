@@ -327,8 +327,16 @@ def main():
             stage_frac[n] = "fused into expert_gemm1"
             continue
         ts = gemm_us.get(n, stage_us[n]) * 1e-6
+        # the stage's roofline time: its algorithmic bytes at the HBM peak or
+        # its matrix work at the MFMA peak, whichever is longer (the bf16
+        # router runs three MFMAs per product for its exact weight split)
+        mf = work[n]["flops"] * (3 if n == "gate_logits" and w.dtype == "bf16" else 1)
+        t_b = work[n]["bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_f = mf / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
         stage_frac[n] = {"GB_s": work[n]["bytes"] / ts / 1e9,
-                         "TFLOP_s": work[n]["flops"] / ts / 1e12}
+                         "TFLOP_s": work[n]["flops"] / ts / 1e12,
+                         "bound": "hbm" if t_b >= t_f else "mfma",
+                         "roofline_frac": max(t_b, t_f) / ts}
 
     out = {
         "metric": METRIC,

@@ -24,8 +24,7 @@ namespace moe {
 namespace {
 constexpr int GL_BM = 64, GL_BN = 64, GL_BK = 32;
 
-template <bool XBF16>
-__global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict__ xv,
+__global__ __launch_bounds__(256) void gate_logits_kernel(const float* __restrict__ x,
                                                           const float* __restrict__ wg,
                                                           const float* __restrict__ bg,
                                                           float* __restrict__ logits,
@@ -54,24 +53,9 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 #pragma unroll
         for (int q = 0; q < 8; ++q) av[q] = 0.f, bv[q] = 0.f;
         if (gs < S) {
-            if (XBF16) {
-                const bf16_t* xr = static_cast<const bf16_t*>(xv) + (size_t)gs * d;
-                if (k0 + lk + 8 <= d) {
-                    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(xr + k0 + lk);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        av[2 * q] = __uint_as_float(raw[q] << 16);
-                        av[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
-                    }
-                } else {
-                    for (int q = 0; q < 8; ++q)
-                        if (k0 + lk + q < d) av[q] = bf16_to_f32(xr[k0 + lk + q]);
-                }
-            } else {
-                const float* xr = static_cast<const float*>(xv) + (size_t)gs * d;
-                for (int q = 0; q < 8; ++q)
-                    if (k0 + lk + q < d) av[q] = xr[k0 + lk + q];
-            }
+            const float* xr = x + (size_t)gs * d;
+            for (int q = 0; q < 8; ++q)
+                if (k0 + lk + q < d) av[q] = xr[k0 + lk + q];
         }
         if (gj < E) {
             const float* wr = wg + (size_t)gj * d;
@@ -304,16 +288,16 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* wg, const float* bg,
                               float* logits, float* xn2, float* wn2, int S, int d, int E,
                               hipStream_t st) {
-    if (x_bf16 && d % GM_BK == 0) {
+    if (x_bf16) {
+        // bf16 layers have d a multiple of 64 (checked when the layer is planned)
+        if (d % GM_BK != 0) return hipErrorInvalidValue;
         dim3 grid((unsigned)ceil_div(S, GM_BM), (unsigned)ceil_div(E, GM_BN));
         gate_logits_mfma_kernel<<<grid, GM_NT, 0, st>>>(static_cast<const bf16_t*>(x), wg, bg,
                                                         logits, xn2, wn2, S, d, E);
     } else {
         dim3 grid((unsigned)ceil_div(E, GL_BN), (unsigned)ceil_div(S, GL_BM));
-        if (x_bf16)
-            gate_logits_kernel<true><<<grid, 256, 0, st>>>(x, wg, bg, logits, xn2, wn2, S, d, E);
-        else
-            gate_logits_kernel<false><<<grid, 256, 0, st>>>(x, wg, bg, logits, xn2, wn2, S, d, E);
+        gate_logits_kernel<<<grid, 256, 0, st>>>(static_cast<const float*>(x), wg, bg, logits,
+                                                 xn2, wn2, S, d, E);
     }
     return hipGetLastError();
 }
