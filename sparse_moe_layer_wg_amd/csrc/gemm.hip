@@ -14,17 +14,18 @@
 //   Block tile BM x 256 x 64.  BM = 256: 512 threads = 8 waves in a 2 x 4
 //   grid, 128 x 64 per wave (two waves per SIMD, 128 fp32 accumulators per
 //   lane); BM = 128 (experts with few rows): 4 waves of 64 x 128.
-//   Operands are staged through registers into two LDS buffers: the global
-//   loads of k-tile t+1 are spread over the MFMAs of the first 16-wide step
-//   of tile t and their LDS stores over the MFMAs of the last step, and the
-//   fragments of the next step are read from LDS while the current MFMAs run
-//   (instruction groups placed with sched_group_barrier; a wave issues in
-//   order, so bursts of memory instructions would stall its MFMAs).  Plain
-//   vector loads are used rather than global->LDS copies: on gfx950 the copy
-//   path moves about 16 bytes per clock per CU, a quarter of the load path.
-//   LDS rows are padded to 144 bytes: the 16 rows a fragment read touches at
-//   one 16-byte column fall on distinct bank groups, and every fragment
-//   read or store is one base register plus an immediate offset.
+//   Operands go from global memory straight into two LDS buffers
+//   (global_load_lds_dwordx4, 1 KB = 8 rows per wave instruction): the
+//   copies of k-tile t+1 are issued at the start of k-tile t and waited for at
+//   its closing barrier, so no registers stage them and no LDS stores are
+//   issued; the fragments of the next step are read from LDS while the
+//   current MFMAs run (spread with sched_group_barrier).  Measured from L2,
+//   the copies move as many bytes per clock as loads into registers, and
+//   against that register-staged loop (padded LDS rows) this runs the
+//   expert GEMMs 2-7% faster with the same results bit for bit.  LDS rows
+//   are 128 bytes with their 16-byte chunks XOR-swizzled by row, so the 16
+//   rows a fragment read touches at one chunk fall on distinct bank
+//   groups.
 //   Rows past an expert's occupancy (and columns past N) load a clamped
 //   valid row; their results are never stored.
 //   An expert's last 256-row m-tile may hold up to 32 more rows (a strip):
@@ -49,8 +50,7 @@
 //   the blocks of one XCD work on neighbouring tiles (sharing A and B tiles
 //   through L2) at the same time and tiles of unequal cost balance out.
 //   The shader clock falls with the matrix work: about 1.7 GHz while the
-//   large (MFMA-bound) shapes run, 2.1 GHz at the weight-streaming ones, so
-//   data moved per MFMA, not issue slots alone, sets the rate.
+//   large (MFMA-bound) shapes run, 2.2 GHz at the weight-streaming ones.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,25 +65,25 @@ namespace {
 template <int BM, int BN, int WNC, bool RELU>
 __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NTH = 128 * WNC;             // threads per block
-    constexpr int BK = 64, CH = BK / 8;        // k-tile; 16-byte chunks per row
-    constexpr int RS = BK * 2 + 16;            // LDS row stride in bytes (padded)
+    constexpr int NW = NTH / 64;               // waves
+    constexpr int BK = 64;                     // k-tile
+    constexpr int RB = BK * 2;                 // LDS row: 128 bytes, 8 swizzled chunks
     constexpr int WM = BM / 2, WNT = BN / WNC; // wave tile
     constexpr int TM = WM / 32, TN = WNT / 32; // 32x32 MFMA tiles per wave
     constexpr int KS = BK / 16;                // MFMA k steps per k-tile
-    constexpr int A_CH = BM * CH / NTH;        // A chunks per thread per k-tile
-    constexpr int B_CH = BN * CH / NTH;        // B chunks per thread per k-tile
-    constexpr int RPI = NTH / CH;              // rows per loader pass
     // An expert's last m-tile may carry SR more rows (the strip): each wave
     // multiplies them into SB extra 32x32 blocks, with B fragments it holds.
     constexpr int SR = BM == 256 ? kStripRows : 0;
-    constexpr int SB = BN / 32 / (NTH / 64);   // strip blocks per wave
-    constexpr int SP = SR * BK * 2 / NTH;      // strip bytes per thread (8 or 16)
-    constexpr int BOFF = (BM + SR) * RS;       // byte offset of B in a stage
-    constexpr int STAGE = BOFF + BN * RS;      // bytes per LDS buffer
-    static_assert(SR == 0 || ((SP == 8 || SP == 16) && SB * 2 == TN),
-                  "strip: 8 or 16 bytes per thread; a wave row's share of the B fragments");
-    using strip_t = std::conditional_t<SP == 16, u32x4_t, uint2>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    constexpr int SB = BN / 32 / NW;           // strip blocks per wave
+    constexpr int AG = BM / 8 / NW;            // 1 KB copies (8 rows) per wave: A
+    constexpr int BG = BN / 8 / NW;            //   and B
+    constexpr int SOFF = BM * RB;              // byte offset of the strip rows
+    constexpr int BOFF = (BM + SR) * RB;       // byte offset of B in a stage
+    constexpr int STAGE = BOFF + BN * RB;      // bytes per LDS buffer
+    static_assert(SR == 0 || (SR / 8 <= NW && SB * 2 == TN),
+                  "strip: one copy per wave of the first SR/8; a wave row's share of the B fragments");
+    static_assert(AG * NW * 8 == BM && BG * NW * 8 == BN, "whole 8-row copies per wave");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
     const int N = p.N, K = p.K;
     const int NT = (N + BN - 1) / BN;
@@ -93,16 +93,26 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
     const int t_end = min(T, (xcd + 1) * per);
     __shared__ int s_next;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave / WNC, wn = wave % WNC;
     const int frow = lane & 31, fhalf = lane >> 5;
     const int KT = K / BK;
-    // LDS byte offsets: loader chunk (row tid/CH + RPI*i, chunk tid%CH);
-    // fragment rows of this lane (row + 32*i, chunk 2*ks + fhalf)
-    const int ld_off = (tid / CH) * RS + (tid % CH) * 16;
-    const int fa_off = (wm * WM + frow) * RS + fhalf * 16;
-    const int fb_off = BOFF + (wn * WNT + frow) * RS + fhalf * 16;
-    const int fs_off = (BM + frow) * RS + fhalf * 16;
-    const int ls_off = (BM + tid * SP / (BK * 2)) * RS + (tid * SP) % (BK * 2);
+    // LDS rows are unpadded; chunk c of row r sits in slot c ^ swz(r), with
+    // swz(r) = (r >> 1) & 7, so the 16 rows a fragment read touches at one
+    // chunk fall on distinct bank groups.  A fragment row of this lane is
+    // frow + 32*i (+ a multiple of 32), whose swizzle is swz(frow): step ks
+    // reads chunk 2*ks + fhalf at the same slot offset co[ks] in every row.
+    auto swz = [](int r) { return (r >> 1) & 7; };
+    const int fa_off = (wm * WM + frow) * RB;
+    const int fb_off = BOFF + (wn * WNT + frow) * RB;
+    const int fs_off = SOFF + frow * RB;
+    int co[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) co[ks] = ((2 * ks + fhalf) ^ swz(frow)) * 16;
+    // Copy g of a wave fills LDS rows 8*(wave + NW*g) .. +7: lane l writes
+    // row 8*(wave + NW*g) + l/8, slot l%8, i.e. chunk (l%8) ^ swz(row).
+    const int crow = lane >> 3;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
     // Tiles of this XCD's chunk are handed out on demand (tiles differ in
     // cost: partly filled m-tiles skip MFMAs).  The next tile is claimed at
@@ -141,46 +151,61 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         const char* __restrict__ Bb =
             reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.B) + (size_t)e * N * K);
 
-        // Global byte offsets of this thread's chunks (rows past the
-        // occupancy or past N load a clamped valid row).
-        uint32_t aoff[A_CH], boff[B_CH];
+        // Global byte offsets of this lane's chunks (rows past the occupancy
+        // or past N load a clamped valid row).
+        uint32_t aoff[AG], boff[BG], soff = 0;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int rg = min(m0 + tid / CH + RPI * i, M - 1);
-            aoff[i] = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u + (uint32_t)(tid % CH) * 16u;
+        for (int g = 0; g < AG; ++g) {
+            const int lr = 8 * (wave + NW * g) + crow;
+            const int rg = min(m0 + lr, M - 1);
+            aoff[g] = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u +
+                      (uint32_t)(((lane & 7) ^ swz(lr)) * 16);
         }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            boff[i] = (uint32_t)min(n0 + tid / CH + RPI * i, N - 1) * (uint32_t)K * 2u +
-                      (uint32_t)(tid % CH) * 16u;
-        // strip rows: one 8-byte piece per thread
-        uint32_t soff = 0;
-        if constexpr (SR > 0) {
-            const int rg = min(m0 + BM + tid * SP / (BK * 2), M - 1);
+        for (int g = 0; g < BG; ++g) {
+            const int lr = 8 * (wave + NW * g) + crow;
+            boff[g] = (uint32_t)min(n0 + lr, N - 1) * (uint32_t)K * 2u +
+                      (uint32_t)(((lane & 7) ^ swz(lr)) * 16);
+        }
+        if (SR > 0 && wave < SR / 8) {
+            const int lr = 8 * wave + crow;                 // strip row
+            const int rg = min(m0 + BM + lr, M - 1);
             soff = (uint32_t)(arow ? arow[rg] : rg) * (uint32_t)K * 2u +
-                   (uint32_t)((tid * SP) % (BK * 2));
+                   (uint32_t)(((lane & 7) ^ swz(lr)) * 16);
         }
-        u32x4_t ra[A_CH], rb[B_CH];
-        strip_t rs;
-        auto gload = [&](auto strip_tag, int kt) {
-            const uint32_t kb = (uint32_t)kt * BK * 2u;
-            if constexpr (decltype(strip_tag)::value)
-                rs = *reinterpret_cast<const strip_t*>(Ab + soff + kb);
-#pragma unroll
-            for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(Ab + aoff[i] + kb);
-#pragma unroll
-            for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(Bb + boff[i] + kb);
+        // k-tile kt into LDS buffer buf by global->LDS copies
+        // (global_load_lds_dwordx4: the wave-uniform base + k offset in
+        // scalar registers, the lane's 32-bit offset in a vector register,
+        // the 1 KB destination in M0, written one wait state ahead; M0 is
+        // saved and restored around it).  They are asm so that the compiler
+        // does not make the fragment reads of the other buffer wait for
+        // them; the k-tile waits for its copies itself before its closing
+        // barrier.
+        auto copy = [](const char* base, uint32_t voff, uint32_t lds) {
+            uint32_t saved;
+            asm volatile(
+                "s_mov_b32 %0, m0\n\t"
+                "s_mov_b32 m0, %1\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %2, %3\n\t"
+                "s_mov_b32 m0, %0"
+                : "=&s"(saved)
+                : "s"(lds), "v"(voff), "s"(base)
+                : "memory");
         };
-        auto sstore = [&](auto strip_tag, int buf) {
-            char* st = smem + buf * STAGE;
-            if constexpr (decltype(strip_tag)::value)
-                *reinterpret_cast<strip_t*>(st + ls_off) = rs;
+        auto gcopy = [&](auto strip_tag, int kt, int buf) {
+            const uint32_t kb = (uint32_t)kt * BK * 2u;
+            const char* Ak = Ab + kb;
+            const char* Bk = Bb + kb;
+            const uint32_t st = lds0 + (uint32_t)(buf * STAGE);
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i)
-                *reinterpret_cast<u32x4_t*>(st + ld_off + i * RPI * RS) = ra[i];
+            for (int g = 0; g < AG; ++g) copy(Ak, aoff[g], st + (uint32_t)((wv + NW * g) * 1024));
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i)
-                *reinterpret_cast<u32x4_t*>(st + BOFF + ld_off + i * RPI * RS) = rb[i];
+            for (int g = 0; g < BG; ++g)
+                copy(Bk, boff[g], st + (uint32_t)(BOFF + (wv + NW * g) * 1024));
+            if constexpr (decltype(strip_tag)::value) {
+                if (wv < SR / 8) copy(Ak, soff, st + (uint32_t)(SOFF + wv * 1024));
+            }
         };
 
         // Fragment (32x32x16): lane l supplies row l%32 and the 8 consecutive
@@ -190,15 +215,15 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
         auto load_frags = [&](auto vi_tag, auto strip_tag, const char* st, int ks, int slot) {
             constexpr int VI = decltype(vi_tag)::value;
             if constexpr (decltype(strip_tag)::value)
-                fs[slot] = *reinterpret_cast<const bf16x8_t*>(st + fs_off + ks * 32);
+                fs[slot] = *reinterpret_cast<const bf16x8_t*>(st + fs_off + co[ks]);
 #pragma unroll
             for (int i = 0; i < VI; ++i)
-                fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(st + fa_off + i * 32 * RS + ks * 32);
+                fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(st + fa_off + co[ks] + i * 32 * RB);
             if constexpr (VI > 0) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     fb[slot][j] =
-                        *reinterpret_cast<const bf16x8_t*>(st + fb_off + j * 32 * RS + ks * 32);
+                        *reinterpret_cast<const bf16x8_t*>(st + fb_off + co[ks] + j * 32 * RB);
             }
         };
 
@@ -215,18 +240,18 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_s[b][r] = 0.f;
 
-        // One k-tile from LDS buffer kt&1.  With REFILL, k-tile kt+1 is loaded
-        // into registers during the first step and stored to the other buffer
-        // (which every wave finished reading before the previous barrier)
-        // during the last step.  VI: how many of this wave's TM row sub-tiles
-        // hold filled rows; the MFMAs of the others are skipped (an expert's
-        // last m-tile is usually partly empty).  Every wave still takes part
-        // in the loads, stores and barriers.
+        // One k-tile from LDS buffer kt&1.  With REFILL, the copies of k-tile
+        // kt+1 into the other buffer (which every wave finished reading
+        // before the previous barrier) are issued at the start of the first
+        // step, and the k-tile waits for them before its closing barrier.
+        // VI: how many of this wave's TM row sub-tiles hold filled rows; the
+        // MFMAs of the others are skipped (an expert's last m-tile is
+        // usually partly empty).  Every wave still takes part in the copies
+        // and barriers.
         auto ktile = [&](auto refill_tag, auto vi_tag, auto strip_tag, int kt) {
             constexpr bool REFILL = decltype(refill_tag)::value;
             constexpr int VI = decltype(vi_tag)::value;
             constexpr int SI = decltype(strip_tag)::value ? 1 : 0;
-            constexpr int NL = A_CH + B_CH + SI;   // loads (and stores) per thread
             constexpr int NF = TM + TN + SI;       // fragment reads per step
             constexpr int NM = TM * TN + SI * SB;  // MFMAs per step (full tile)
             const char* st = smem + (kt & 1) * STAGE;
@@ -235,8 +260,7 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if constexpr (REFILL) {
-                    if (ks == 0) gload(strip_tag, kt + 1);
-                    if (ks == KS - 1) sstore(strip_tag, (kt + 1) & 1);
+                    if (ks == 0) gcopy(strip_tag, kt + 1, (kt + 1) & 1);
                 }
                 if (ks + 1 < KS) load_frags(vi_tag, strip_tag, st, ks + 1, (ks + 1) & 1);
 #pragma unroll
@@ -254,21 +278,9 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
                                                                            0, 0, 0);
                     }
                 }
-                // instruction groups: spread memory instructions over the MFMAs
-                if (REFILL && ks == 0) {
-#pragma unroll
-                    for (int g = 0; g < NL; ++g) {
-                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
-                        if (g < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                        __builtin_amdgcn_sched_group_barrier(0x008, (NM + NL - 1) / NL, 0);
-                    }
-                } else if (REFILL && ks == KS - 1) {
-#pragma unroll
-                    for (int g = 0; g < NL; ++g) {
-                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // LDS write
-                        __builtin_amdgcn_sched_group_barrier(0x008, (NM + NL - 1) / NL, 0);
-                    }
-                } else if (ks + 1 < KS) {
+                // the next step's fragment reads spread over the MFMAs (a
+                // wave issues in order, so a burst would stall its MFMAs)
+                if (ks + 1 < KS) {
 #pragma unroll
                     for (int g = 0; g < NF; ++g) {
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
@@ -277,11 +289,12 @@ __global__ __launch_bounds__(128 * WNC, 1) void gemm_bf16_kernel(GemmParams p) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if constexpr (REFILL) __builtin_amdgcn_s_waitcnt(0);   // copies landed
             __syncthreads();
         };
         auto kloop = [&](auto vi_tag, auto strip_tag) {
-            gload(strip_tag, 0);
-            sstore(strip_tag, 0);
+            gcopy(strip_tag, 0, 0);
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             int kt = 0;
             for (; kt + 1 < KT; ++kt) ktile(std::true_type{}, vi_tag, strip_tag, kt);
