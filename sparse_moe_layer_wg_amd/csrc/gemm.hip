@@ -22,10 +22,11 @@
 //   current MFMAs run (spread with sched_group_barrier).  Measured from L2,
 //   the copies move as many bytes per clock as loads into registers, and
 //   against that register-staged loop (padded LDS rows) this runs the
-//   expert GEMMs 2-7% faster with the same results bit for bit.  LDS rows
-//   are 128 bytes with their 16-byte chunks XOR-swizzled by row, so the 16
-//   rows a fragment read touches at one chunk fall on distinct bank
-//   groups.
+//   expert GEMMs 2-4% faster on average with the same results bit for bit
+//   (the stores and the waits for them were a tenth of the waves' cycles).
+//   LDS rows are 128 bytes with their 16-byte chunks XOR-swizzled by row,
+//   so the 16 rows a fragment read touches at one chunk fall on distinct
+//   bank groups.
 //   Rows past an expert's occupancy (and columns past N) load a clamped
 //   valid row; their results are never stored.
 //   An expert's last 256-row m-tile may hold up to 32 more rows (a strip):
