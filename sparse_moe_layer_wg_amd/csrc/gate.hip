@@ -478,43 +478,48 @@ __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, in
         v[q] = j < E ? (lds_row ? lds_row[j] : lrow[j]) : 0.f;
         if (lds_row && j < E) lds_row[j] = 0.f;
     }
-    // top[r]: key of the r-th largest logit (wave-uniform)
-    uint64_t top[kMaxSel];
+    // The sorted keys live one per lane: lane r holds the key of the r-th
+    // largest logit (r < n), so the close pairs come from one ballot and no
+    // array of keys sits in scalar registers.
+    uint64_t kl = 0;
     uint32_t taken = 0;
-#pragma unroll
-    for (int r = 0; r < kMaxK + 1; ++r)
-        if (r < nsel) top[r] = select_next<EQ>(v, E, lane, taken);
+    uint64_t top0 = 0;
+    float v_prev = 0.f, v_last = 0.f;   // values of the last two keys taken
+#pragma unroll 1
+    for (int r = 0; r < nsel; ++r) {
+        const uint64_t key = select_next<EQ>(v, E, lane, taken);
+        if (lane == r) kl = key;
+        if (r == 0) top0 = key;
+        v_prev = v_last;
+        v_last = key_value(key);
+    }
 
     const float tau = tau_in >= 0.f ? tau_in : token_margin(p, ms, s);
     if (tau > 0.f && nsel > 1) {
         // Pair r joins sorted positions r and r+1 and is "close" when their
         // difference is below tau.  Pairs r < k decide the ordered top-k.
-        bool need = false;
-#pragma unroll
-        for (int r = 0; r < kMaxK; ++r)
-            if (r < k && r + 1 < nsel)
-                need |= key_value(top[r]) - key_value(top[r + 1]) < tau;
-        if (need) {
+        auto close_pairs = [&](int n) {
+            const float vl = key_value(kl);
+            const float vn = __shfl_down(vl, 1);
+            return static_cast<uint32_t>(__ballot(lane + 1 < n && vl - vn < tau));
+        };
+        uint32_t closebits = close_pairs(nsel);
+        if (closebits & ((1u << k) - 1u)) {
             // follow a chain of close pairs past position k
             int n = nsel;
-#pragma unroll
-            for (int r = 2; r < kMaxSel; ++r) {
-                if (r == n && n < E && key_value(top[r - 2]) - key_value(top[r - 1]) < tau) {
-                    top[r] = select_next<EQ>(v, E, lane, taken);
-                    ++n;
-                }
+#pragma unroll 1
+            while (n < kMaxSel && n < E && v_prev - v_last < tau) {
+                const uint64_t key = select_next<EQ>(v, E, lane, taken);
+                if (lane == n) kl = key;
+                v_prev = v_last;
+                v_last = key_value(key);
+                ++n;
             }
-            const bool overflow =
-                n == kMaxSel && n < E &&
-                key_value(top[kMaxSel - 2]) - key_value(top[kMaxSel - 1]) < tau;
+            const bool overflow = n == kMaxSel && n < E && v_prev - v_last < tau;
             int ncand = 0;
             if (!overflow) {
                 // members of the close chains that contain a pair r < k
-                uint32_t closebits = 0;
-#pragma unroll
-                for (int r = 0; r + 1 < kMaxSel; ++r)
-                    if (r + 1 < n && key_value(top[r]) - key_value(top[r + 1]) < tau)
-                        closebits |= 1u << r;
+                closebits = close_pairs(n);
                 uint32_t members = 0;
                 int r = 0;
                 while (r + 1 < n) {
@@ -526,13 +531,10 @@ __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, in
                     while (r + 1 < n && ((closebits >> r) & 1u)) ++r;
                     if (a < k) members |= ((2u << r) - 1u) & ~((1u << a) - 1u);
                 }
-#pragma unroll
-                for (int q = 0; q < kMaxSel; ++q) {
-                    if ((members >> q) & 1u) {
-                        s_cand[ncand] = key_index(top[q]);
-                        ++ncand;
-                    }
-                }
+                // their experts, in sorted order
+                if (lane < kMaxSel && ((members >> lane) & 1u))
+                    s_cand[__popc(members & ((1u << lane) - 1u))] = key_index(kl);
+                ncand = __popc(members);
             }
             // a chain longer than kMaxSel: refine every logit of the token
             const int total = overflow ? E : ncand;
@@ -546,14 +548,18 @@ __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, in
                 apply_refined<EQ>(v, lrow, js, nv, lane);
             }
             taken = 0;
-#pragma unroll
-            for (int r = 0; r < kMaxK; ++r)
-                if (r < k) top[r] = select_next<EQ>(v, E, lane, taken);
+            kl = 0;
+#pragma unroll 1
+            for (int r = 0; r < k; ++r) {
+                const uint64_t key = select_next<EQ>(v, E, lane, taken);
+                if (lane == r) kl = key;
+                if (r == 0) top0 = key;
+            }
         }
     }
 
     // softmax over all E logits, stabilised by the largest
-    const float m = key_value(top[0]);
+    const float m = key_value(top0);
     float ev[EQ], part = 0.f;
 #pragma unroll
     for (int q = 0; q < EQ; ++q) {
@@ -569,18 +575,15 @@ __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, in
     zacc += lse * lse;
 
     // renormalised top-k weights: p_r / sum_r' p_r' = e_r / sum_r' e_r'
+    // (summed in rank order; lane r holds the r-th key)
     float den = 0.f;
 #pragma unroll
     for (int r = 0; r < kMaxK; ++r)
-        if (r < k) den += expf(key_value(top[r]) - m);
+        if (r < k) den += expf(key_value(readlane_u64(kl, r)) - m);
     if (lane < k) {
-        uint64_t mine = top[0];
-#pragma unroll
-        for (int r = 1; r < kMaxK; ++r)
-            if (r == lane) mine = top[r];
-        const int j = key_index(mine);
+        const int j = key_index(kl);
         p.topk_idx[(size_t)s * k + lane] = j;
-        p.topk_w[(size_t)s * k + lane] = expf(key_value(mine) - m) / den;
+        p.topk_w[(size_t)s * k + lane] = expf(key_value(kl) - m) / den;
         atomicAdd(&s_hist[lane * E + j], 1);
     }
 }
