@@ -363,16 +363,30 @@ __device__ __forceinline__ uint64_t select_next(const float (&v)[EQ], int E, int
 }
 
 // fp64 dot products x[s,:] . wg[j_u,:] (+ bg) for up to four experts, rounded
-// once to fp32.  Lanes take 8-element (bf16) or 4-element (fp32) chunks.
+// once to fp32.  Lanes take 8-element (bf16) or 4-element (fp32) chunks.  A
+// slot without an expert (js[u] < 0) reads the first expert's row and its
+// sum is dropped, so every load of a chunk is issued before the chunk's
+// products (and four chunks' loads are in flight): the loop is bound by
+// memory latency, not by the arithmetic.
 __device__ __forceinline__ void refine_group(const RouteParams& p, int s, const int (&js)[4],
                                              float (&nv)[4]) {
     const int lane = threadIdx.x & (kWave - 1);
+    const float* wr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        wr[u] = p.wg + (size_t)__builtin_amdgcn_readfirstlane(js[u] >= 0 ? js[u] : js[0]) * p.d;
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     if (p.x_bf16) {
         const bf16_t* xr = static_cast<const bf16_t*>(p.x) + (size_t)s * p.d;
-#pragma unroll 1
+#pragma unroll 4
         for (int i = lane * 8; i < p.d; i += kWave * 8) {
             const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(xr + i);
+            f32x4_t w0[4], w1[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                w0[u] = *reinterpret_cast<const f32x4_t*>(wr[u] + i);
+                w1[u] = *reinterpret_cast<const f32x4_t*>(wr[u] + i + 4);
+            }
             float xv[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -380,29 +394,25 @@ __device__ __forceinline__ void refine_group(const RouteParams& p, int s, const 
                 xv[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (js[u] < 0) continue;
-                const f32x4_t* wr = reinterpret_cast<const f32x4_t*>(p.wg + (size_t)js[u] * p.d + i);
-                const f32x4_t w0 = wr[0], w1 = wr[1];
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[u] += (double)xv[q] * (double)w0[q];
-                    acc[u] += (double)xv[4 + q] * (double)w1[q];
+                    acc[u] += (double)xv[q] * (double)w0[u][q];
+                    acc[u] += (double)xv[4 + q] * (double)w1[u][q];
                 }
-            }
         }
     } else {
         const float* xr = static_cast<const float*>(p.x) + (size_t)s * p.d;
-#pragma unroll 1
+#pragma unroll 4
         for (int i = lane * 4; i < p.d; i += kWave * 4) {
             const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xr + i);
+            f32x4_t w0[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (js[u] < 0) continue;
-                const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(p.wg + (size_t)js[u] * p.d + i);
+            for (int u = 0; u < 4; ++u) w0[u] = *reinterpret_cast<const f32x4_t*>(wr[u] + i);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[u] += (double)xv[q] * (double)w0[q];
-            }
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u] += (double)xv[q] * (double)w0[u][q];
         }
     }
 #pragma unroll
