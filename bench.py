@@ -259,17 +259,19 @@ def main():
     step_events = [make_events(gemm_bounds) for _ in range(a.steps)]
     torch.cuda.synchronize()
 
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # step boundaries: bounds[0] opens the timed region, bounds[i+1] closes
+    # step i (the last one closes the region)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     wall0 = time.perf_counter()
-    t_start.record(stream)
+    bounds[0].record(stream)
     for i in range(a.steps):
         layer.forward(xs[i % len(xs)], events=step_events[i])
-    t_end.record(stream)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = bounds[0].elapsed_time(bounds[-1])
     ms = total_ms / a.steps
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(a.steps)]
     gemm_us = {
         "expert_gemm1": float(np.mean([ev[5].elapsed_time(ev[6]) * 1000.0 for ev in step_events])),
         "expert_gemm2": float(np.mean([ev[6].elapsed_time(ev[7]) * 1000.0 for ev in step_events])),
@@ -346,6 +348,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_min": float(np.min(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
