@@ -123,11 +123,15 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const float* __restric
 // shape; no single unit is saturated: matrix pipes busy a quarter to a third
 // of the time, the texture path a quarter, L2 hit rate 70-80%).
 // Operands are staged through registers into two LDS buffers (x and the
-// three weight planes, XOR-swizzled by row); the fp32 weights are read once
-// per block, 32 bytes per thread per k-tile.  Rows past S or E load a
-// clamped valid row and are never stored.
+// three weight planes, XOR-swizzled by row), with the global loads two
+// k-tiles ahead; the fp32 weights are read once per block, 32 bytes per
+// thread per k-tile.  Rows past S or E load a clamped valid row and are
+// never stored.
 namespace {
 constexpr int GM_BM = 128, GM_BN = 64, GM_BK = 64, GM_CH = GM_BK / 8, GM_NT = 512;
+// k-tiles of global loads in flight (register slots).  Two: 114 VGPRs, so two
+// 512-thread blocks still share a CU; three need 137 and leave one.
+constexpr int GM_PF = 2;
 
 __device__ __forceinline__ int gm_swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
 
@@ -182,8 +186,9 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
         wb = wg + (size_t)min(j0 + row, E - 1) * d + ch * 8;
         bld = A_SZ + row * GM_CH + gm_swz(row, ch);
     }
-    u32x4_t rx[XI];
-    f32x4_t rw[2];
+    // the loads of k-tile t sit in register slot t % GM_PF until staged
+    u32x4_t rx[GM_PF][XI];
+    f32x4_t rw[GM_PF][2];
     // this thread's shares of the squared row norms (x rows tid/8 + 64 i,
     // router row tid/8), added as the chunks are staged by the blocks that
     // store them: x by the first expert tile, wg by the first token tile
@@ -191,22 +196,23 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
     float xsq[XI], wsq = 0.f;
 #pragma unroll
     for (int i = 0; i < XI; ++i) xsq[i] = 0.f;
-    auto gload = [&](int k0) {
+    auto gload = [&](int k0, int sl) {
 #pragma unroll
-        for (int i = 0; i < XI; ++i) rx[i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
+        for (int i = 0; i < XI; ++i) rx[sl][i] = *reinterpret_cast<const u32x4_t*>(xa[i] + k0);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) rw[q] = *reinterpret_cast<const f32x4_t*>(wb + k0 + 4 * q);
+        for (int q = 0; q < 2; ++q)
+            rw[sl][q] = *reinterpret_cast<const f32x4_t*>(wb + k0 + 4 * q);
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, int sl) {
         u32x4_t* st = smem + buf * STAGE;
 #pragma unroll
         for (int i = 0; i < XI; ++i) {
-            st[ald[i]] = rx[i];
+            st[ald[i]] = rx[sl][i];
             if (xnorm) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float lo = __uint_as_float(rx[i][q] << 16);
-                    const float hi = __uint_as_float(rx[i][q] & 0xffff0000u);
+                    const float lo = __uint_as_float(rx[sl][i][q] << 16);
+                    const float hi = __uint_as_float(rx[sl][i][q] & 0xffff0000u);
                     xsq[i] = fmaf(lo, lo, fmaf(hi, hi, xsq[i]));
                 }
             }
@@ -215,10 +221,10 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) wsq = fmaf(rw[q][u], rw[q][u], wsq);
+                for (int u = 0; u < 4; ++u) wsq = fmaf(rw[sl][q][u], rw[sl][q][u], wsq);
         }
         u32x4_t hi, lo1, lo2;
-        split3(rw[0], rw[1], hi, lo1, lo2);
+        split3(rw[sl][0], rw[sl][1], hi, lo1, lo2);
         st[bld] = hi;
         st[bld + B_SZ] = lo1;
         st[bld + 2 * B_SZ] = lo2;
@@ -229,12 +235,26 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
     for (int r = 0; r < 16; ++r) acc_hi[r] = 0.f, acc_lo[r] = 0.f;
     const int frow = lane & 31, fhalf = lane >> 5;
     const int KT = d / GM_BK;
-    gload(0);
-    sstore(0);
+#pragma unroll
+    for (int t = 0; t < GM_PF; ++t) gload(min(t, KT - 1) * GM_BK, t);
+    sstore(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
+    // k-tile kt: the loads of k-tile kt+GM_PF go into the slot k-tile kt has
+    // left (staged to LDS at the end of the previous k-tile), and k-tile kt+1
+    // is staged at the end, its loads having had a whole k-tile more to
+    // land.  The loads are issued on every k-tile (past the end: the last
+    // k-tile again, never used), so that the compiler's wait before a slot is
+    // read leaves the same number of later loads in flight on every path; a
+    // conditional issue made it wait for all of them (a full vmcnt(0)).  The
+    // loop is unrolled by GM_PF so that the slots are static registers.
+    // (Two-deep against one: 4-11% faster, logits bit-identical.)
+    for (int kb = 0; kb < KT; kb += GM_PF)
+#pragma unroll
+    for (int u = 0; u < GM_PF; ++u) {
+        const int kt = kb + u;
+        if (kt >= KT) break;
         const int buf = kt & 1;
-        if (kt + 1 < KT) gload((kt + 1) * GM_BK);
+        gload(min(kt + GM_PF, KT - 1) * GM_BK, u);
         const u32x4_t* st = smem + buf * STAGE;
 #pragma unroll
         for (int ks = 0; ks < GM_BK / 16; ++ks) {
@@ -249,7 +269,7 @@ __global__ __launch_bounds__(GM_NT, 1) void gate_logits_mfma_kernel(const bf16_t
             acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc_lo, 0, 0, 0);
             acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b2, acc_lo, 0, 0, 0);
         }
-        if (kt + 1 < KT) sstore(buf ^ 1);
+        if (kt + 1 < KT) sstore(buf ^ 1, (u + 1) % GM_PF);
         __syncthreads();
     }
     // row norms: the 8 loader threads of a row (consecutive lanes) add their
