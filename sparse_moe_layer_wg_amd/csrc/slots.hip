@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hi
     __shared__ double s_red[256];
     const int e = blockIdx.x, tid = threadIdx.x;
     double pa = 0.0;
+#pragma unroll 4
     for (int b = tid; b < nb; b += 256) pa += (double)ppart[(size_t)b * E + e];
     s_red[tid] = pa;
     __syncthreads();
@@ -91,17 +92,30 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t* __restrict__ hi
         __syncthreads();
     }
     if (tid == 0) psum[e] = s_red[0];
+    // Each thread takes CH consecutive entries of a 256*CH-entry chunk: all
+    // of its loads go out at once and one block scan of the per-thread sums
+    // covers the chunk (a row of k*nb entries is one chunk up to 2048).
+    constexpr int CH = 8;
     const int T = k * nb;
     int32_t* row = hist + (size_t)e * T;
     int carry = 0;
-    for (int base = 0; base < T; base += 256) {
-        const int i = base + tid;
-        const int v = i < T ? row[i] : 0;
+    for (int base = 0; base < T; base += 256 * CH) {
+        const int i0 = base + tid * CH;
+        int v[CH], sum = 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) v[j] = i0 + j < T ? row[i0 + j] : 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) sum += v[j];
         int total;
-        const int ex = block_exclusive_scan(v, s_wave, &total);
-        if (i < T) {
-            row[i] = carry + ex;
-            if (i % nb == 0) s_rank_start[i / nb] = carry + ex;
+        int run = carry + block_exclusive_scan(sum, s_wave, &total);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int i = i0 + j;
+            if (i < T) {
+                row[i] = run;
+                if (i % nb == 0) s_rank_start[i / nb] = run;
+            }
+            run += v[j];
         }
         carry += total;
     }
@@ -364,13 +378,24 @@ __global__ __launch_bounds__(256) void reroute_scan_kernel(int32_t* __restrict__
     const int T = k * nb;
     int32_t* row = hist + (size_t)e * T;
     const int o = occ[e];
+    // CH consecutive entries per thread, one block scan per 256*CH entries
+    // (as in slot_scan_kernel)
+    constexpr int CH = 8;
     int carry = 0;
-    for (int base = 0; base < T; base += 256) {
-        const int i = base + tid;
-        const int v = i < T ? row[i] : 0;
+    for (int base = 0; base < T; base += 256 * CH) {
+        const int i0 = base + tid * CH;
+        int v[CH], sum = 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) v[j] = i0 + j < T ? row[i0 + j] : 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) sum += v[j];
         int total;
-        const int ex = block_exclusive_scan(v, s_wave, &total);
-        if (i < T) row[i] = o + carry + ex;
+        int run = o + carry + block_exclusive_scan(sum, s_wave, &total);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (i0 + j < T) row[i0 + j] = run;
+            run += v[j];
+        }
         carry += total;
     }
     __syncthreads();   // every thread has read occ[e]
