@@ -494,10 +494,12 @@ __device__ __forceinline__ float token_margin(const RouteParams& p, const Margin
 template <int EQ>
 // lds_row: NULL (the logits are read from p.logits), or the token's raw
 // logits in LDS, which are read and then zeroed; tau_in: the token's margin
-// when already known (>= 0), else computed here.
+// when already known (>= 0), else computed here; seed: NULL, or the token's
+// k+1 largest keys already sorted (LDS), which then replace the first k+1
+// selections.
 __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, int s, int lane,
                                  int* s_hist, int* s_cand, float (&pacc)[EQ], float& zacc,
-                                 float* lds_row, float tau_in) {
+                                 float* lds_row, float tau_in, const uint64_t* seed) {
     const int E = p.E, k = p.k;
     const int nsel = k + 1 <= E ? k + 1 : E;
     float* lrow = p.logits + (size_t)s * E;
@@ -515,13 +517,29 @@ __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, in
     uint32_t taken = 0;
     uint64_t top0 = 0;
     float v_prev = 0.f, v_last = 0.f;   // values of the last two keys taken
+    if (seed) {
+        // the same keys in the same order as the selections below would take
+        // them: lane r keeps key r, and each listed expert's owner lane marks
+        // it taken
 #pragma unroll 1
-    for (int r = 0; r < nsel; ++r) {
-        const uint64_t key = select_next<EQ>(v, E, lane, taken);
-        if (lane == r) kl = key;
-        if (r == 0) top0 = key;
-        v_prev = v_last;
-        v_last = key_value(key);
+        for (int r = 0; r < nsel; ++r) {
+            const uint64_t key = seed[r];
+            if (lane == r) kl = key;
+            const int j = key_index(key);
+            if ((j & (kWave - 1)) == lane) taken |= 1u << (j / kWave);
+        }
+        top0 = seed[0];
+        v_last = key_value(seed[nsel - 1]);
+        v_prev = nsel >= 2 ? key_value(seed[nsel - 2]) : 0.f;
+    } else {
+#pragma unroll 1
+        for (int r = 0; r < nsel; ++r) {
+            const uint64_t key = select_next<EQ>(v, E, lane, taken);
+            if (lane == r) kl = key;
+            if (r == 0) top0 = key;
+            v_prev = v_last;
+            v_last = key_value(key);
+        }
     }
 
     const float tau = tau_in >= 0.f ? tau_in : token_margin(p, ms, s);
@@ -642,7 +660,8 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(RouteParams p) {
     for (int t = 0; t < kTokBlock / NW; ++t) {
         const int s = b * kTokBlock + wave * (kTokBlock / NW) + t;
         if (s >= p.S) break;
-        route_token_wave<EQ>(p, ms, s, lane, s_hist, s_cand[wave], pacc, zacc, nullptr, -1.f);
+        route_token_wave<EQ>(p, ms, s, lane, s_hist, s_cand[wave], pacc, zacc, nullptr, -1.f,
+                             nullptr);
     }
 
     // deterministic block reduction of the probability and lse^2 partials
@@ -694,6 +713,7 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
     __shared__ float s_lse2[kTokBlock], s_z[L], s_tau[kTokBlock];
     __shared__ int s_flag[kTokBlock], s_list[kTokBlock], s_nlist;
     __shared__ int s_cand[L][kMaxSel];
+    __shared__ uint64_t s_seed[kTokBlock][K1];                  // flagged tokens' top keys
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t = tid / L, l = tid % L;                          // token of the tile, part
@@ -792,8 +812,16 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
             if (r < k && r + 1 < nsel) flag |= kval(gk[r]) - kval(gk[r + 1]) < tau;
     }
     const bool fast = live && !flag;
-    // a flagged token's raw logits and margin go to LDS for the wave router
-    // (its probability row is written there only by that router, as zeros)
+    // a flagged token's raw logits, margin and sorted top k+1 keys go to LDS
+    // for the wave router (its probability row is written there only by
+    // that router, as zeros)
+    if (live && flag && l == 0) {
+#pragma unroll
+        for (int r = 0; r < K1; ++r)
+            if (r < nsel)
+                s_seed[t][r] = (static_cast<uint64_t>(gk[r]) << 32) |
+                               (0xffffffffu - static_cast<uint32_t>(gi[r]));
+    }
     if (live && flag) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -864,7 +892,7 @@ __global__ __launch_bounds__(64 * L) void route_fast_kernel(RouteParams p) {
     const int nl = s_nlist;
     for (int f = wave; f < nl; f += L)
         route_token_wave<EQ>(p, ms, b * kTokBlock + s_list[f], lane, s_hist, s_cand[wave], pacc,
-                             zacc, s_pt + s_list[f] * EP, s_tau[s_list[f]]);
+                             zacc, s_pt + s_list[f] * EP, s_tau[s_list[f]], s_seed[s_list[f]]);
 #pragma unroll
     for (int q = 0; q < EQ; ++q) {
         const int j = lane + 64 * q;
