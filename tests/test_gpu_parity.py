@@ -32,6 +32,8 @@ ROUTE_CASES = [
     # S, E, k, C   (ragged S, E not a multiple of 64, tiny and large E)
     (1, 1, 1, 1), (63, 3, 2, 5), (64, 8, 2, 16), (65, 8, 2, 16), (1000, 65, 3, 40),
     (777, 128, 2, 9), (2048, 256, 8, 70), (300, 1000, 4, 2), (129, 2048, 8, 1), (500, 7, 7, 500),
+    # histogram rows of k * ceil(S/64) > 2048 entries: the slot scan's second chunk
+    (20000, 16, 8, 2000), (70000, 40, 2, 3000),
 ]
 
 

@@ -218,6 +218,8 @@ def test_reroute_forward_replays_in_a_hip_graph():
 REROUTE_ROUTE_CASES = [
     (1, 2, 1, 1), (63, 3, 2, 5), (65, 8, 2, 16), (1000, 65, 3, 40), (777, 128, 2, 9),
     (2048, 256, 8, 70), (300, 1000, 4, 2), (129, 2048, 8, 1), (500, 9, 7, 60),
+    # scanned rows of k * ceil(S/64) > 2048 entries (two chunks)
+    (20000, 16, 8, 900),
 ]
 
 
