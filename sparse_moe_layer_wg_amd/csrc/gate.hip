@@ -452,9 +452,10 @@ __device__ __forceinline__ void apply_refined(float (&v)[EQ], float* lrow, const
     for (int u = 0; u < 4; ++u) {
         const int j = js[u];
         if (j < 0 || (j & (kWave - 1)) != lane) continue;
+        // a select per register (a guarded store lets the compiler index v
+        // dynamically, which moves it to scratch memory)
 #pragma unroll
-        for (int q = 0; q < EQ; ++q)
-            if (q == (j >> 6)) v[q] = nv[u];
+        for (int q = 0; q < EQ; ++q) v[q] = q == (j >> 6) ? nv[u] : v[q];
         lrow[j] = nv[u];
     }
 }
@@ -504,11 +505,21 @@ __device__ void route_token_wave(const RouteParams& p, const MarginScale& ms, in
     const int nsel = k + 1 <= E ? k + 1 : E;
     float* lrow = p.logits + (size_t)s * E;
     float v[EQ];
+    // two loops, not one pointer chosen between LDS and global memory (that
+    // makes generic flat loads, which wait on both counters)
+    if (lds_row) {
 #pragma unroll
-    for (int q = 0; q < EQ; ++q) {
-        const int j = lane + kWave * q;
-        v[q] = j < E ? (lds_row ? lds_row[j] : lrow[j]) : 0.f;
-        if (lds_row && j < E) lds_row[j] = 0.f;
+        for (int q = 0; q < EQ; ++q) {
+            const int j = lane + kWave * q;
+            v[q] = j < E ? lds_row[j] : 0.f;
+            if (j < E) lds_row[j] = 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < EQ; ++q) {
+            const int j = lane + kWave * q;
+            v[q] = j < E ? lrow[j] : 0.f;
+        }
     }
     // The sorted keys live one per lane: lane r holds the key of the r-th
     // largest logit (r < n), so the close pairs come from one ballot and no
